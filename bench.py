@@ -1,0 +1,278 @@
+"""Throughput of the DFlash2 block-drafting hot path on one MI355X.
+
+One step = one pass of the whole path for a batch of 32 sequences with blocks
+of 8 (7 drafted tokens each), a 4,096-token window and the drafter's head
+layout (40 query / 8 KV heads x 128), over a 151,936-token vocabulary:
+
+  dflash_context_fuse   the up to 8 newly verified tokens of every sequence
+                        (256 rows): [256 x 25600] x [25600 x 5120], RMSNorm,
+                        K/V projection for 5 layers, append to the rings
+  dflash_block_attn x5  one call per drafter layer, reading that layer's ring
+  dflash_topk           top-8, lse and a T=0.7 draft draw for all 256 rows
+  spec_verify           T=0.7 sampled verification of the 7 drafts + bonus
+
+Inputs are synthetic and seeded (block_drafting_context_amd.synthetic) and
+resident in HBM before timing: context lengths uniform in [512, 131072]
+(attention reads min(len, 4096) ring rows + 8 block rows), bf16 Q/K/V ~
+N(0,1)/sqrt(128), target logits ~ N(0, 2^2), drafter = target + N(0, 1).
+
+Prints one JSON line: drafted tokens/s (value), the roofline of the dominant
+kernel (block attention, HBM-bound) measured with HIP events on its stream
+inside the timed region, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import block_drafting_context_amd as dfl  # noqa: E402
+from block_drafting_context_amd import synthetic as syn  # noqa: E402
+
+B, G, HQ, HKV, D, W = 32, 8, 40, 8, 128, 4096
+V, TOPK, T = 151936, 8, 0.7
+LAYERS = 5
+N_TAPS, D_TGT, D_MODEL = 5, 5120, 5120
+CTX_LO, CTX_HI = 512, 131072
+HBM_PEAK_GBS = 8000.0
+SEED = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(dev):
+    cl = syn.ctx_lengths(B, CTX_LO, CTX_HI, SEED).to(dev)
+    rows = B * G
+    fz = syn.fuse_inputs(rows, N_TAPS, D_TGT, D_MODEL, LAYERS, HKV, D, SEED, device=dev)
+    ring = syn.normal((LAYERS, 2, B, HKV, W, D), SEED, "ring", std=1 / np.sqrt(D),
+                      dtype=torch.bfloat16, device=dev)
+    row_seq = torch.arange(B, device=dev, dtype=torch.int32).repeat_interleave(G)
+    row_pos = (cl.repeat_interleave(G) - G + torch.arange(G, device=dev).repeat(B)).to(torch.int64)
+    layers = []
+    for i in range(LAYERS):
+        s = SEED * 100 + i
+        std = 1 / np.sqrt(D)
+        layers.append({
+            "q": syn.normal((B, G, HQ, D), s, "q", std=std, dtype=torch.bfloat16, device=dev),
+            "k_blk": syn.normal((B, G, HKV, D), s, "k_blk", std=std, dtype=torch.bfloat16, device=dev),
+            "v_blk": syn.normal((B, G, HKV, D), s, "v_blk", std=std, dtype=torch.bfloat16, device=dev),
+            "out": torch.empty((B, G, HQ, D), dtype=torch.bfloat16, device=dev),
+        })
+    zt, zd = syn.logits_pair(B, G, V, 2.0, 1.0, SEED, device=dev)
+    seeds = syn.philox_seeds(B, 0, device=dev)
+    wl = {"ctx_len": cl, "fuse": fz, "ring": ring, "row_seq": row_seq, "row_pos": row_pos,
+          "layers": layers, "zt": zt, "zd": zd, "seeds": seeds}
+    wl["ws_attn"] = torch.empty(max(1, dfl.dflash_block_attn_workspace_size(B, G, HQ, HKV, D, W)),
+                                dtype=torch.uint8, device=dev)
+    wl["ws_topk"] = torch.empty(dfl.dflash_topk_workspace_size(B, G, V, TOPK), dtype=torch.uint8,
+                                device=dev)
+    wl["ws_verify"] = torch.empty(dfl.spec_verify_workspace_size(B, G, V), dtype=torch.uint8,
+                                  device=dev)
+    wl["ws_fuse"] = torch.empty(dfl.dflash_context_fuse_workspace_size(rows, N_TAPS, D_TGT, D_MODEL,
+                                                                       LAYERS, HKV, D),
+                                dtype=torch.uint8, device=dev)
+    wl["topk_out"] = {"idx": torch.empty((B, G, TOPK), dtype=torch.int32, device=dev),
+                      "val": torch.empty((B, G, TOPK), dtype=torch.float32, device=dev),
+                      "lse": torch.empty((B, G), dtype=torch.float64, device=dev),
+                      "draft": torch.empty((B, G), dtype=torch.int32, device=dev)}
+    wl["verify_out"] = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+                        "out_tokens": torch.empty((B, G), dtype=torch.int32, device=dev),
+                        "accepted": torch.empty((B, G - 1), dtype=torch.uint8, device=dev)}
+    return wl
+
+
+OPS = ["context_fuse"] + [f"block_attn_l{i}" for i in range(LAYERS)] + ["topk", "spec_verify"]
+
+
+def run_step(wl, step, stream, events=None):
+    """One pass of the path; if `events` is a list, a HIP event is recorded on
+    `stream` before every operation and after the last one."""
+    def mark():
+        if events is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            events.append(e)
+    fz = wl["fuse"]
+    mark()
+    dfl.dflash_context_fuse(fz["x"], fz["w_c"], fz["gain"], 1e-6, fz["w_kv"], wl["row_seq"],
+                            wl["row_pos"], wl["ring"], N_TAPS, workspace=wl["ws_fuse"],
+                            stream=stream)
+    for i, L in enumerate(wl["layers"]):
+        mark()
+        dfl.dflash_block_attn(L["q"], L["k_blk"], L["v_blk"], wl["ring"][i, 0], wl["ring"][i, 1],
+                              wl["ctx_len"], 1 / np.sqrt(D), out=L["out"], workspace=wl["ws_attn"],
+                              stream=stream)
+    mark()
+    tk = dfl.dflash_topk(wl["zd"], TOPK, T, seeds=wl["seeds"], step=step, outputs=wl["topk_out"],
+                         workspace=wl["ws_topk"], stream=stream)
+    mark()
+    dfl.spec_verify(wl["zt"], wl["zd"], tk["draft"], T, seeds=wl["seeds"], step=step,
+                    draft_lse=tk["lse"], outputs=wl["verify_out"], workspace=wl["ws_verify"],
+                    stream=stream)
+    mark()
+
+
+def algorithmic_bytes(ctx_len):
+    n = np.minimum(ctx_len, W)
+    attn = float(n.sum()) * HKV * D * 2 * 2 + B * G * HQ * D * 2 * 2 + B * G * HKV * D * 2 * 2
+    rows = B * G
+    kvc = LAYERS * 2 * HKV * D
+    fuse = rows * N_TAPS * D_TGT * 2 + D_MODEL * N_TAPS * D_TGT * 2 + kvc * D_MODEL * 2 + rows * kvc * 2
+    row_bytes = B * G * V * 4
+    return {"block_attn": attn, "topk": float(row_bytes), "spec_verify": float(row_bytes),
+            "context_fuse": float(fuse)}
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per block-attention launch from the committed counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(HERE, "profiles", "block_attn_b32_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_seq):
+    """The fp64 oracle, as it stands, on `n_seq` sequences of the same workload:
+    their 8 fused rows, 5 attention layers, top-k/draws and sampled verify."""
+    import oracle
+    threads = oracle.num_threads()
+    to64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    fz = wl["fuse"]
+    wc, wkv, g = to64(fz["w_c"]), to64(fz["w_kv"]), to64(fz["gain"])
+    ring = wl["ring"]
+    cl = wl["ctx_len"].cpu().numpy()
+    t0 = time.perf_counter()
+    for b in range(n_seq):
+        x = to64(fz["x"][b * G:(b + 1) * G])
+        oracle.context_fuse(x, wc, g, float(np.float32(1e-6)), wkv, np.zeros(G, int),
+                            np.arange(G), np.zeros((LAYERS, 2, 1, HKV, G, D)), LAYERS, HKV, D)
+        for i, L in enumerate(wl["layers"]):
+            oracle.block_attn(to64(L["q"][b:b + 1]), to64(L["k_blk"][b:b + 1]),
+                              to64(L["v_blk"][b:b + 1]), to64(ring[i, 0, b:b + 1]),
+                              to64(ring[i, 1, b:b + 1]), cl[b:b + 1], 1 / np.sqrt(D))
+        zd, zt = to64(wl["zd"][b:b + 1]), to64(wl["zt"][b:b + 1])
+        sd = np.array([b], dtype=np.uint64)
+        dr = oracle.draft_rows(zd, TOPK, float(np.float32(T)), seeds=sd)
+        oracle.spec_verify(zt, zd, dr["draft"][:, :G - 1], float(np.float32(T)), seeds=sd)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_seq * (G - 1) / dt, 3), "unit": "drafted tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {B} sequences, whole step (fuse 8 rows, 5 attention layers, "
+                      f"top-8 + draws, sampled verify), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seqs", type=int, default=2,
+                    help="sequences of the workload the CPU oracle baseline runs on")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no "
+              "multi-GPU mode (each sequence is independent; see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    dfl.load()
+    log(f"[bench] building workload B={B} gamma={G} W={W} V={V}")
+    wl = build_workload(dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for s in range(args.warmup):
+        run_step(wl, s, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    events = []
+    for s in range(args.steps):
+        run_step(wl, args.warmup + s, stream, events)
+    torch.cuda.synchronize()
+    nops = len(OPS)
+    per = np.zeros((args.steps, nops))
+    for s in range(args.steps):
+        for o in range(nops):
+            per[s, o] = events[s * (nops + 1) + o].elapsed_time(events[s * (nops + 1) + o + 1])
+    total_ms = events[0].elapsed_time(events[-1])
+    ms_step = total_ms / args.steps
+    drafted = B * (G - 1)
+    value = drafted * args.steps / (total_ms / 1e3)
+
+    ab = algorithmic_bytes(wl["ctx_len"].cpu().numpy())
+    op_us = {name: float(per[:, o].mean() * 1e3) for o, name in enumerate(OPS)}
+    attn_us = float(per[:, 1:1 + LAYERS].mean() * 1e3)
+    achieved = ab["block_attn"] / (attn_us * 1e-6) / 1e9
+    step_bytes = ab["context_fuse"] + LAYERS * ab["block_attn"] + ab["topk"] + ab["spec_verify"]
+    kernel_src = os.path.join(HERE, "block_drafting_context_amd", "csrc", "block_attn.hip")
+    traffic = traffic_from_profile(kernel_src)
+    acc = wl["verify_out"]["accept_len"].float().mean().item() + 1.0
+
+    log("[bench] cpu baseline")
+    cpu = cpu_baseline(wl, args.cpu_seqs) if args.cpu_seqs > 0 else None
+
+    res = {
+        "metric": "drafted tokens/s for block-attn+top-k+verify at B=32,γ=8,W=4096; % HBM peak",
+        "value": round(value, 1),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DFlash2 drafter serving step: context_fuse(256 rows) + 5 x block_attn "
+                        "+ top-k + sampled spec_verify",
+            "batch": B, "gamma": G, "window": W, "n_q": HQ, "n_kv": HKV, "d_head": D,
+            "vocab": V, "top_k": TOPK, "temperature": T, "attn_layers": LAYERS,
+            "ctx_len": f"uniform[{CTX_LO},{CTX_HI}]", "logits": "fp32",
+            "fuse": "[256x25600]x[25600x5120] + RMSNorm + [256x5120]x[5120x10240]",
+        },
+        "roofline": {
+            "kernel": "block_attn_bf16_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["block_attn"],
+            "avg_launch_us": round(attn_us, 2),
+        },
+        "breakdown_us": {k: round(v, 2) for k, v in op_us.items()},
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "attn_topk_verify_tok_s": round(drafted / ((LAYERS * attn_us + op_us["topk"] +
+                                                    op_us["spec_verify"]) * 1e-6), 1),
+        "mean_tau": round(acc, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

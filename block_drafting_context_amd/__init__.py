@@ -1,1 +1,260 @@
-"""MI355X-native DFlash2 block-drafting hot path (package under construction)."""
+"""MI355X (gfx950) DFlash2 block-drafting hot path: Python binding of libdflash.so.
+
+Each function below has the name of the C entry point it wraps (declared in
+include/dflash.h) and does argument marshalling only: shape/dtype checks,
+output and workspace allocation through torch, and the call on torch's current
+HIP stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  If the library has not been built (``python -m
+block_drafting_context_amd.build``), importing the binding's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DFlashError", "lib_path", "load", "dflash_status_string", "dflash_version",
+    "dflash_block_attn", "dflash_block_attn_workspace_size",
+    "dflash_topk", "dflash_topk_workspace_size",
+    "spec_verify", "spec_verify_workspace_size",
+    "dflash_context_fuse", "dflash_context_fuse_workspace_size",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libdflash.so")
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "dflash_status_string", "dflash_version",
+    "dflash_block_attn_workspace_size", "dflash_block_attn",
+    "dflash_topk_workspace_size", "dflash_topk",
+    "spec_verify_workspace_size", "spec_verify",
+    "dflash_context_fuse_workspace_size", "dflash_context_fuse",
+)
+
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+
+_vp, _i, _sz, _f, _u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_uint64
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = dflash_status_string(status) if _lib is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libdflash.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"libdflash.so not found at {lib_path}; build it with "
+                           "`python -m block_drafting_context_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    sig = {
+        "dflash_status_string": (ctypes.c_char_p, [_i]),
+        "dflash_version": (_i, []),
+        "dflash_block_attn_workspace_size": (_sz, [_i] * 7),
+        "dflash_block_attn": (_i, [_vp] * 6 + [_f, _vp, _vp, _i] + [_i] * 6 + [_vp, _sz, _vp]),
+        "dflash_topk_workspace_size": (_sz, [_i] * 4),
+        "dflash_topk": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "spec_verify_workspace_size": (_sz, [_i] * 3),
+        "spec_verify": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
+                             _vp, _sz, _vp]),
+        "dflash_context_fuse_workspace_size": (_sz, [_i] * 7),
+        "dflash_context_fuse": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp] + [_i] * 9 +
+                                [_vp, _sz, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def dflash_status_string(status: int) -> str:
+    return load().dflash_status_string(int(status)).decode()
+
+
+def dflash_version() -> int:
+    return int(load().dflash_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {nbytes}")
+    return workspace, workspace.numel()
+
+
+def _call(fn_name, *args):
+    rc = getattr(load(), fn_name)(*args)
+    if rc != 0:
+        raise DFlashError(fn_name, rc)
+
+
+# ------------------------------------------------------------------ attention
+def dflash_block_attn_workspace_size(batch, gamma, n_q, n_kv, d_head, window, dtype=DTYPE_BF16):
+    return int(load().dflash_block_attn_workspace_size(batch, gamma, n_q, n_kv, d_head, window,
+                                                       dtype))
+
+
+def dflash_block_attn(q, k_blk, v_blk, k_ring, v_ring, ctx_len, scale=None, out=None,
+                      want_lse=False, lse=None, workspace=None, stream=None):
+    """Block-draft attention of one draft layer.
+
+    q [B,G,HQ,D]; k_blk, v_blk [B,G,HKV,D]; k_ring, v_ring [B,HKV,W,D] (bf16 or
+    fp32, all the same); ctx_len [B] int64.  Returns out [B,G,HQ,D] (and lse
+    [B,G,HQ] fp32 if asked)."""
+    B, G, HQ, D = q.shape
+    HKV = k_blk.shape[2]
+    W = k_ring.shape[2]
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    dev = q.device
+    for t, n, s in ((q, "q", (B, G, HQ, D)), (k_blk, "k_blk", (B, G, HKV, D)),
+                    (v_blk, "v_blk", (B, G, HKV, D)), (k_ring, "k_ring", (B, HKV, W, D)),
+                    (v_ring, "v_ring", (B, HKV, W, D))):
+        _need(t, n, dt, s, dev)
+    _need(ctx_len, "ctx_len", torch.int64, (B,), dev)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dtype_code = DTYPE_BF16 if dt == torch.bfloat16 else DTYPE_FP32
+    if out is None:
+        out = torch.empty((B, G, HQ, D), dtype=dt, device=dev)
+    _need(out, "out", dt, (B, G, HQ, D), dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, G, HQ), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, G, HQ), dev)
+    ws, wsb = _workspace(dflash_block_attn_workspace_size(B, G, HQ, HKV, D, W, dtype_code), dev,
+                         workspace)
+    _call("dflash_block_attn", _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ring), _ptr(v_ring),
+          _ptr(ctx_len), float(scale), _ptr(out), _ptr(lse), dtype_code, B, G, HQ, HKV, D, W,
+          _ptr(ws), wsb, _stream(stream))
+    return (out, lse) if lse is not None else out
+
+
+# ---------------------------------------------------------------------- top-k
+def dflash_topk_workspace_size(batch, gamma, vocab, k):
+    return int(load().dflash_topk_workspace_size(batch, gamma, vocab, k))
+
+
+def dflash_topk(logits, k, temperature, seeds=None, step=0, outputs=None, workspace=None,
+                stream=None):
+    """Drafter rows: logits [B,G,V] fp32 -> dict(idx [B,G,k] int32, val [B,G,k] fp32,
+    lse [B,G] fp64, draft [B,G] int32).  seeds: [B] int64 (bits read as uint64)."""
+    B, G, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (B, G, V), dev)
+    if seeds is not None:
+        _need(seeds, "seeds", torch.int64, (B,), dev)
+    o = outputs or {}
+    idx = o.get("idx") if o.get("idx") is not None else torch.empty((B, G, k), dtype=torch.int32, device=dev)
+    val = o.get("val") if o.get("val") is not None else torch.empty((B, G, k), dtype=torch.float32, device=dev)
+    lse = o.get("lse") if o.get("lse") is not None else torch.empty((B, G), dtype=torch.float64, device=dev)
+    draft = o.get("draft") if o.get("draft") is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, (B, G, k), dev)
+    _need(val, "val", torch.float32, (B, G, k), dev)
+    _need(lse, "lse", torch.float64, (B, G), dev)
+    _need(draft, "draft", torch.int32, (B, G), dev)
+    ws, wsb = _workspace(dflash_topk_workspace_size(B, G, V, k), dev, workspace)
+    _call("dflash_topk", _ptr(logits), B, G, V, int(k), float(temperature), _ptr(seeds),
+          int(step), _ptr(idx), _ptr(val), _ptr(lse), _ptr(draft), _ptr(ws), wsb, _stream(stream))
+    return {"idx": idx, "val": val, "lse": lse, "draft": draft}
+
+
+# --------------------------------------------------------------------- verify
+def spec_verify_workspace_size(batch, gamma, vocab):
+    return int(load().spec_verify_workspace_size(batch, gamma, vocab))
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=None, step=0,
+                draft_lse=None, outputs=None, workspace=None, stream=None):
+    """target_logits, draft_logits [B,G,V] fp32; draft_tokens [B,G] int32 (first G-1 used);
+    draft_lse [B,G] fp64 or None.  Returns dict(accept_len [B] int32, out_tokens [B,G] int32,
+    accepted [B,G-1] uint8)."""
+    B, G, V = target_logits.shape
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, G, V), dev)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, (B, G, V), dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
+    if draft_lse is not None:
+        _need(draft_lse, "draft_lse", torch.float64, (B, G), dev)
+    if seeds is not None:
+        _need(seeds, "seeds", torch.int64, (B,), dev)
+    o = outputs or {}
+    acc_len = o.get("accept_len") if o.get("accept_len") is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = o.get("out_tokens") if o.get("out_tokens") is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
+    accepted = o.get("accepted") if o.get("accepted") is not None else torch.empty((B, max(G - 1, 1)), dtype=torch.uint8, device=dev)
+    ws, wsb = _workspace(spec_verify_workspace_size(B, G, V), dev, workspace)
+    _call("spec_verify", _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+          _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
+          _ptr(out_tok), _ptr(accepted), B, G, V, _ptr(ws), wsb, _stream(stream))
+    return {"accept_len": acc_len, "out_tokens": out_tok, "accepted": accepted[:, :G - 1]}
+
+
+# --------------------------------------------------------------------- fusion
+def dflash_context_fuse_workspace_size(rows, n_taps, d_tgt, d_model, n_layers, n_kv, d_head):
+    return int(load().dflash_context_fuse_workspace_size(rows, n_taps, d_tgt, d_model, n_layers,
+                                                         n_kv, d_head))
+
+
+def dflash_context_fuse(taps, w_c, rms_gain, eps, w_kv, row_seq, row_pos, kv_ring, n_taps,
+                        h_t_out=None, workspace=None, stream=None):
+    """taps [rows, n_taps*d_tgt] bf16; w_c [d_model, n_taps*d_tgt] bf16; rms_gain [d_model]
+    fp32; w_kv [n_layers*2*n_kv*d_head, d_model] bf16; row_seq [rows] int32; row_pos [rows]
+    int64; kv_ring [n_layers, 2, B, n_kv, W, d_head] bf16 (updated in place)."""
+    rows, kx = taps.shape
+    d_model = w_c.shape[0]
+    NL, two, B, NKV, W, DH = kv_ring.shape
+    dev = taps.device
+    if two != 2 or kx % n_taps:
+        raise ValueError("bad shapes")
+    _need(taps, "taps", torch.bfloat16, (rows, kx), dev)
+    _need(w_c, "w_c", torch.bfloat16, (d_model, kx), dev)
+    _need(rms_gain, "rms_gain", torch.float32, (d_model,), dev)
+    _need(w_kv, "w_kv", torch.bfloat16, (NL * 2 * NKV * DH, d_model), dev)
+    _need(row_seq, "row_seq", torch.int32, (rows,), dev)
+    _need(row_pos, "row_pos", torch.int64, (rows,), dev)
+    _need(kv_ring, "kv_ring", torch.bfloat16, None, dev)
+    if h_t_out is not None:
+        _need(h_t_out, "h_t_out", torch.bfloat16, (rows, d_model), dev)
+    ws, wsb = _workspace(dflash_context_fuse_workspace_size(rows, n_taps, kx // n_taps, d_model,
+                                                            NL, NKV, DH), dev, workspace)
+    _call("dflash_context_fuse", _ptr(taps), _ptr(w_c), _ptr(rms_gain), float(eps), _ptr(w_kv),
+          _ptr(row_seq), _ptr(row_pos), _ptr(kv_ring), _ptr(h_t_out), rows, n_taps, kx // n_taps,
+          d_model, NL, NKV, DH, W, B, _ptr(ws), wsb, _stream(stream))
+    return kv_ring

@@ -1,0 +1,594 @@
+// block_attn.hip -- block-draft attention for gfx950.
+//
+// "DFlash vs DFlash 2", "DFlash: generate the block all at once" and
+// "Conditioning on the target model" (Q_i, K_i, V_i equation): the block's
+// queries attend without a causal mask to the context window and to the
+// block's own keys.  "Beam 1.0 DFlash2", "Model": 40 query heads share 8 KV
+// heads of dimension 128; the window holds the last 4,096 context tokens.
+//
+// bf16 path.  One workgroup (4 waves) owns one (sequence, KV head, key split,
+// query-tile group).  The key sequence of a (sequence, KV head) is virtual:
+// index t < n_b reads ring slot t, t >= n_b reads block row t - n_b, so the
+// block keys are streamed like the window keys.  Every query row of the GQA
+// group (group * gamma rows, padded to 16) is a column of one MFMA tile, so
+// each K/V byte is fetched once and used by all query heads of its group.
+//
+// Per 32-key tile a wave
+//   1. has the tile's K rows in registers, already in the A-operand layout of
+//      v_mfma_f32_16x16x32_bf16 (each lane reads 64 contiguous bytes of rows),
+//      and the tile's V rows in registers (4 tokens x 8 dims per lane);
+//   2. issues the loads of its next tile (register double buffer);
+//   3. writes V transposed into its private LDS tile (8-byte stores);
+//   4. computes S^T = K Q^T (keys x query rows) with MFMA, fp32;
+//   5. runs the online softmax in base 2 (column max across the 4 lane
+//      groups, rescale of the running sum and of O^T);
+//   6. packs P^T to bf16 straight from the S^T accumulator layout and
+//      accumulates O^T += V^T P^T with MFMA, reading V^T from LDS.
+// The four waves of a workgroup take interleaved tiles and are merged
+// through LDS at the end; key splits are merged by a second kernel.
+//
+// fp32 path (small shapes): one wave per query, scores in LDS, exact expf.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace dfl {
+namespace {
+
+constexpr int kTile = 32;          // keys per wave iteration
+constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kVtStride = kTile + 4;  // bf16 per V^T row in LDS (pad against bank conflicts)
+constexpr int kMaxNT = 4;          // query tiles (of 16 rows) per workgroup
+constexpr int kCUs = 256;          // MI355X compute units
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* kb;
+    const uint16_t* vb;
+    const uint16_t* kr;
+    const uint16_t* vr;
+    const int64_t* ctx_len;
+    float scale_log2;  // softmax scale * log2(e)
+    uint16_t* out;
+    float* lse;
+    float* part_o;   // [B*HKV][n_splits][n_qt*16][D]
+    float* part_ml;  // [B*HKV][n_splits][n_qt*16][2]  (max, sum), base 2
+    int B, G, HQ, HKV, W, group, nrows, n_qt, n_splits, nt_per_group;
+};
+
+__device__ __forceinline__ const uint16_t* key_row(const uint16_t* ring, const uint16_t* blk,
+                                                   int b, int kvh, int t, int n, int HKV,
+                                                   int W, int G, int D) {
+    return t < n ? ring + ((size_t)((size_t)b * HKV + kvh) * W + t) * D
+                 : blk + ((size_t)((size_t)b * G + (t - n)) * HKV + kvh) * D;
+}
+
+template <int D>
+struct TileRegs {
+    u32x4 k[2][D / 32];         // [16-key subtile][k-step]  A operand of S^T = K Q^T
+    u32x4 v[D / 64][4];         // [combo][token in group]   8 dims of 4 tokens
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const AttnArgs& a, int b, int kvh,
+                                          int n, int tb, int t1, int lane) {
+    const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int t = tb + st * 16 + i16;
+        const bool ok = t < t1;
+        const uint16_t* row = key_row(a.kr, a.kb, b, kvh, ok ? t : 0, n, a.HKV, a.W, a.G, D);
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            r.k[st][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 32 + g * 8) : z;
+        }
+    }
+    const int tg = lane & 7;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        const int dg = (lane >> 3) + 8 * c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = tb + 4 * tg + e;
+            const bool ok = t < t1;
+            const uint16_t* row = key_row(a.vr, a.vb, b, kvh, ok ? t : 0, n, a.HKV, a.W, a.G, D);
+            u32x4 z = {0u, 0u, 0u, 0u};
+            r.v[c][e] = ok ? *reinterpret_cast<const u32x4*>(row + dg * 8) : z;
+        }
+    }
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int NT>
+__global__ void __launch_bounds__(256, 1) block_attn_bf16_kernel(AttnArgs a) {
+    constexpr int DT = D / 16;  // 16-dim tiles of O^T
+    constexpr int KS = D / 32;  // k-steps of S^T
+    __shared__ __attribute__((aligned(16))) unsigned char smem[
+        (kWaves * D * kVtStride * 2) > (2 * NT * 16 * D * 4 + kWaves * NT * 16 * 2 * 4)
+            ? (kWaves * D * kVtStride * 2)
+            : (2 * NT * 16 * D * 4 + kWaves * NT * 16 * 2 * 4)];
+
+    const int split = blockIdx.x;
+    const int bk = blockIdx.y;
+    const int b = bk / a.HKV, kvh = bk % a.HKV;
+    const int qt0 = blockIdx.z * a.nt_per_group;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4, i16 = lane & 15;
+
+    const int64_t cl = a.ctx_len[b];
+    const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
+    const int total = n + a.G;
+    int per = (total + a.n_splits - 1) / a.n_splits;
+    per = (per + kTile - 1) / kTile * kTile;
+    const int t0 = split * per;
+    const int t1 = min(t0 + per, total);
+
+    // Q^T operands: B[k = dims of (s, g)][col = query row]
+    u32x4 qreg[NT][KS];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+        const int j = (qt0 + qt) * 16 + i16;
+        const bool ok = (qt0 + qt) < a.n_qt && j < a.nrows;
+        const int r = ok ? j / a.group : 0, hl = ok ? j % a.group : 0;
+        const uint16_t* qrow = a.q + ((size_t)((size_t)b * a.G + r) * a.HQ + kvh * a.group + hl) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[qt][s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
+        }
+    }
+
+    f32x4 o[DT][NT];
+    float m[NT], l[NT];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+        m[qt] = -INFINITY;
+        l[qt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * D * kVtStride;
+
+    TileRegs<D> cur, nxt;
+    int tb = t0 + wave * kTile;
+    if (tb < t1) load_tile<D>(cur, a, b, kvh, n, tb, t1, lane);
+
+    for (; tb < t1; tb += kWaves * kTile) {
+        const int tbn = tb + kWaves * kTile;
+        if (tbn < t1) load_tile<D>(nxt, a, b, kvh, n, tbn, t1, lane);
+
+        // (3) V^T into this wave's LDS tile: dims 8*dg+i, tokens 4*tg..4*tg+3
+        wave_lds_sync();
+        {
+            const int tg = lane & 7;
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+                const int dg = (lane >> 3) + 8 * c;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t a0 = cur.v[c][0][w], a1 = cur.v[c][1][w];
+                    const uint32_t a2 = cur.v[c][2][w], a3 = cur.v[c][3][w];
+                    u32x2 lo, hi;
+                    lo[0] = (a0 & 0xffffu) | (a1 << 16);
+                    lo[1] = (a2 & 0xffffu) | (a3 << 16);
+                    hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+                    hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+                    const int d = dg * 8 + 2 * w;
+                    *reinterpret_cast<u32x2*>(vt + d * kVtStride + 4 * tg) = lo;
+                    *reinterpret_cast<u32x2*>(vt + (d + 1) * kVtStride + 4 * tg) = hi;
+                }
+            }
+        }
+
+        // (4) S^T = K Q^T
+        f32x4 sacc[2][NT];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, cur.k[st][s]),
+                        __builtin_bit_cast(bf16x8, qreg[qt][s]), acc, 0, 0, 0);
+                sacc[st][qt] = acc;
+            }
+
+        // (5) online softmax per query column
+        bf16x8 pb[NT];
+#pragma unroll
+        for (int qt = 0; qt < NT; ++qt) {
+            float x[8];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tb + st * 16 + g * 4 + i;
+                    x[st * 4 + i] = t < t1 ? sacc[st][qt][i] * a.scale_log2 : -INFINITY;
+                }
+            float tmax = x[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            const float mnew = fmaxf(m[qt], tmax);
+            const float muse = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = fast_exp2(m[qt] - muse);
+            float p[8], psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = fast_exp2(x[i] - muse);
+                psum += p[i];
+            }
+            l[qt] = l[qt] * alpha + psum;
+            m[qt] = mnew;
+            if (alpha != 1.f) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
+            }
+            u32x4 pk;
+            pk[0] = pack_bf16x2(p[0], p[1]);
+            pk[1] = pack_bf16x2(p[2], p[3]);
+            pk[2] = pack_bf16x2(p[4], p[5]);
+            pk[3] = pack_bf16x2(p[6], p[7]);
+            pb[qt] = __builtin_bit_cast(bf16x8, pk);
+        }
+
+        // (6) O^T += V^T P^T
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t* vrow = vt + (dt * 16 + i16) * kVtStride;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
+            u32x4 av;
+            av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
+            const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt)
+                o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[qt], o[dt][qt], 0, 0, 0);
+        }
+        cur = nxt;
+    }
+
+    // lane partial sums -> column sums (the 4 lane groups hold disjoint keys)
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+        l[qt] += __shfl_xor(l[qt], 16, kWave);
+        l[qt] += __shfl_xor(l[qt], 32, kWave);
+    }
+
+    // ---- merge the four waves (deterministic pairwise tree through LDS)
+    __syncthreads();
+    float* obuf = reinterpret_cast<float*>(smem);                      // [2][NT*16*D]
+    float* mlb = obuf + 2 * NT * 16 * D;                               // [4][NT*16][2]
+    if (g == 0) {
+#pragma unroll
+        for (int qt = 0; qt < NT; ++qt) {
+            mlb[(wave * NT * 16 + qt * 16 + i16) * 2 + 0] = m[qt];
+            mlb[(wave * NT * 16 + qt * 16 + i16) * 2 + 1] = l[qt];
+        }
+    }
+    __syncthreads();
+    float M[NT], L[NT];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+        float mm = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, mlb[(w * NT * 16 + qt * 16 + i16) * 2]);
+        const float muse = mm == -INFINITY ? 0.f : mm;
+        float ll = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            ll += mlb[(w * NT * 16 + qt * 16 + i16) * 2 + 1] *
+                  fast_exp2(mlb[(w * NT * 16 + qt * 16 + i16) * 2] - muse);
+        M[qt] = mm;
+        L[qt] = ll;
+        const float f = fast_exp2(m[qt] - muse);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
+    }
+    // element index of (dt, qt, i) in a wave's O^T registers: lane-major
+    auto oidx = [&](int dt, int qt, int i) { return ((dt * NT + qt) * 4 + i) * 64 + lane; };
+    if (wave >= 2) {
+        float* dst = obuf + (wave - 2) * NT * 16 * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[oidx(dt, qt, i)] = o[dt][qt][i];
+    }
+    __syncthreads();
+    if (wave < 2) {
+        const float* src = obuf + wave * NT * 16 * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[dt][qt][i] += src[oidx(dt, qt, i)];
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) obuf[oidx(dt, qt, i)] = o[dt][qt][i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[dt][qt][i] += obuf[oidx(dt, qt, i)];
+
+    // ---- write: final output (one split) or the split's partial
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+        const int j = (qt0 + qt) * 16 + i16;
+        if ((qt0 + qt) >= a.n_qt || j >= a.nrows) continue;
+        if (a.n_splits == 1) {
+            const int r = j / a.group, h = kvh * a.group + j % a.group;
+            const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
+            const float inv = 1.f / L[qt];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                u32x2 w2;
+                w2[0] = pack_bf16x2(o[dt][qt][0] * inv, o[dt][qt][1] * inv);
+                w2[1] = pack_bf16x2(o[dt][qt][2] * inv, o[dt][qt][3] * inv);
+                *reinterpret_cast<u32x2*>(a.out + row * D + dt * 16 + g * 4) = w2;
+            }
+            if (a.lse && g == 0) a.lse[row] = (M[qt] + __log2f(L[qt])) * (float)kLn2;
+        } else {
+            const size_t prow = ((size_t)bk * a.n_splits + split) * (a.n_qt * 16) + j;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4*>(a.part_o + prow * D + dt * 16 + g * 4) = o[dt][qt];
+            if (g == 0) {
+                a.part_ml[prow * 2 + 0] = M[qt];
+                a.part_ml[prow * 2 + 1] = L[qt];
+            }
+        }
+    }
+}
+
+// Merge key splits: O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// One workgroup per (sequence, KV head, query tile); 16 threads per row.
+template <int D>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+    const int bk = blockIdx.x, qt = blockIdx.y;
+    const int b = bk / a.HKV, kvh = bk % a.HKV;
+    const int jl = threadIdx.x >> 4, part = threadIdx.x & 15;
+    const int j = qt * 16 + jl;
+    if (j >= a.nrows) return;
+    const int S = a.n_splits;
+    const size_t base = (size_t)bk * S * (a.n_qt * 16) + j;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(base + (size_t)s * a.n_qt * 16) * 2]);
+    const float muse = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    constexpr int PER = D / 16;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const size_t prow = base + (size_t)s * a.n_qt * 16;
+        const float f = fast_exp2(a.part_ml[prow * 2] - muse);
+        L += a.part_ml[prow * 2 + 1] * f;
+        if (f == 0.f) continue;
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + prow * D + part * PER);
+#pragma unroll
+        for (int e = 0; e < PER / 4; ++e) {
+            const f32x4 v = src[e];
+            acc[4 * e + 0] += v[0] * f;
+            acc[4 * e + 1] += v[1] * f;
+            acc[4 * e + 2] += v[2] * f;
+            acc[4 * e + 3] += v[3] * f;
+        }
+    }
+    const float inv = 1.f / L;
+    const int r = j / a.group, h = kvh * a.group + j % a.group;
+    const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + row * D + part * PER);
+#pragma unroll
+    for (int e = 0; e < PER / 2; ++e) dst[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    if (a.lse && part == 0) a.lse[row] = (M + __log2f(L)) * (float)kLn2;
+}
+
+// ------------------------------------------------------------- fp32 path
+struct Attn32Args {
+    const float* q;
+    const float* kb;
+    const float* vb;
+    const float* kr;
+    const float* vr;
+    const int64_t* ctx_len;
+    float scale;
+    float* out;
+    float* lse;
+    int B, G, HQ, HKV, W, D;
+};
+
+constexpr int kMaxKeys32 = 4096 + 32;
+
+__global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
+    __shared__ float sc[kWaves][kMaxKeys32];
+    __shared__ float qs[kWaves][128];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int qi = blockIdx.x * kWaves + wave;  // (b, r, h) flattened
+    if (qi >= a.B * a.G * a.HQ) return;
+    const int h = qi % a.HQ, b = qi / (a.HQ * a.G);
+    const int kvh = h / (a.HQ / a.HKV);
+    const int64_t cl = a.ctx_len[b];
+    const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
+    const int total = n + a.G;
+    const int D = a.D;
+    const float* qrow = a.q + (size_t)qi * D;
+    for (int d = lane; d < D; d += kWave) qs[wave][d] = qrow[d];
+    __builtin_amdgcn_wave_barrier();
+    float mx = -INFINITY;
+    for (int t = lane; t < total; t += kWave) {
+        const float* krow = t < n ? a.kr + ((size_t)((size_t)b * a.HKV + kvh) * a.W + t) * D
+                                  : a.kb + ((size_t)((size_t)b * a.G + (t - n)) * a.HKV + kvh) * D;
+        float s = 0.f;
+        for (int d = 0; d < D; ++d) s = fmaf(qs[wave][d], krow[d], s);
+        s *= a.scale;
+        sc[wave][t] = s;
+        mx = fmaxf(mx, s);
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int t = lane; t < total; t += kWave) {
+        const float p = expf(sc[wave][t] - mx);
+        sc[wave][t] = p;
+        sum += p;
+    }
+    sum = wave_sum(sum);
+    wave_lds_sync();
+    const float inv = 1.f / sum;
+    for (int d = lane; d < D; d += kWave) {
+        float acc = 0.f;
+        for (int t = 0; t < total; ++t) {
+            const float* vrow = t < n ? a.vr + ((size_t)((size_t)b * a.HKV + kvh) * a.W + t) * D
+                                      : a.vb + ((size_t)((size_t)b * a.G + (t - n)) * a.HKV + kvh) * D;
+            acc = fmaf(sc[wave][t], vrow[d], acc);
+        }
+        a.out[(size_t)qi * D + d] = acc * inv;
+    }
+    if (a.lse && lane == 0) a.lse[qi] = mx + logf(sum);
+}
+
+// --------------------------------------------------------------- planning
+struct AttnPlan {
+    int n_qt, nt, n_qgroups, n_splits;
+    size_t off_o, off_ml, bytes;
+};
+
+AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int window, int dtype) {
+    AttnPlan p{};
+    const int group = n_q / n_kv;
+    const int nrows = group * gamma;
+    p.n_qt = (nrows + 15) / 16;
+    p.n_qgroups = (p.n_qt + kMaxNT - 1) / kMaxNT;
+    p.nt = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
+    if (dtype != DFLASH_DTYPE_BF16) {
+        p.n_splits = 1;
+        p.bytes = 0;
+        return p;
+    }
+    const long units = (long)batch * n_kv * p.n_qgroups;
+    const long want = kCUs;  // one resident workgroup per CU at this register footprint
+    int splits = (int)((want + units - 1) / units);
+    const int max_splits = (window + gamma + kWaves * kTile - 1) / (kWaves * kTile);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    p.n_splits = splits;
+    Carve c;
+    if (splits > 1) {
+        const size_t rows = (size_t)batch * n_kv * splits * p.n_qt * 16;
+        p.off_o = c.take<float>(rows * d_head);
+        p.off_ml = c.take<float>(rows * 2);
+    }
+    p.bytes = c.total();
+    return p;
+}
+
+template <int D, int NT>
+void launch_bf16(const AttnArgs& a, int n_qgroups, hipStream_t st) {
+    dim3 grid(a.n_splits, a.B * a.HKV, n_qgroups);
+    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NT>), grid, dim3(256), 0, st, a);
+}
+
+template <int D>
+void launch_bf16_nt(const AttnArgs& a, int nt, int n_qgroups, hipStream_t st) {
+    switch (nt) {
+        case 1: launch_bf16<D, 1>(a, n_qgroups, st); break;
+        case 2: launch_bf16<D, 2>(a, n_qgroups, st); break;
+        case 3: launch_bf16<D, 3>(a, n_qgroups, st); break;
+        default: launch_bf16<D, 4>(a, n_qgroups, st); break;
+    }
+}
+
+}  // namespace
+}  // namespace dfl
+
+using namespace dfl;
+
+extern "C" size_t dflash_block_attn_workspace_size(int batch, int gamma, int n_q, int n_kv,
+                                                   int d_head, int window, int dtype) {
+    if (batch < 0 || gamma < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || window < 1) return 0;
+    return plan_attn(batch, gamma, n_q, n_kv, d_head, window, dtype).bytes;
+}
+
+extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
+                                 const void* k_ring, const void* v_ring, const int64_t* ctx_len,
+                                 float scale, void* out, float* lse, int dtype, int batch,
+                                 int gamma, int n_q, int n_kv, int d_head, int window,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || gamma < 1 || n_q < 1 || n_kv < 1 || d_head < 1 || window < 1)
+        return DFLASH_ERR_SHAPE;
+    if (n_q % n_kv != 0 || !(scale > 0.f) || !std::isfinite(scale)) return DFLASH_ERR_SHAPE;
+    if (dtype != DFLASH_DTYPE_BF16 && dtype != DFLASH_DTYPE_FP32) return DFLASH_ERR_SHAPE;
+    if (batch == 0) return DFLASH_OK;
+    if (!q || !k_blk || !v_blk || !k_ring || !v_ring || !ctx_len || !out) return DFLASH_ERR_NULL;
+    if (gamma > 32 || window % 64 != 0) return DFLASH_ERR_UNSUPPORTED;
+    if (dtype == DFLASH_DTYPE_BF16 && d_head != 64 && d_head != 128) return DFLASH_ERR_UNSUPPORTED;
+    if (dtype == DFLASH_DTYPE_FP32 && (d_head > 128 || window + gamma > kMaxKeys32))
+        return DFLASH_ERR_UNSUPPORTED;
+    const AttnPlan p = plan_attn(batch, gamma, n_q, n_kv, d_head, window, dtype);
+    if (p.bytes > 0) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < p.bytes)
+            return DFLASH_ERR_WORKSPACE;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == DFLASH_DTYPE_FP32) {
+        Attn32Args a{static_cast<const float*>(q), static_cast<const float*>(k_blk),
+                     static_cast<const float*>(v_blk), static_cast<const float*>(k_ring),
+                     static_cast<const float*>(v_ring), ctx_len, scale,
+                     static_cast<float*>(out), lse, batch, gamma, n_q, n_kv, window, d_head};
+        const int nq = batch * gamma * n_q;
+        hipLaunchKernelGGL(block_attn_f32_kernel, dim3((nq + kWaves - 1) / kWaves), dim3(256), 0,
+                           st, a);
+        return launch_status();
+    }
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kb = static_cast<const uint16_t*>(k_blk);
+    a.vb = static_cast<const uint16_t*>(v_blk);
+    a.kr = static_cast<const uint16_t*>(k_ring);
+    a.vr = static_cast<const uint16_t*>(v_ring);
+    a.ctx_len = ctx_len;
+    a.scale_log2 = scale * kLog2e;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = p.n_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+    a.part_ml = p.n_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+    a.B = batch; a.G = gamma; a.HQ = n_q; a.HKV = n_kv; a.W = window;
+    a.group = n_q / n_kv;
+    a.nrows = a.group * gamma;
+    a.n_qt = p.n_qt;
+    a.n_splits = p.n_splits;
+    a.nt_per_group = p.nt;
+    if (d_head == 128) launch_bf16_nt<128>(a, p.nt, p.n_qgroups, st);
+    else launch_bf16_nt<64>(a, p.nt, p.n_qgroups, st);
+    int rc = launch_status();
+    if (rc != DFLASH_OK || p.n_splits == 1) return rc;
+    dim3 grid(batch * n_kv, p.n_qt);
+    if (d_head == 128) hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, st, a);
+    return launch_status();
+}

@@ -1,0 +1,132 @@
+// common.hpp -- device and host helpers shared by the gfx950 kernels of
+// libdflash.so.  Nothing here is shared with the CPU reference.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dflash.h"
+
+namespace dfl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- numbers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// two floats -> packed bf16 pair (lo = a), round to nearest even (hardware cvt)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
+
+// ------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+// inclusive prefix sum over the wave's lanes (lane order)
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        double o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// (value desc, index asc) ordering: true if (va, ia) ranks ahead of (vb, ib)
+__device__ __forceinline__ bool ranks_ahead(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && (unsigned)ia < (unsigned)ib);
+}
+
+// wave-wide best (value desc, index asc); idx -1 = empty (ranks last via unsigned compare)
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        float ov = __shfl_xor(v, m, kWave);
+        int oi = __shfl_xor(i, m, kWave);
+        if (ranks_ahead(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+// ------------------------------------------------------------------ Philox
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// two-multiplier S-box over a 4x64-bit counter with a Weyl key schedule.
+__device__ __forceinline__ void philox4x64_10(uint64_t& x0, uint64_t& x1, uint64_t& x2,
+                                              uint64_t& x3, uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t hi0 = __umul64hi(M0, x0), lo0 = M0 * x0;
+        const uint64_t hi1 = __umul64hi(M1, x2), lo1 = M1 * x2;
+        const uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+        x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
+        k0 += W0; k1 += W1;
+    }
+}
+
+// uniform in [0,1): key (seed, 0), counter (step, b, row, purpose), top 53 bits
+__device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t step, uint64_t b,
+                                                 uint64_t row, uint64_t purpose) {
+    uint64_t x0 = step, x1 = b, x2 = row, x3 = purpose;
+    philox4x64_10(x0, x1, x2, x3, seed, 0);
+    return (double)(x0 >> 11) * 0x1.0p-53;
+}
+
+enum Purpose : uint64_t { kDraftDraw = 0, kAcceptTest = 1, kFinalDraw = 2 };
+
+// ----------------------------------------------------------------- host side
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Bump allocator over the caller's workspace (offsets only, no allocation).
+struct Carve {
+    size_t off = 0;
+    template <class T>
+    size_t take(size_t count) {
+        const size_t at = align_up(off, 256);
+        off = at + count * sizeof(T);
+        return at;
+    }
+    size_t total() const { return align_up(off, 256); }
+};
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+}  // namespace dfl

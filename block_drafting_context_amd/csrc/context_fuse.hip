@@ -1,0 +1,253 @@
+// context_fuse.hip -- context fusion and context K/V append, for gfx950.
+//
+// "DFlash vs DFlash 2", "Conditioning on the target model", equation for H_t:
+// the tapped target states of each new token are concatenated, projected by
+// W_c and RMS-normalised; equation for K_i, V_i: the context half of every
+// draft layer's keys and values is W_i^K H_t, W_i^V H_t.
+//
+//   1. gemm  : P1[s] = X[:, Ks] W_c[:, Ks]^T      (bf16 MFMA, fp32 partials)
+//   2. norm  : H_t = RMSNorm(sum_s P1[s]) * g   -> bf16
+//   3. gemm  : P2[s] = H_t[:, Ks] W_kv[:, Ks]^T
+//   4. append: kv_ring[slot(row)] = bf16(sum_s P2[s])
+//
+// The GEMM is "NT": both operands are K-contiguous (weights stored one row
+// per output feature), so global loads and the MFMA operand layout agree.
+// Workgroup tile 128 x 128, K-tile 64, four waves of 64 x 64 built from
+// v_mfma_f32_16x16x32_bf16; LDS double buffer with an XOR swizzle of the
+// 16-byte chunks of each 128-byte row (conflict-free ds_read_b128); split-K
+// across workgroups to fill the 256 CUs when M is only a few hundred rows.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace dfl {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kCUs = 256;
+
+struct GemmArgs {
+    const uint16_t* A;  // [M, K]
+    const uint16_t* B;  // [N, K]
+    float* C;           // [S, M, N]
+    int M, N, K, kps;   // kps = K per split
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+__global__ void __launch_bounds__(256, 2) gemm_nt_bf16_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) u32x4 sa[2][BM * 8];
+    __shared__ __attribute__((aligned(16))) u32x4 sb[2][BN * 8];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
+    const int kbeg = split * g.kps, kend = kbeg + g.kps;
+    const int i16 = lane & 15, grp = lane >> 4;
+
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = tid + 256 * i, row = id >> 3, ch = id & 7;
+            const int m = m0 + row;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            ra[i] = m < g.M ? *reinterpret_cast<const u32x4*>(g.A + (size_t)m * g.K + k0 + ch * 8) : z;
+            rb[i] = *reinterpret_cast<const u32x4*>(g.B + (size_t)(n0 + row) * g.K + k0 + ch * 8);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = tid + 256 * i, row = id >> 3, ch = id & 7;
+            sa[buf][swz(row, ch)] = ra[i];
+            sb[buf][swz(row, ch)] = rb[i];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    gload(kbeg);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+        const bool more = k0 + BK < kend;
+        if (more) gload(k0 + BK);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ra_row = wm * 64 + i * 16 + i16;
+                const int rb_row = wn * 64 + i * 16 + i16;
+                fa[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(ra_row, s * 4 + grp)]);
+                fb[i] = __builtin_bit_cast(bf16x8, sb[buf][swz(rb_row, s * 4 + grp)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+    // acc[i][j]: rows m0+wm*64+i*16+4*grp+e, column n0+wn*64+j*16+i16
+    float* C = g.C + (size_t)split * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = m0 + wm * 64 + i * 16 + 4 * grp + e;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) C[(size_t)m * g.N + n0 + wn * 64 + j * 16 + i16] = acc[i][j][e];
+        }
+}
+
+// H_t[r] = bf16( g * y / sqrt(mean(y^2) + eps) ),  y = sum_s P1[s][r]
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* P, int S, int M, int N,
+                                                      const float* gain, float eps,
+                                                      uint16_t* H, uint16_t* h_out) {
+    extern __shared__ float y[];
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    float ss = 0.f;
+    for (int n = tid; n < N; n += 256) {
+        float v = 0.f;
+        for (int s = 0; s < S; ++s) v += P[((size_t)s * M + r) * N + n];
+        y[n] = v;
+        ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float inv = 1.f / sqrtf(tot / (float)N + eps);
+    for (int n = tid; n < N; n += 256) {
+        const uint16_t hb = f32_to_bf16_bits(y[n] * inv * gain[n]);
+        H[(size_t)r * N + n] = hb;
+        if (h_out) h_out[(size_t)r * N + n] = hb;
+    }
+}
+
+// kv_ring[i, t, seq, h, pos % W, d] = bf16(sum_s P2[s][r][c])
+__global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int S, int M, int NC,
+                                                        const int32_t* row_seq,
+                                                        const int64_t* row_pos, uint16_t* ring,
+                                                        int B, int NKV, int DH, int W) {
+    const int r = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 2;
+    if (c >= NC) return;
+    float v0 = 0.f, v1 = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float* p = P + ((size_t)s * M + r) * NC + c;
+        v0 += p[0];
+        v1 += p[1];
+    }
+    const int seq = row_seq[r];
+    const int64_t pos = row_pos[r];
+    if (seq < 0 || seq >= B || pos < 0) return;  // violated precondition: row skipped
+    const int64_t slot = pos % W;
+    const int d = c % DH, h = (c / DH) % NKV, lt = c / (DH * NKV);  // lt = layer*2 + t
+    const size_t at = ((((size_t)lt * B + seq) * NKV + h) * W + (size_t)slot) * DH + d;
+    *reinterpret_cast<uint32_t*>(ring + at) = pack_bf16x2(v0, v1);
+}
+
+int pick_splits(int M, int N, int K) {
+    const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
+    const int kt = K / BK;
+    int best = 1;
+    for (int s = 1; s <= 32 && s <= kt; ++s) {
+        if (kt % s) continue;
+        best = s;
+        if (tiles * s >= 2L * kCUs) break;
+    }
+    return best;
+}
+
+struct FuseLayout {
+    int s1, s2;
+    size_t p1, h, p2, bytes;
+};
+
+FuseLayout fuse_layout(int rows, int kx, int d_model, int nkvc) {
+    FuseLayout L{};
+    L.s1 = pick_splits(rows, d_model, kx);
+    L.s2 = pick_splits(rows, nkvc, d_model);
+    Carve c;
+    L.p1 = c.take<float>((size_t)L.s1 * rows * d_model);
+    L.h = c.take<uint16_t>((size_t)rows * d_model);
+    L.p2 = c.take<float>((size_t)L.s2 * rows * nkvc);
+    L.bytes = c.total();
+    return L;
+}
+
+void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K, int S,
+                 hipStream_t st) {
+    GemmArgs g{A, B, C, M, N, K, K / S};
+    dim3 grid(N / BN, (M + BM - 1) / BM, S);
+    hipLaunchKernelGGL(gemm_nt_bf16_kernel, grid, dim3(256), 0, st, g);
+}
+
+}  // namespace
+}  // namespace dfl
+
+using namespace dfl;
+
+extern "C" size_t dflash_context_fuse_workspace_size(int rows, int n_taps, int d_tgt, int d_model,
+                                                     int n_layers, int n_kv, int d_head) {
+    if (rows < 1 || n_taps < 1 || d_tgt < 1 || d_model < 1 || n_layers < 1 || n_kv < 1 ||
+        d_head < 1)
+        return 0;
+    const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
+    if (kx % BK || d_model % BN || d_model % BK || nkvc % BN) return 0;
+    return fuse_layout(rows, (int)kx, d_model, (int)nkvc).bytes;
+}
+
+extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, const float* rms_gain,
+                                   float eps, const uint16_t* w_kv, const int32_t* row_seq,
+                                   const int64_t* row_pos, uint16_t* kv_ring, uint16_t* h_t_out,
+                                   int rows, int n_taps, int d_tgt, int d_model, int n_layers,
+                                   int n_kv, int d_head, int window, int batch, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (rows < 1 || n_taps < 1 || d_tgt < 1 || d_model < 1 || n_layers < 1 || n_kv < 1 ||
+        d_head < 1 || window < 1 || batch < 1)
+        return DFLASH_ERR_SHAPE;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return DFLASH_ERR_SHAPE;
+    if (!taps || !w_c || !rms_gain || !w_kv || !row_seq || !row_pos || !kv_ring)
+        return DFLASH_ERR_NULL;
+    const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
+    if (kx % BK || d_model % BN || nkvc % BN || d_model > 8192 || kx > (1L << 30) ||
+        nkvc > (1L << 30) || d_head % 2)
+        return DFLASH_ERR_UNSUPPORTED;
+    const FuseLayout L = fuse_layout(rows, (int)kx, d_model, (int)nkvc);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.bytes)
+        return DFLASH_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    float* P1 = reinterpret_cast<float*>(ws + L.p1);
+    uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
+    float* P2 = reinterpret_cast<float*>(ws + L.p2);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    launch_gemm(taps, w_c, P1, rows, d_model, (int)kx, L.s1, st);
+    int rc = launch_status();
+    if (rc) return rc;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), (size_t)d_model * sizeof(float), st,
+                       P1, L.s1, rows, d_model, rms_gain, eps, H, h_t_out);
+    rc = launch_status();
+    if (rc) return rc;
+    launch_gemm(H, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
+    rc = launch_status();
+    if (rc) return rc;
+    dim3 grid((unsigned)((nkvc / 2 + 255) / 256), rows);
+    hipLaunchKernelGGL(kv_append_kernel, grid, dim3(256), 0, st, P2, L.s2, rows, (int)nkvc,
+                       row_seq, row_pos, kv_ring, batch, n_kv, d_head, window);
+    return launch_status();
+}

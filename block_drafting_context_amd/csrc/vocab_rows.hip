@@ -1,0 +1,787 @@
+// vocab_rows.hip -- per-position top-k, drafted-token draws and lossless
+// verification over 151,936-entry logits rows, for gfx950.
+//
+// "DFlash vs DFlash 2", "The candidate selector": top-k candidates per block
+// position.  "The problem: one expensive token at a time": the drafter
+// proposes y ~ q; the target keeps the longest valid prefix (greedy: drafts
+// equal to its argmax; sampled: accept with probability min(1, p/q)),
+// corrects the first rejection from [p - q]_+ and adds a bonus token when
+// every draft survives.
+//
+// Every pass over a row is one streaming read, split into 2,048-element
+// segments.  A wave owns a run of consecutive segments of one row and, per
+// segment, holds all 32 of each lane's elements in registers (8 float4
+// loads issued together), so it can take an exact wave-uniform segment
+// maximum m_s before exponentiating.  Per segment it can produce
+//   * s_s = sum 2^((z - m_s) * log2(e)/T)   (fp32 pairwise sums, fp64 across)
+//   * the wave's argmax, or
+//   * top-k candidates: elements beating the wave's running k-th best are
+//     compacted into an LDS buffer; the list is rebuilt by k rounds of a
+//     wave-wide (value desc, index asc) reduction when the buffer fills.
+// An inverse-CDF draw then needs only the segment sums plus one re-read of
+// the single 2,048-element segment holding the crossing, recomputing the
+// element weights with exactly the arithmetic that produced the sums.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace dfl {
+namespace {
+
+constexpr int kSeg = 2048;             // elements per segment (8 x 64 lanes x 4)
+constexpr int kIters = kSeg / 256;     // float4 loads per lane per segment
+constexpr int kCap = 256;              // top-k candidate buffer fill that triggers a rebuild
+constexpr int kBuf = kCap + 256;       // buffer size: one load group (4 x 64) of slack
+constexpr int kMaxCand = 4096;         // candidates merged per row by the finalize
+constexpr int kScanWaves = 4;          // waves per workgroup
+constexpr int kTargetWaves = 3072;     // waves per row-scan launch (~12 per CU)
+
+enum : int { kArgmax = 1, kSumExp = 2, kTopK = 4 };
+
+struct ScanArgs {
+    const float* z;  // [rows, V]
+    int rows, V, nseg, spw, wpr, k;
+    float c2;        // log2(e) / T
+    float* seg_m;    // [rows][nseg]
+    double* seg_s;   // [rows][nseg]
+    float* cand_v;   // [rows][wpr][k]
+    int* cand_i;
+};
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------- wave top-k state
+struct TopKState {
+    float* lv;   // [64] sorted list
+    int* li;
+    float* bv;   // [kCap + 64] candidate buffer
+    int* bi;
+    int cnt;     // buffer fill (wave-uniform)
+    int lcount;  // list length (wave-uniform)
+    float tv;    // filter: an element passes if it ranks ahead of (tv, ti)
+    int ti;
+};
+
+// Rebuild the sorted list from list + buffer: k rounds of wave-wide best.
+__device__ __noinline__ void topk_compact(TopKState& s, int k, int lane) {
+    wave_lds_sync();
+    constexpr int NPL = (64 + kBuf + 63) / 64;
+    const int N = s.lcount + s.cnt;
+    float cv[NPL];
+    int ci[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int at = e * 64 + lane;
+        if (at < s.lcount) { cv[e] = s.lv[at]; ci[e] = s.li[at]; }
+        else if (at < N) { cv[e] = s.bv[at - s.lcount]; ci[e] = s.bi[at - s.lcount]; }
+        else { cv[e] = -INFINITY; ci[e] = -1; }
+    }
+    wave_lds_sync();
+    const int newcount = N < k ? N : k;
+    float lastv = -INFINITY;
+    int lasti = -1;
+    for (int r = 0; r < newcount; ++r) {
+        float bv = cv[0];
+        int bi = ci[0];
+#pragma unroll
+        for (int e = 1; e < NPL; ++e)
+            if (ranks_ahead(cv[e], ci[e], bv, bi)) { bv = cv[e]; bi = ci[e]; }
+        wave_best(bv, bi);
+#pragma unroll
+        for (int e = 0; e < NPL; ++e)
+            if (ci[e] == bi && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
+        if (lane == 0) { s.lv[r] = bv; s.li[r] = bi; }
+        lastv = bv;
+        lasti = bi;
+    }
+    wave_lds_sync();
+    s.lcount = newcount;
+    s.cnt = 0;
+    if (newcount == k) { s.tv = lastv; s.ti = lasti; }
+    else { s.tv = -INFINITY; s.ti = -1; }
+}
+
+// k-th largest of the 64 lane values (k <= 64): a safe first filter, since
+// k distinct elements are at least that large.
+__device__ float kth_of_lanes(float v, int k, int lane) {
+    float kth = -INFINITY;
+    for (int r = 0; r < k; ++r) {
+        float bv = v;
+        int bi = lane;
+        wave_best(bv, bi);
+        if (lane == bi) v = -INFINITY;
+        kth = bv;
+    }
+    return kth;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
+    __shared__ float s_lv[kScanWaves][64];
+    __shared__ int s_li[kScanWaves][64];
+    __shared__ float s_bv[kScanWaves][kBuf];
+    __shared__ int s_bi[kScanWaves][kBuf];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * kScanWaves + wave;
+    const int row = gw / a.wpr, wr = gw % a.wpr;
+    if (row >= a.rows) return;
+    const int seg0 = wr * a.spw;
+    const int seg1 = min(seg0 + a.spw, a.nseg);
+    const float* zr = a.z + (size_t)row * a.V;
+
+    float best_v = -INFINITY;
+    int best_i = -1;
+    TopKState tk;
+    if (MODE & kTopK) {
+        tk.lv = s_lv[wave]; tk.li = s_li[wave];
+        tk.bv = s_bv[wave]; tk.bi = s_bi[wave];
+        tk.cnt = 0; tk.lcount = 0; tk.tv = -INFINITY; tk.ti = -1;
+    }
+
+    for (int seg = seg0; seg < seg1; ++seg) {
+        float v[kIters][4];
+        const int base = seg * kSeg + 4 * lane;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = base + it * 256;
+            if (e < a.V) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(zr + e);
+                v[it][0] = x[0]; v[it][1] = x[1]; v[it][2] = x[2]; v[it][3] = x[3];
+            } else {
+                v[it][0] = v[it][1] = v[it][2] = v[it][3] = -INFINITY;
+            }
+        }
+
+        if (MODE & kArgmax) {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (v[it][c] > best_v) { best_v = v[it][c]; best_i = base + it * 256 + c; }
+        }
+
+        float lane_m = -INFINITY;
+        if (MODE & (kSumExp | kTopK)) {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) lane_m = fmaxf(lane_m, v[it][c]);
+        }
+
+        if (MODE & kSumExp) {
+            const float m = wave_max(lane_m);
+            double s = 0.0;
+            if (m != -INFINITY) {
+#pragma unroll
+                for (int h = 0; h < kIters / 2; ++h) {
+                    float w[8];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            w[q * 4 + c] = fast_exp2((v[2 * h + q][c] - m) * a.c2);
+                    const float t = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+                    s += (double)t;
+                }
+            }
+            s = wave_sum(s);
+            if (lane == 0) {
+                a.seg_m[(size_t)row * a.nseg + seg] = m;
+                a.seg_s[(size_t)row * a.nseg + seg] = s;
+            }
+        }
+
+        if (MODE & kTopK) {
+            if (tk.lcount == 0 && tk.cnt == 0) {
+                tk.tv = kth_of_lanes(lane_m, a.k, lane);
+                tk.ti = -1;  // ties with the filter value pass
+            }
+            bool lane_may = lane_m >= tk.tv;
+            if (ballot(lane_may)) {
+#pragma unroll
+                for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int idx = base + it * 256 + c;
+                        const bool pass = lane_may && idx < a.V &&
+                                          ranks_ahead(v[it][c], idx, tk.tv, tk.ti);
+                        const uint64_t mask = ballot(pass);
+                        if (mask) {
+                            if (pass) {
+                                const int pos = tk.cnt + lanes_below(mask);
+                                tk.bv[pos] = v[it][c];
+                                tk.bi[pos] = idx;
+                            }
+                            tk.cnt += __popcll(mask);
+                        }
+                    }
+                    if (tk.cnt > kCap) {
+                        topk_compact(tk, a.k, lane);
+                        lane_may = lane_m >= tk.tv;
+                    }
+                }
+            }
+        }
+    }
+
+    const size_t cbase = ((size_t)row * a.wpr + wr) * a.k;
+    if (MODE & kArgmax) {
+        wave_best(best_v, best_i);
+        if (lane == 0) { a.cand_v[cbase] = best_v; a.cand_i[cbase] = best_i; }
+    }
+    if (MODE & kTopK) {
+        if (tk.cnt > 0 || tk.lcount < a.k) topk_compact(tk, a.k, lane);
+        if (lane < a.k) {
+            a.cand_v[cbase + lane] = lane < tk.lcount ? tk.lv[lane] : -INFINITY;
+            a.cand_i[cbase + lane] = lane < tk.lcount ? tk.li[lane] : -1;
+        }
+    }
+}
+
+// ----------------------------------------------------------- draws
+// Merge a row's segment statistics: M = max m_s, S = sum s_s 2^((m_s - M) c2).
+__device__ void merge_row_stats(const float* sm, const double* ss, int nseg, float c2, int lane,
+                                float& M, double& S) {
+    float m = -INFINITY;
+    for (int s = lane; s < nseg; s += 64) m = fmaxf(m, sm[s]);
+    M = wave_max(m);
+    double acc = 0.0;
+    for (int s = lane; s < nseg; s += 64)
+        if (sm[s] != -INFINITY) acc += ss[s] * (double)fast_exp2((sm[s] - M) * c2);
+    S = wave_sum(acc);
+}
+
+// Smallest element index of segment `seg` whose running weight (increasing
+// index) exceeds tgt; weights come from wfn(index) in fp32, summed in fp64.
+// Falls back to the last positive-weight element of the segment when
+// rounding leaves no crossing.  Wave-wide; every lane returns the index.
+template <class WFn>
+__device__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int lane) {
+    const int lo = seg * kSeg + lane * 32;
+    float w[32];
+    double mine = 0.0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        w[j] = (lo + j < V) ? wfn(lo + j) : 0.f;
+        mine += (double)w[j];
+    }
+    const double incl = wave_inclusive_scan(mine);
+    const double excl = incl - mine;
+    const uint64_t hit = ballot(mine > 0.0 && incl > tgt);
+    int result = -1;
+    if (hit) {
+        const int src = __builtin_ctzll(hit);
+        int found = -1;
+        if (lane == src) {
+            double acc = excl;
+            int lastpos = -1;
+            for (int j = 0; j < 32; ++j) {
+                if (w[j] > 0.f) lastpos = lo + j;
+                acc += (double)w[j];
+                if (found < 0 && w[j] > 0.f && acc > tgt) found = lo + j;
+            }
+            if (found < 0) found = lastpos;
+        }
+        result = __shfl(found, src, kWave);
+    } else {
+        const uint64_t pos = ballot(mine > 0.0);
+        if (pos) {
+            const int src = 63 - __builtin_clzll(pos);
+            int last = -1;
+            if (lane == src)
+                for (int j = 0; j < 32; ++j)
+                    if (w[j] > 0.f) last = lo + j;
+            result = __shfl(last, src, kWave);
+        }
+    }
+    return result;
+}
+
+// Pick the segment whose cumulative weight crosses `target`.  seg_w(s) is a
+// segment's weight in the units of target.  Returns the segment and the
+// weight before it.
+template <class SegW>
+__device__ int find_segment(int nseg, double target, const SegW& seg_w, int lane, double& before) {
+    double carry = 0.0;
+    int last_pos_seg = -1;
+    double before_last = 0.0;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+        const int s = s0 + lane;
+        const double w = s < nseg ? seg_w(s) : 0.0;
+        const double incl = wave_inclusive_scan(w);
+        const uint64_t hit = ballot(w > 0.0 && carry + incl > target);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            before = carry + __shfl(incl - w, src, kWave);
+            return s0 + src;
+        }
+        const uint64_t pos = ballot(w > 0.0);
+        if (pos) {
+            const int src = 63 - __builtin_clzll(pos);
+            last_pos_seg = s0 + src;
+            before_last = carry + __shfl(incl - w, src, kWave);
+        }
+        carry += __shfl(incl, 63, kWave);
+    }
+    before = before_last;
+    return last_pos_seg;
+}
+
+// Draw from softmax(z / T) of one row using its segment statistics.
+__device__ int draw_softmax_row(const float* zr, int V, const float* sm, const double* ss,
+                                int nseg, float c2, float M, double S, double u, int lane) {
+    const double target = u * S;
+    double before = 0.0;
+    auto segw = [&](int s) -> double {
+        return sm[s] == -INFINITY ? 0.0 : ss[s] * (double)fast_exp2((sm[s] - M) * c2);
+    };
+    const int seg = find_segment(nseg, target, segw, lane, before);
+    if (seg < 0) return 0;
+    const float ms = sm[seg];
+    const double f = (double)fast_exp2((ms - M) * c2);
+    const double tgt = (target - before) / f;
+    auto wfn = [&](int v) -> float { return fast_exp2((zr[v] - ms) * c2); };
+    return draw_in_segment(seg, V, tgt, wfn, lane);
+}
+
+// ------------------------------------------------------- top-k finalize
+struct TopKFin {
+    const float* z;
+    int B, G, V, nseg, wpr, k;
+    float T, c2;
+    const uint64_t* seeds;
+    uint64_t step;
+    const float* seg_m;
+    const double* seg_s;
+    const float* cand_v;
+    const int* cand_i;
+    int32_t* topk_idx;
+    float* topk_val;
+    double* lse;
+    int32_t* draft;
+};
+
+__global__ void __launch_bounds__(64) topk_finalize_kernel(TopKFin a) {
+    __shared__ float cv[kMaxCand];
+    __shared__ int ci[kMaxCand];
+    const int row = blockIdx.x, lane = threadIdx.x;
+    const int b = row / a.G, r = row % a.G;
+    const int N = a.wpr * a.k;
+    const float* src_v = a.cand_v + (size_t)row * N;
+    const int* src_i = a.cand_i + (size_t)row * N;
+    for (int e = lane; e < N; e += 64) { cv[e] = src_v[e]; ci[e] = src_i[e]; }
+    wave_lds_sync();
+    int top0 = -1;
+    for (int rr = 0; rr < a.k; ++rr) {
+        float bv = -INFINITY;
+        int bi = -1, bpos = -1;
+        for (int e = lane; e < N; e += 64)
+            if (ranks_ahead(cv[e], ci[e], bv, bi)) { bv = cv[e]; bi = ci[e]; bpos = e; }
+        float wv = bv;
+        int wi = bi;
+        wave_best(wv, wi);
+        if (bi == wi && bpos >= 0 && wi != -1) { cv[bpos] = -INFINITY; ci[bpos] = -1; }
+        wave_lds_sync();
+        if (lane == 0) {
+            a.topk_idx[(size_t)row * a.k + rr] = wi;
+            a.topk_val[(size_t)row * a.k + rr] = wv;
+        }
+        if (rr == 0) top0 = wi;
+    }
+    if (a.T == 0.f) {
+        if (lane == 0) {
+            if (a.lse) a.lse[row] = NAN;
+            if (a.draft) a.draft[row] = top0;
+        }
+        return;
+    }
+    float M;
+    double S;
+    const float* sm = a.seg_m + (size_t)row * a.nseg;
+    const double* ss = a.seg_s + (size_t)row * a.nseg;
+    merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+    if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
+    if (a.draft) {
+        const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
+        const int tok = draw_softmax_row(a.z + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S,
+                                         u, lane);
+        if (lane == 0) a.draft[row] = tok;
+    }
+}
+
+// --------------------------------------------------------- verification
+struct VerifyArgs {
+    const float* zp;   // target logits [B, G, V]
+    const float* zq;   // draft logits  [B, G, V]
+    const int32_t* drafts;  // [B, G]
+    const double* draft_lse;  // [B, G] or null
+    int B, G, V, nseg, wpr;
+    float T, c2;
+    const uint64_t* seeds;
+    uint64_t step;
+    const float* p_seg_m;   // target rows' segment stats
+    const double* p_seg_s;
+    const float* q_seg_m;   // draft rows' segment stats (when draft_lse is null)
+    const double* q_seg_s;
+    const float* cand_v;    // target rows' per-wave argmax
+    const int* cand_i;
+    int* seq_j;             // [B]
+    double* seq_lse;        // [B][2]: LSE_p, LSE_q of row j
+    double* resid_s;        // [B][nseg]
+    int32_t* accept_len;
+    int32_t* out_tokens;
+    uint8_t* accepted;
+};
+
+__device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >= V ? V - 1 : d); }
+
+__global__ void __launch_bounds__(64) verify_commit_kernel(VerifyArgs a) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int G = a.G;
+    const int r = lane;
+    const bool is_row = r < G, is_draft = r < G - 1;
+    const int d = is_draft ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : 0;
+    bool acc = false;
+    int tgt_tok = -1;
+    double lsep = 0.0, lseq = 0.0;
+    if (a.T == 0.f) {
+        if (is_row) {
+            const size_t cb = ((size_t)b * G + r) * a.wpr;
+            float bv = -INFINITY;
+            int bi = -1;
+            for (int w = 0; w < a.wpr; ++w)
+                if (ranks_ahead(a.cand_v[cb + w], a.cand_i[cb + w], bv, bi)) {
+                    bv = a.cand_v[cb + w];
+                    bi = a.cand_i[cb + w];
+                }
+            tgt_tok = bi;
+        }
+        acc = is_draft && d == tgt_tok;
+    } else if (is_row) {
+        const size_t rb = ((size_t)b * G + r) * a.nseg;
+        float M = -INFINITY;
+        for (int s = 0; s < a.nseg; ++s) M = fmaxf(M, a.p_seg_m[rb + s]);
+        double S = 0.0;
+        for (int s = 0; s < a.nseg; ++s)
+            if (a.p_seg_m[rb + s] != -INFINITY)
+                S += a.p_seg_s[rb + s] * (double)fast_exp2((a.p_seg_m[rb + s] - M) * a.c2);
+        const double Td = (double)a.T;
+        lsep = (double)M / Td + log(S);
+        if (is_draft) {
+            if (a.draft_lse) {
+                lseq = a.draft_lse[(size_t)b * G + r];
+            } else {
+                float Mq = -INFINITY;
+                for (int s = 0; s < a.nseg; ++s) Mq = fmaxf(Mq, a.q_seg_m[rb + s]);
+                double Sq = 0.0;
+                for (int s = 0; s < a.nseg; ++s)
+                    if (a.q_seg_m[rb + s] != -INFINITY)
+                        Sq += a.q_seg_s[rb + s] * (double)fast_exp2((a.q_seg_m[rb + s] - Mq) * a.c2);
+                lseq = (double)Mq / Td + log(Sq);
+            }
+            const size_t off = ((size_t)b * G + r) * a.V + d;
+            const double ratio = exp(((double)a.zp[off] - (double)a.zq[off]) / Td - lsep + lseq);
+            const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
+            acc = u < (ratio < 1.0 ? ratio : 1.0);
+        }
+    }
+    const uint64_t accmask = ballot(acc);
+    const int j = __builtin_ctzll(~accmask) < G - 1 ? __builtin_ctzll(~accmask) : G - 1;
+    if (is_draft && a.accepted) a.accepted[(size_t)b * (G - 1) + r] = acc ? 1 : 0;
+    int final_tok = -1;
+    bool final_known = true;
+    if (a.T == 0.f) {
+        final_tok = __shfl(tgt_tok, j, kWave);
+    } else if (j == G - 1) {
+        // bonus token from the target's last row
+        const int row = b * G + (G - 1);
+        const float* sm = a.p_seg_m + (size_t)row * a.nseg;
+        const double* ss = a.p_seg_s + (size_t)row * a.nseg;
+        float M;
+        double S;
+        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+        const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
+        final_tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+    } else {
+        final_known = false;  // correction drawn by the residual kernels
+        const double lp = __shfl(lsep, j, kWave), lq = __shfl(lseq, j, kWave);
+        if (lane == 0) { a.seq_lse[2 * b] = lp; a.seq_lse[2 * b + 1] = lq; }
+    }
+    if (lane == 0) {
+        a.accept_len[b] = j;
+        a.seq_j[b] = final_known ? -1 : j;
+    }
+    if (is_row) {
+        int tok = r < j ? d : -1;
+        if (r == j) tok = final_known ? final_tok : -1;
+        a.out_tokens[(size_t)b * G + r] = tok;
+    }
+}
+
+// Element weight of the residual [p - q]_+ at row j, from the row log-normalisers.
+struct ResidualW {
+    const float* zpr;
+    const float* zqr;
+    float Rp, Rq, Fp, Fq, c2;
+    __device__ float operator()(int v) const {
+        const float p = fast_exp2((zpr[v] - Rp) * c2) * Fp;
+        const float q = fast_exp2((zqr[v] - Rq) * c2) * Fq;
+        return fmaxf(p - q, 0.f);
+    }
+};
+
+__device__ ResidualW make_residual(const VerifyArgs& a, int b, int j) {
+    ResidualW w;
+    const size_t row = (size_t)b * a.G + j;
+    w.zpr = a.zp + row * a.V;
+    w.zqr = a.zq + row * a.V;
+    const double Td = (double)a.T;
+    const double lp = a.seq_lse[2 * b], lq = a.seq_lse[2 * b + 1];
+    w.Rp = (float)(lp * Td);
+    w.Rq = (float)(lq * Td);
+    w.Fp = (float)exp((double)w.Rp / Td - lp);
+    w.Fq = (float)exp((double)w.Rq / Td - lq);
+    w.c2 = a.c2;
+    return w;
+}
+
+// Residual mass per segment of row j, for sequences that rejected a draft.
+__global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * kScanWaves + wave;
+    const int b = gw / a.nseg, seg = gw % a.nseg;
+    if (b >= a.B) return;
+    const int j = a.seq_j[b];
+    if (j < 0) return;
+    const ResidualW w = make_residual(a, b, j);
+    const int base = seg * kSeg + 4 * lane;
+    double s = 0.0;
+#pragma unroll
+    for (int h = 0; h < kIters / 2; ++h) {
+        float t[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = base + (2 * h + q) * 256;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[q * 4 + c] = e < a.V ? w(e + c) : 0.f;
+        }
+        s += (double)(((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7])));
+    }
+    s = wave_sum(s);
+    if (lane == 0) a.resid_s[(size_t)b * a.nseg + seg] = s;
+}
+
+// Correction draw from [p_j - q_j]_+ (or from p_j when it has no mass).
+__global__ void __launch_bounds__(64) verify_draw_kernel(VerifyArgs a) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int j = a.seq_j[b];
+    if (j < 0) return;
+    const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)j, kFinalDraw);
+    const double* rs = a.resid_s + (size_t)b * a.nseg;
+    double tot = 0.0;
+    for (int s = lane; s < a.nseg; s += 64) tot += rs[s];
+    tot = wave_sum(tot);
+    int tok;
+    if (tot > 0.0) {
+        const ResidualW w = make_residual(a, b, j);
+        double before = 0.0;
+        auto segw = [&](int s) -> double { return rs[s]; };
+        const double target = u * tot;
+        const int seg = find_segment(a.nseg, target, segw, lane, before);
+        tok = seg < 0 ? 0 : draw_in_segment(seg, a.V, target - before, w, lane);
+    } else {
+        const int row = b * a.G + j;
+        const float* sm = a.p_seg_m + (size_t)row * a.nseg;
+        const double* ss = a.p_seg_s + (size_t)row * a.nseg;
+        float M;
+        double S;
+        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+        tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+    }
+    if (lane == 0) a.out_tokens[(size_t)b * a.G + j] = tok;
+}
+
+// ------------------------------------------------------------- planning
+struct ScanPlan {
+    int nseg, spw, wpr;
+};
+
+ScanPlan plan_scan(long rows, int V, int k) {
+    ScanPlan p;
+    p.nseg = (V + kSeg - 1) / kSeg;
+    long spw = (rows * p.nseg + kTargetWaves - 1) / kTargetWaves;
+    if (spw < 1) spw = 1;
+    if (spw > p.nseg) spw = p.nseg;
+    // the finalize merges wpr * k candidates in a kMaxCand-entry LDS array
+    while (spw < p.nseg && ((p.nseg + spw - 1) / spw) * (long)k > kMaxCand) ++spw;
+    p.spw = (int)spw;
+    p.wpr = (p.nseg + p.spw - 1) / p.spw;
+    return p;
+}
+
+struct TopKLayout {
+    ScanPlan sp;
+    size_t seg_m, seg_s, cand_v, cand_i, bytes;
+};
+
+TopKLayout topk_layout(int batch, int gamma, int vocab, int k) {
+    TopKLayout L{};
+    const long rows = (long)batch * gamma;
+    L.sp = plan_scan(rows, vocab, k);
+    Carve c;
+    L.seg_m = c.take<float>((size_t)rows * L.sp.nseg);
+    L.seg_s = c.take<double>((size_t)rows * L.sp.nseg);
+    L.cand_v = c.take<float>((size_t)rows * L.sp.wpr * k);
+    L.cand_i = c.take<int>((size_t)rows * L.sp.wpr * k);
+    L.bytes = c.total();
+    return L;
+}
+
+struct VerifyLayout {
+    ScanPlan sp;
+    size_t p_m, p_s, q_m, q_s, cand_v, cand_i, seq_j, seq_lse, resid, bytes;
+};
+
+VerifyLayout verify_layout(int batch, int gamma, int vocab) {
+    VerifyLayout L{};
+    const long rows = (long)batch * gamma;
+    L.sp = plan_scan(rows, vocab, 1);
+    const size_t rs = (size_t)rows * L.sp.nseg;
+    Carve c;
+    L.p_m = c.take<float>(rs);
+    L.p_s = c.take<double>(rs);
+    L.q_m = c.take<float>(rs);
+    L.q_s = c.take<double>(rs);
+    L.cand_v = c.take<float>((size_t)rows * L.sp.wpr);
+    L.cand_i = c.take<int>((size_t)rows * L.sp.wpr);
+    L.seq_j = c.take<int>((size_t)batch);
+    L.seq_lse = c.take<double>((size_t)batch * 2);
+    L.resid = c.take<double>((size_t)batch * L.sp.nseg);
+    L.bytes = c.total();
+    return L;
+}
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+    return ws && !(reinterpret_cast<uintptr_t>(ws) & 255) && have >= need;
+}
+
+template <int MODE>
+void launch_scan(const ScanArgs& s, hipStream_t st) {
+    const long waves = (long)s.rows * s.wpr;
+    hipLaunchKernelGGL((row_scan_kernel<MODE>), dim3((unsigned)((waves + kScanWaves - 1) / kScanWaves)),
+                       dim3(64 * kScanWaves), 0, st, s);
+}
+
+}  // namespace
+}  // namespace dfl
+
+using namespace dfl;
+
+extern "C" size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k) {
+    if (batch < 0 || gamma < 1 || vocab < 1 || k < 1) return 0;
+    return topk_layout(batch, gamma, vocab, k).bytes;
+}
+
+extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
+                           float temperature, const uint64_t* seeds, uint64_t step,
+                           int32_t* topk_idx, float* topk_val, double* lse, int32_t* draft,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || gamma < 1 || vocab < 1 || k < 1 || k > vocab) return DFLASH_ERR_SHAPE;
+    if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
+    if (batch == 0) return DFLASH_OK;
+    if (!logits || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
+    if (temperature > 0.f && draft && !seeds) return DFLASH_ERR_NULL;
+    if (k > 64 || gamma > 32 || vocab % 4 != 0) return DFLASH_ERR_UNSUPPORTED;
+    const TopKLayout L = topk_layout(batch, gamma, vocab, k);
+    if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
+    ScanArgs s{logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, k, c2,
+               reinterpret_cast<float*>(ws + L.seg_m), reinterpret_cast<double*>(ws + L.seg_s),
+               reinterpret_cast<float*>(ws + L.cand_v), reinterpret_cast<int*>(ws + L.cand_i)};
+    if (temperature > 0.f) launch_scan<kTopK | kSumExp>(s, st);
+    else launch_scan<kTopK>(s, st);
+    int rc = launch_status();
+    if (rc) return rc;
+    TopKFin f{logits, batch, gamma, vocab, L.sp.nseg, L.sp.wpr, k, temperature, c2, seeds, step,
+              s.seg_m, s.seg_s, s.cand_v, s.cand_i, topk_idx, topk_val, lse, draft};
+    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(64), 0, st, f);
+    return launch_status();
+}
+
+extern "C" size_t spec_verify_workspace_size(int batch, int gamma, int vocab) {
+    if (batch < 0 || gamma < 1 || vocab < 1) return 0;
+    return verify_layout(batch, gamma, vocab).bytes;
+}
+
+extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, const double* draft_lse,
+                           float temperature, const uint64_t* seeds, uint64_t step,
+                           int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
+                           int batch, int gamma, int vocab, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (batch < 0 || gamma < 1 || vocab < 1) return DFLASH_ERR_SHAPE;
+    if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
+    if (batch == 0) return DFLASH_OK;
+    if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_ERR_NULL;
+    if (temperature > 0.f && (!draft_logits || !seeds)) return DFLASH_ERR_NULL;
+    if (gamma > 32 || vocab % 4 != 0) return DFLASH_ERR_UNSUPPORTED;
+    const VerifyLayout L = verify_layout(batch, gamma, vocab);
+    if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
+    VerifyArgs v{};
+    v.zp = target_logits; v.zq = draft_logits; v.drafts = draft_tokens; v.draft_lse = draft_lse;
+    v.B = batch; v.G = gamma; v.V = vocab; v.nseg = L.sp.nseg; v.wpr = L.sp.wpr;
+    v.T = temperature; v.c2 = c2; v.seeds = seeds; v.step = step;
+    v.p_seg_m = reinterpret_cast<float*>(ws + L.p_m);
+    v.p_seg_s = reinterpret_cast<double*>(ws + L.p_s);
+    v.q_seg_m = reinterpret_cast<float*>(ws + L.q_m);
+    v.q_seg_s = reinterpret_cast<double*>(ws + L.q_s);
+    v.cand_v = reinterpret_cast<float*>(ws + L.cand_v);
+    v.cand_i = reinterpret_cast<int*>(ws + L.cand_i);
+    v.seq_j = reinterpret_cast<int*>(ws + L.seq_j);
+    v.seq_lse = reinterpret_cast<double*>(ws + L.seq_lse);
+    v.resid_s = reinterpret_cast<double*>(ws + L.resid);
+    v.accept_len = accept_len; v.out_tokens = out_tokens; v.accepted = accepted;
+    ScanArgs s{target_logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, 1, c2,
+               const_cast<float*>(v.p_seg_m), const_cast<double*>(v.p_seg_s),
+               const_cast<float*>(v.cand_v), const_cast<int*>(v.cand_i)};
+    if (temperature == 0.f) {
+        launch_scan<kArgmax>(s, st);
+    } else {
+        launch_scan<kSumExp>(s, st);
+        if (!draft_lse) {
+            ScanArgs q = s;
+            q.z = draft_logits;
+            q.seg_m = const_cast<float*>(v.q_seg_m);
+            q.seg_s = const_cast<double*>(v.q_seg_s);
+            launch_scan<kSumExp>(q, st);
+        }
+    }
+    int rc = launch_status();
+    if (rc) return rc;
+    hipLaunchKernelGGL(verify_commit_kernel, dim3(batch), dim3(64), 0, st, v);
+    rc = launch_status();
+    if (rc || temperature == 0.f) return rc;
+    const long waves = (long)batch * L.sp.nseg;
+    hipLaunchKernelGGL(verify_residual_kernel, dim3((unsigned)((waves + kScanWaves - 1) / kScanWaves)),
+                       dim3(64 * kScanWaves), 0, st, v);
+    rc = launch_status();
+    if (rc) return rc;
+    hipLaunchKernelGGL(verify_draw_kernel, dim3(batch), dim3(64), 0, st, v);
+    return launch_status();
+}

@@ -1,0 +1,224 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash2 block-drafting hot path.
+ *
+ * Four operations, each a stream-ordered sequence of hand-written HIP kernels:
+ *
+ *   dflash_context_fuse  fuse tapped target hidden states into the context
+ *                        representation H_t and append every draft layer's
+ *                        context K/V rows to per-sequence ring buffers;
+ *   dflash_block_attn    block-draft attention of one draft layer;
+ *   dflash_topk          per-position top-k candidates, log-normaliser and
+ *                        drafted token of the drafter's logits;
+ *   spec_verify          lossless verification of one drafted block.
+ *
+ * Sources (web pages, cited by title and section):
+ *   "DFlash vs DFlash 2" (blog): "The problem: one expensive token at a time",
+ *       "DFlash: generate the block all at once", "Conditioning on the target
+ *       model", "The candidate selector".
+ *   "Beam 1.0 DFlash2" (model card): "Model", "Evaluation".
+ *   "Speculative decoding" (Reflection docs): "How it works".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer (memory visible to the GPU that
+ *   `stream` belongs to), except where a comment says otherwise.  bf16 values
+ *   are passed as uint16_t bit patterns.  All tensors are dense, row-major, in
+ *   the index order written next to them.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on it and returns; nothing is synchronised.
+ * - The caller owns every buffer.  The library never allocates or frees
+ *   memory and keeps no state between calls; scratch space comes only from
+ *   the caller's `workspace` (device memory of at least the size the matching
+ *   *_workspace_size() query returns, 256-byte aligned).  Two calls may run
+ *   concurrently if their workspaces and outputs do not overlap.
+ * - Inputs are read-only.  Outputs are fully overwritten, except the ring
+ *   buffer of dflash_context_fuse, of which only the addressed slots change.
+ * - Every argument the host can check is checked BEFORE any HIP call; a
+ *   rejected call enqueues nothing.  Device-side data (token ids, lengths) are
+ *   preconditions stated per call: out-of-range values there are undefined
+ *   behaviour (they are clamped where clamping is cheap, never trapped).
+ * - Temperatures: T == 0 selects greedy behaviour; T > 0 samples.
+ * - Random numbers: one Philox4x64-10 block (Salmon et al., SC'11) per draw,
+ *   key = (seed[b], 0), counter = (step, b, row, purpose), uniform =
+ *   (first output word >> 11) * 2^-53.  Purposes: 0 draft draw, 1 accept test,
+ *   2 correction or bonus draw.  `row` is the 0-based position in the block.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define DFLASH_OK                0
+#define DFLASH_ERR_NULL         -1  /* a required pointer is NULL               */
+#define DFLASH_ERR_SHAPE        -2  /* a size or scalar argument is invalid     */
+#define DFLASH_ERR_UNSUPPORTED  -3  /* valid, but outside what this build runs  */
+#define DFLASH_ERR_WORKSPACE    -4  /* workspace NULL, misaligned or too small  */
+#define DFLASH_ERR_HIP          -5  /* a HIP launch failed                      */
+
+/* Element types of dflash_block_attn's Q/K/V/output tensors. */
+#define DFLASH_DTYPE_BF16 0
+#define DFLASH_DTYPE_FP32 1
+
+/* Static description of a status code (never NULL). */
+const char* dflash_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dflash_version(void);
+
+/* ------------------------------------------------------------------------
+ * dflash_block_attn -- block-draft attention of one draft layer.
+ *
+ * "DFlash vs DFlash 2", "DFlash: generate the block all at once" and
+ * "Conditioning on the target model" (equation for Q_i, K_i, V_i): the
+ * queries come from the block of gamma positions (anchor + masks) only; keys
+ * and values are the target-context rows followed by the block's own rows;
+ * positions inside the block attend to one another without a causal mask.
+ * "Speculative decoding", "How it works" / "Beam 1.0 DFlash2", "Model": the
+ * context is a sliding window of the most recent `window` (4,096) tokens;
+ * 40 query heads share 8 KV heads of dimension 128.
+ *
+ * For each sequence b, query head h (KV head h / (n_q / n_kv)) and block row r:
+ *   out[b,r,h,:] = sum_j softmax_j(scale * <q[b,r,h,:], k_j>) v_j
+ * over the key set { ring slots 0 .. n_b-1 } U { block rows 0 .. gamma-1 },
+ * n_b = min(ctx_len[b], window).  The ring is a set: slot order is irrelevant
+ * (a writer puts absolute position p at slot p mod window).  Q and K arrive
+ * already projected (and rotated, if the model rotates them).
+ *
+ *   q       [batch, gamma, n_q,  d_head]   dtype
+ *   k_blk   [batch, gamma, n_kv, d_head]   dtype
+ *   v_blk   [batch, gamma, n_kv, d_head]   dtype
+ *   k_ring  [batch, n_kv, window, d_head]  dtype  (slots >= n_b are never read)
+ *   v_ring  [batch, n_kv, window, d_head]  dtype
+ *   ctx_len [batch] int64, >= 0 (precondition)
+ *   out     [batch, gamma, n_q, d_head]    dtype (bf16 rounded to nearest even)
+ *   lse     [batch, gamma, n_q] float32, natural-log normaliser of the scaled
+ *           scores; may be NULL.
+ * Supported: d_head in {64, 128}; n_q % n_kv == 0; 1 <= gamma <= 32;
+ *   window % 64 == 0 and window >= 64; fp32 additionally needs d_head <= 128.
+ * Accuracy: fp32 softmax and accumulation; bf16 products.
+ * ------------------------------------------------------------------------ */
+size_t dflash_block_attn_workspace_size(int batch, int gamma, int n_q, int n_kv,
+                                        int d_head, int window, int dtype);
+int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
+                      const void* k_ring, const void* v_ring, const int64_t* ctx_len,
+                      float scale, void* out, float* lse, int dtype,
+                      int batch, int gamma, int n_q, int n_kv, int d_head, int window,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_topk -- drafter side of one block: per-position top-k candidates,
+ * log-normaliser and drafted token.
+ *
+ * "DFlash vs DFlash 2", "The candidate selector": keep the top k candidates
+ * of each position's draft logits.  "The problem: one expensive token at a
+ * time": the drafter proposes token y from its distribution q.
+ *
+ *   logits   [batch, gamma, vocab] float32; row r is the drafter's logits of
+ *            block position r+1 (the token after anchor + r masks).
+ *   topk_idx [batch, gamma, k] int32, topk_val [batch, gamma, k] float32:
+ *            the k largest raw logits of each row, descending; equal logits
+ *            in increasing index order.
+ *   lse      [batch, gamma] float64, log sum_v exp(logit_v / T)  (T > 0;
+ *            NaN when T == 0); may be NULL.
+ *   draft    [batch, gamma] int32; may be NULL.  T == 0: the row's argmax
+ *            (lowest index among equal maxima).  T > 0: a draw from
+ *            softmax(logits / T) by inverse CDF in increasing vocabulary order
+ *            with the purpose-0 uniform of (seeds[b], step, b, r).
+ *   seeds    [batch] uint64 (device); may be NULL when T == 0.
+ * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, 1 <= gamma <= 32.
+ * ------------------------------------------------------------------------ */
+size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k);
+int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
+                float temperature, const uint64_t* seeds, uint64_t step,
+                int32_t* topk_idx, float* topk_val, double* lse, int32_t* draft,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_verify -- verification of one drafted block per sequence.
+ *
+ * "DFlash vs DFlash 2", "The problem: one expensive token at a time": the
+ * target scores the whole block in one pass, keeps the longest valid prefix
+ * and corrects the first rejection.  Greedy (T == 0): a draft survives while
+ * it equals the target's argmax.  Sampled (T > 0): draft y at row r survives
+ * if u < min(1, p_r(y) / q_r(y)) (u: purpose-1 uniform at row r); the first
+ * rejected row j draws a correction from [p_j - q_j]_+ renormalised (from p_j
+ * if that has no mass); if all gamma-1 drafts survive, a bonus token is
+ * drawn from the target's last row p_{gamma-1}.  Draws are inverse CDF in
+ * increasing vocabulary order with the purpose-2 uniform at the row drawn
+ * from.  p_r = softmax(target_logits[b,r,:] / T),
+ * q_r = softmax(draft_logits[b,r,:] / T).  "Beam 1.0 DFlash2",
+ * "Evaluation": a block of 8 verifies 7 drafts.
+ *
+ *   target_logits [batch, gamma, vocab] float32; row r is the target's
+ *            distribution for the token after anchor + drafts 0..r-1;
+ *            rows 0..gamma-2 verify, row gamma-1 gives the bonus.
+ *   draft_logits  [batch, gamma, vocab] float32 (rows 0..gamma-2 are read;
+ *            may be NULL when T == 0).
+ *   draft_tokens  [batch, gamma] int32 (as written by dflash_topk); entries
+ *            0..gamma-2 are the drafts, in [0, vocab) (precondition).
+ *   draft_lse     [batch, gamma] float64 from dflash_topk at the same T;
+ *            may be NULL (then recomputed from draft_logits).
+ *   seeds         [batch] uint64 (device); may be NULL when T == 0.
+ *   accept_len    [batch] int32: j = accepted drafts (0..gamma-1);
+ *                 tau = j + 1 tokens are committed.
+ *   out_tokens    [batch, gamma] int32: drafts 0..j-1, then the correction
+ *                 or bonus token, then -1.
+ *   accepted      [batch, gamma-1] uint8 or NULL: the accept test of every
+ *                 draft row (also rows after the first rejection).
+ * Supported: 1 <= gamma <= 32, vocab % 4 == 0.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_workspace_size(int batch, int gamma, int vocab);
+int spec_verify(const float* target_logits, const float* draft_logits,
+                const int32_t* draft_tokens, const double* draft_lse,
+                float temperature, const uint64_t* seeds, uint64_t step,
+                int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
+                int batch, int gamma, int vocab,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_context_fuse -- context fusion and context K/V append.
+ *
+ * "DFlash vs DFlash 2", "Conditioning on the target model", equation for
+ * H_t: the hidden states of five target layers ("Beam 1.0 DFlash2", "Model":
+ * layers 4, 16, 28, 40, 46) are concatenated, projected by W_c and
+ * RMS-normalised; equation for K_i, V_i: the context half of draft layer i's
+ * keys and values is W_i^K H_t, W_i^V H_t, a read-only memory at every layer.
+ *
+ *   H_t[r,:] = g * y / sqrt(mean(y^2) + eps),  y = W_c x_r
+ *   kv[r,c]  = sum_n H_t[r,n] * w_kv[c,n],  c = ((i*2 + t)*n_kv + h)*d_head + d
+ *              (layer i, t = 0 key / 1 value, KV head h)
+ *   kv_ring[i, t, row_seq[r], h, row_pos[r] % window, d] = bf16(kv[r,c])
+ *
+ *   taps     [rows, n_taps*d_tgt] bf16, the tapped states of each new token
+ *   w_c      [d_model, n_taps*d_tgt] bf16 (one row per output feature)
+ *   rms_gain [d_model] float32
+ *   w_kv     [n_layers*2*n_kv*d_head, d_model] bf16
+ *   row_seq  [rows] int32 in [0, batch), row_pos [rows] int64 >= 0
+ *            (preconditions; no two rows may address the same slot)
+ *   kv_ring  [n_layers, 2, batch, n_kv, window, d_head] bf16, in/out
+ *   h_t_out  [rows, d_model] bf16, or NULL
+ * Supported: d_model % 128 == 0, (n_taps*d_tgt) % 64 == 0,
+ *   (n_layers*2*n_kv*d_head) % 128 == 0, d_head even, rows >= 1, d_model <= 8192.
+ * Accuracy: bf16 products, fp32 accumulation; H_t is rounded to bf16 before
+ * the K/V projection.
+ * ------------------------------------------------------------------------ */
+size_t dflash_context_fuse_workspace_size(int rows, int n_taps, int d_tgt, int d_model,
+                                          int n_layers, int n_kv, int d_head);
+int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, const float* rms_gain,
+                        float eps, const uint16_t* w_kv, const int32_t* row_seq,
+                        const int64_t* row_pos, uint16_t* kv_ring, uint16_t* h_t_out,
+                        int rows, int n_taps, int d_tgt, int d_model, int n_layers,
+                        int n_kv, int d_head, int window, int batch,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

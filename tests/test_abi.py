@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/dflash.h declares, answers workspace queries, and rejects every
+host-checkable bad argument with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_drafting_context_amd as dfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_symbols_are_exported():
+    lib = dfl.load()
+    names = declared_functions()
+    assert set(names) == set(dfl.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert dfl.dflash_status_string(code) != "unknown status"
+    assert dfl.dflash_status_string(17) == "unknown status"
+    assert dfl.dflash_version() >= 100
+
+
+def test_workspace_queries():
+    assert dfl.dflash_block_attn_workspace_size(1, 8, 40, 8, 128, 4096) > 0   # split keys at B=1
+    assert dfl.dflash_block_attn_workspace_size(32, 8, 40, 8, 128, 4096, 1) == 0  # fp32: none
+    assert dfl.dflash_block_attn_workspace_size(32, 8, 41, 8, 128, 4096) == 0      # bad GQA
+    assert dfl.dflash_topk_workspace_size(32, 8, 151936, 8) > 0
+    assert dfl.spec_verify_workspace_size(32, 8, 151936) > 0
+    assert dfl.dflash_context_fuse_workspace_size(512, 5, 5120, 5120, 5, 8, 128) > 0
+    assert dfl.dflash_context_fuse_workspace_size(512, 5, 5120, 5100, 5, 8, 128) == 0
+
+
+def attn(**kw):
+    a = dict(q=P, kb=P, vb=P, kr=P, vr=P, cl=P, scale=0.1, out=P, lse=None, dtype=0, B=2, G=8,
+             HQ=40, HKV=8, D=128, W=4096, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return dfl.load().dflash_block_attn(a["q"], a["kb"], a["vb"], a["kr"], a["vr"], a["cl"],
+                                        a["scale"], a["out"], a["lse"], a["dtype"], a["B"], a["G"],
+                                        a["HQ"], a["HKV"], a["D"], a["W"], a["ws"], a["wsb"],
+                                        a["st"])
+
+
+def test_block_attn_validation():
+    assert attn(q=None) == -1
+    assert attn(out=None) == -1
+    assert attn(HQ=41) == -2
+    assert attn(G=0) == -2
+    assert attn(scale=0.0) == -2
+    assert attn(scale=float("nan")) == -2
+    assert attn(dtype=7) == -2
+    assert attn(G=33) == -3
+    assert attn(D=96) == -3
+    assert attn(W=4000) == -3
+    assert attn(B=1) == -4         # needs a workspace at this size
+    assert attn(ws=ctypes.c_void_p(0x1001), wsb=1 << 30) == -4  # misaligned
+    assert attn(B=0) == 0           # nothing to do, nothing launched
+
+
+def topk(**kw):
+    a = dict(z=P, B=2, G=8, V=151936, k=8, T=0.7, seeds=P, step=0, idx=P, val=P, lse=None,
+             draft=P, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return dfl.load().dflash_topk(a["z"], a["B"], a["G"], a["V"], a["k"], a["T"], a["seeds"],
+                                  a["step"], a["idx"], a["val"], a["lse"], a["draft"], a["ws"],
+                                  a["wsb"], a["st"])
+
+
+def test_topk_validation():
+    assert topk(z=None) == -1
+    assert topk(seeds=None) == -1          # sampling needs seeds
+    assert topk(k=0) == -2
+    assert topk(k=151937) == -2
+    assert topk(T=-1.0) == -2
+    assert topk(T=float("inf")) == -2
+    assert topk(k=65) == -3
+    assert topk(V=151935) == -3
+    assert topk(G=40) == -3
+    assert topk() == -4
+    assert topk(seeds=None, T=0.0) == -4   # greedy needs no seeds; fails on workspace only
+
+
+def verify(**kw):
+    a = dict(zp=P, zq=P, d=P, lse=None, T=0.7, seeds=P, step=0, j=P, out=P, acc=None, B=2, G=8,
+             V=151936, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return dfl.load().spec_verify(a["zp"], a["zq"], a["d"], a["lse"], a["T"], a["seeds"],
+                                  a["step"], a["j"], a["out"], a["acc"], a["B"], a["G"], a["V"],
+                                  a["ws"], a["wsb"], a["st"])
+
+
+def test_verify_validation():
+    assert verify(zp=None) == -1
+    assert verify(zq=None) == -1
+    assert verify(seeds=None) == -1
+    assert verify(j=None) == -1
+    assert verify(G=0) == -2
+    assert verify(T=-0.5) == -2
+    assert verify(G=33) == -3
+    assert verify(V=1001) == -3
+    assert verify() == -4
+    assert verify(zq=None, seeds=None, T=0.0) == -4
+
+
+def fuse(**kw):
+    a = dict(x=P, wc=P, g=P, eps=1e-6, wkv=P, rs=P, rp=P, ring=P, h=None, rows=512, taps=5,
+             dt=5120, dm=5120, nl=5, nkv=8, dh=128, W=4096, B=64, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return dfl.load().dflash_context_fuse(a["x"], a["wc"], a["g"], a["eps"], a["wkv"], a["rs"],
+                                          a["rp"], a["ring"], a["h"], a["rows"], a["taps"], a["dt"],
+                                          a["dm"], a["nl"], a["nkv"], a["dh"], a["W"], a["B"],
+                                          a["ws"], a["wsb"], a["st"])
+
+
+def test_fuse_validation():
+    assert fuse(x=None) == -1
+    assert fuse(ring=None) == -1
+    assert fuse(rows=0) == -2
+    assert fuse(eps=-1.0) == -2
+    assert fuse(dm=5100) == -3
+    assert fuse(dm=16384) == -3
+    assert fuse(dh=127) == -3
+    assert fuse() == -4
+
+
+def test_binding_raises_on_bad_status():
+    with pytest.raises(dfl.DFlashError) as e:
+        dfl._call("dflash_topk", P, 1, 1, 1024, 0, 0.0, None, 0, P, P, None, None, None, 0, None)
+    assert e.value.status == -2

@@ -1,0 +1,143 @@
+"""GPU parity of dflash_block_attn against the fp64 oracle (through the C ABI).
+
+Bar: bf16 inputs with fp32 accumulation, max|err| <= 1e-2 * max|ref| + 1e-3;
+fp32 path, max|err| <= 1e-5 * max|ref| + 1e-6; lse within 1e-3 (bf16) / 1e-5
+(fp32) absolute.  Inputs are seeded and synthetic (block_drafting_context_amd.
+synthetic); the stress cases give the scores real spread (score std ~3), plant
+needles, shift V by 100 and poison unused ring slots with NaN, because with the
+workload's own N(0,1)/sqrt(d) inputs a kernel that ignored Q would also pass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_drafting_context_amd as dfl
+from block_drafting_context_amd import synthetic as syn
+from parity_util import (ATTN_ABS, ATTN_REL, F32_ABS, F32_REL, assert_close_scaled, cuda, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(a, scale, want_lse=True):
+    dev = cuda()
+    t = {k: v.to(dev) for k, v in a.items()}
+    out, lse = dfl.dflash_block_attn(t["q"], t["k_blk"], t["v_blk"], t["k_ring"], t["v_ring"],
+                                     t["ctx_len"], scale, want_lse=True)
+    torch.cuda.synchronize()
+    return to64(out), to64(lse)
+
+
+def _ref(a, scale):
+    return oracle.block_attn(to64(a["q"]), to64(a["k_blk"]), to64(a["v_blk"]), to64(a["k_ring"]),
+                             to64(a["v_ring"]), to64(a["ctx_len"]), scale, want_lse=True)
+
+
+def _check(a, scale, fp32=False, what=""):
+    print(f"[attn] {what} q{tuple(a['q'].shape)} ring{tuple(a['k_ring'].shape)} "
+          f"ctx={a['ctx_len'].tolist()[:8]}", flush=True)
+    out, lse = _run(a, scale)
+    ref, rlse = _ref(a, scale)
+    rel, ab = (F32_REL, F32_ABS) if fp32 else (ATTN_REL, ATTN_ABS)
+    assert_close_scaled(out, ref, rel, ab, what)
+    assert np.abs(lse - rlse).max() <= (1e-5 if fp32 else 1e-3) * max(1.0, np.abs(rlse).max())
+
+
+def test_tiny_fp32_workload():
+    """Batch 1, gamma 8, 4 q / 1 kv heads, d 64, 256 context tokens, fp32."""
+    a = syn.attention_inputs(1, 8, 4, 1, 64, 4096, [256], seed=1, dtype=torch.float32)
+    _check(a, 1 / 8.0, fp32=True, what="tiny fp32")
+
+
+def test_tiny_fp32_stress_scores():
+    a = syn.attention_inputs(2, 8, 4, 1, 64, 256, [256, 77], seed=2, dtype=torch.float32,
+                             q_mult=3 * 8.0, k_std=1.0)
+    _check(a, 1 / 8.0, fp32=True, what="tiny fp32 stress")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_ragged_lengths_several_tiles(D):
+    ctx = [0, 1, 63, 65, 300, 512, 2000]
+    a = syn.attention_inputs(len(ctx), 8, 40, 8, D, 512, ctx, seed=3, q_mult=3 * np.sqrt(D),
+                             k_std=1.0)
+    _check(a, 1 / np.sqrt(D), what=f"bf16 ragged D={D}")
+
+
+def test_bf16_edge_lengths_full_window():
+    ctx = [0, 1, 63, 64, 65, 4095, 4096, 9000]
+    a = syn.attention_inputs(len(ctx), 8, 40, 8, 128, 4096, ctx, seed=4, q_mult=3 * np.sqrt(128),
+                             k_std=1.0, poison_invalid=True)
+    _check(a, 1 / np.sqrt(128), what="bf16 edge lengths + NaN-poisoned slots")
+
+
+def test_bf16_workload_distribution_and_v_shift():
+    a = syn.attention_inputs(2, 8, 40, 8, 128, 4096, [4096, 1500], seed=5, v_mean=100.0)
+    _check(a, 1 / np.sqrt(128), what="bf16 V mean 100")
+
+
+def test_bf16_gamma16_two_query_groups():
+    """Trained block size: 16 positions x 5 heads = 80 query rows per KV head."""
+    a = syn.attention_inputs(2, 16, 40, 8, 128, 4096, [4096, 3000], seed=6,
+                             q_mult=3 * np.sqrt(128), k_std=1.0)
+    _check(a, 1 / np.sqrt(128), what="bf16 gamma 16")
+
+
+def test_bf16_needle_in_window():
+    a = syn.attention_inputs(1, 8, 40, 8, 128, 4096, [3000], seed=7)
+    q = a["q"].float()
+    # plant, for query (row 2, head 11 -> kv head 2), a key aligned with it at slot 1234
+    qv = q[0, 2, 11]
+    a["k_ring"][0, 2, 1234] = (qv / qv.norm() * 12.0).to(torch.bfloat16)
+    a["q"][0, 2, 11] = (qv / qv.norm() * 12.0).to(torch.bfloat16)
+    _check(a, 1.0, what="needle")
+    out, _ = _run(a, 1.0)
+    vref = to64(a["v_ring"][0, 2, 1234])
+    assert np.abs(out[0, 2, 11] - vref).max() < 0.05 * np.abs(vref).max() + 1e-3
+
+
+def test_bf16_single_block_key_only():
+    """Empty context: each query attends to the gamma block keys only."""
+    a = syn.attention_inputs(3, 4, 10, 2, 128, 64, [0, 0, 0], seed=8, q_mult=3 * np.sqrt(128),
+                             k_std=1.0)
+    _check(a, 1 / np.sqrt(128), what="no context")
+
+
+def test_bf16_batched_serving_shape_sampled():
+    """Batch 32, lengths uniform in [512, 131072] in 4,096-slot rings (the
+    throughput workload), checked on three sampled sequences."""
+    B, W = 32, 4096
+    cl = syn.ctx_lengths(B, 512, 131072, seed=9)
+    cl[0] = 700  # make sure a short sequence is among the sampled ones
+    dev = cuda()
+    a = syn.attention_inputs(B, 8, 40, 8, 128, W, cl, seed=9, device=dev,
+                             q_mult=3 * np.sqrt(128), k_std=1.0)
+    print(f"[attn] batched B=32 W=4096 ctx[:4]={cl[:4].tolist()}", flush=True)
+    out, lse = dfl.dflash_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ring"], a["v_ring"],
+                                     a["ctx_len"], 1 / np.sqrt(128), want_lse=True)
+    torch.cuda.synchronize()
+    for b in (0, 13, 31):
+        sl = {k: v[b:b + 1] for k, v in a.items()}
+        ref, rlse = _ref(sl, 1 / np.sqrt(128))
+        assert_close_scaled(to64(out[b:b + 1]), ref, ATTN_REL, ATTN_ABS, f"batched seq {b}")
+        assert np.abs(to64(lse[b:b + 1]) - rlse).max() < 1e-3 * max(1.0, np.abs(rlse).max())
+
+
+def test_bf16_deterministic():
+    a = syn.attention_inputs(4, 8, 40, 8, 128, 4096, [4096, 100, 2048, 4000], seed=10)
+    o1, l1 = _run(a, 1 / np.sqrt(128))
+    o2, l2 = _run(a, 1 / np.sqrt(128))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_block_row_permutation_equivariance_on_gpu():
+    a = syn.attention_inputs(2, 8, 40, 8, 128, 1024, [1024, 600], seed=11,
+                             q_mult=3 * np.sqrt(128), k_std=1.0)
+    perm = torch.randperm(8, generator=torch.Generator().manual_seed(0))
+    o1, _ = _run(a, 1 / np.sqrt(128))
+    b = dict(a)
+    for k in ("q", "k_blk", "v_blk"):
+        b[k] = a[k][:, perm].contiguous()
+    o2, _ = _run(b, 1 / np.sqrt(128))
+    # same keys, same arithmetic up to summation order: within the bf16 bar
+    assert_close_scaled(o2, o1[:, perm.numpy()], ATTN_REL, ATTN_ABS, "permuted block")

@@ -1,0 +1,210 @@
+"""GPU parity of dflash_topk and spec_verify against the fp64 oracle (C ABI).
+
+Bar: top-k indices, greedy drafts and greedy verification bit-exact; top-k
+values exact (they are copies of the inputs); lse within 1e-6 absolute;
+sampled accept flags bit-exact except where the oracle has |u - r| < 1e-6;
+sampled tokens bit-exact except where u lies within 1e-6 of a CDF boundary
+between the two indices (weights from scipy in fp64).  The temperature is the
+fp32 value the library receives, widened to fp64 for the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_drafting_context_amd as dfl
+from block_drafting_context_amd import synthetic as syn
+from parity_util import U_EXEMPT, cuda, draw_boundary_ok, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def _topk_case(zd, k, T, seeds, step=0, what=""):
+    print(f"[topk] {what} logits{tuple(zd.shape)} k={k} T={T}", flush=True)
+    dev = cuda()
+    res = dfl.dflash_topk(zd.to(dev), k, T, seeds=None if seeds is None else seeds.to(dev),
+                          step=step)
+    torch.cuda.synchronize()
+    z = to64(zd)
+    ref = oracle.draft_rows(z, k, f32(T), seeds=None if seeds is None else to64(seeds).astype(np.uint64),
+                            step=step)
+    np.testing.assert_array_equal(to64(res["idx"]), ref["idx"])
+    np.testing.assert_array_equal(to64(res["val"]), ref["val"])
+    B, G, _ = zd.shape
+    draft = to64(res["draft"])
+    if T == 0:
+        np.testing.assert_array_equal(draft, ref["draft"])
+        return res
+    assert np.abs(to64(res["lse"]) - ref["lse"]).max() < 1e-6
+    sd = to64(seeds).astype(np.uint64)
+    for b in range(B):
+        for g in range(G):
+            if draft[b, g] != ref["draft"][b, g]:
+                u = oracle.uniform(int(sd[b]), step, b, g, 0)
+                assert draw_boundary_ok(z[b, g], f32(T), u, int(draft[b, g]),
+                                        int(ref["draft"][b, g])), (b, g)
+    return res
+
+
+def test_topk_tiny_workload():
+    zt, zd = syn.logits_pair(1, 8, 1024, 2.0, 1.0, seed=1)
+    _topk_case(zd, 4, 1.0, syn.philox_seeds(1, 0), what="tiny T=1")
+    _topk_case(zd, 4, 0.0, None, what="tiny greedy")
+
+
+def test_topk_full_vocab_single_sequence():
+    zt, zd = syn.logits_pair(1, 8, 151936, 3.0, 1.5, seed=2)
+    _topk_case(zd, 8, 0.7, syn.philox_seeds(1, 0), step=5, what="V=151936 T=0.7")
+
+
+def test_topk_batched_serving_rows():
+    zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=3)
+    _topk_case(zd, 8, 0.7, syn.philox_seeds(32, 0), what="B=32 V=151936")
+
+
+@pytest.mark.parametrize("k", [1, 3, 16, 64])
+def test_topk_sizes_and_ragged_vocab(k):
+    zt, zd = syn.logits_pair(2, 3, 5000, 2.0, 1.0, seed=4)   # 5000 = 2 full segments + tail
+    _topk_case(zd, k, 0.9, syn.philox_seeds(2, 7), what=f"k={k} V=5000")
+
+
+def test_topk_exact_ties_take_lower_index():
+    zt, zd = syn.logits_pair(2, 4, 8192, 1.0, 0.5, seed=5)
+    zd = torch.round(zd * 4) / 4  # massive exact ties
+    _topk_case(zd, 16, 0.0, None, what="ties greedy")
+    _topk_case(zd, 16, 0.5, syn.philox_seeds(2, 1), what="ties sampled")
+
+
+def test_topk_all_equal_row():
+    zd = torch.zeros((1, 2, 4096), dtype=torch.float32)
+    _topk_case(zd, 8, 0.0, None, what="all equal")
+    _topk_case(zd, 64, 1.0, syn.philox_seeds(1, 3), what="all equal sampled")
+
+
+def test_topk_trained_block_size_rows():
+    """Batch 16, gamma 16, drafter noise growing from 0.5 to 3.0 along the block."""
+    zt, zd = syn.logits_pair(16, 16, 151936, 3.0, syn.linear_noise_std(16, 0.5, 3.0), seed=6)
+    _topk_case(zd, 8, 0.0, None, what="B=16 gamma=16 greedy")
+
+
+# --------------------------------------------------------------------- verify
+def _verify_case(zt, zd, drafts, T, seeds, step=0, use_lse=True, what=""):
+    print(f"[verify] {what} logits{tuple(zt.shape)} T={T} lse={use_lse}", flush=True)
+    dev = cuda()
+    B, G, V = zt.shape
+    d_full = torch.zeros((B, G), dtype=torch.int32)
+    d_full[:, :G - 1] = drafts.to(torch.int32)
+    lse = None
+    if T > 0 and use_lse:
+        lse = dfl.dflash_topk(zd.to(dev), 1, T, seeds=seeds.to(dev))["lse"]
+    res = dfl.spec_verify(zt.to(dev), zd.to(dev) if T > 0 else None, d_full.to(dev), T,
+                          seeds=None if seeds is None else seeds.to(dev), step=step,
+                          draft_lse=lse)
+    torch.cuda.synchronize()
+    ref = oracle.spec_verify(to64(zt), to64(zd) if T > 0 else None, to64(drafts), f32(T),
+                             seeds=None if seeds is None else to64(seeds).astype(np.uint64),
+                             step=step)
+    j = to64(res["accept_len"])
+    out = to64(res["out_tokens"])
+    acc = to64(res["accepted"])
+    if T == 0:
+        np.testing.assert_array_equal(j, ref["accept_len"])
+        np.testing.assert_array_equal(out, ref["out_tokens"])
+        np.testing.assert_array_equal(acc, ref["accepted"])
+        return j
+    sd = to64(seeds).astype(np.uint64)
+    z_t, z_d = to64(zt), to64(zd)
+    for b in range(B):
+        near = False
+        for r in range(G - 1):
+            if acc[b, r] != ref["accepted"][b, r]:
+                u = oracle.uniform(int(sd[b]), step, b, r, 1)
+                assert abs(u - min(1.0, ref["ratio"][b, r])) < U_EXEMPT, (b, r)
+                near = True
+        if near:
+            continue  # a flipped decision changes everything after it
+        assert j[b] == ref["accept_len"][b], b
+        jj = int(j[b])
+        np.testing.assert_array_equal(out[b, :jj], ref["out_tokens"][b, :jj])
+        np.testing.assert_array_equal(out[b, jj + 1:], ref["out_tokens"][b, jj + 1:])
+        if out[b, jj] != ref["out_tokens"][b, jj]:
+            u = oracle.uniform(int(sd[b]), step, b, jj, 2)
+            rq = z_d[b, jj] if jj < G - 1 else None
+            assert draw_boundary_ok(z_t[b, jj], f32(T), u, int(out[b, jj]),
+                                    int(ref["out_tokens"][b, jj]), residual_q=rq), b
+    return j
+
+
+def _drafts_from(zd, T, seeds):
+    """Drafts as the drafter would propose them (oracle draw from q)."""
+    ref = oracle.draft_rows(to64(zd), 1, f32(T) if T > 0 else 0.0,
+                            seeds=None if seeds is None else to64(seeds).astype(np.uint64))
+    return torch.from_numpy(ref["draft"][:, :-1].copy())
+
+
+def test_verify_tiny_greedy_and_sampled():
+    zt, zd = syn.logits_pair(1, 8, 1024, 2.0, 1.0, seed=11)
+    s = syn.philox_seeds(1, 0)
+    _verify_case(zt, zd, _drafts_from(zd, 0.0, None), 0.0, None, what="tiny greedy")
+    for step in range(4):
+        _verify_case(zt, zd, _drafts_from(zd, 1.0, s), 1.0, s, step=step, what=f"tiny T=1 {step}")
+
+
+def test_verify_greedy_planted_prefixes():
+    """Drafts equal to the target argmax for a planted number of leading rows."""
+    B, G, V = 9, 8, 4096
+    zt, zd = syn.logits_pair(B, G, V, 3.0, 1.5, seed=12)
+    am = torch.argmax(zt, dim=-1)
+    drafts = (am[:, :G - 1] + 1) % V
+    for b in range(B):
+        m = min(b, G - 1)
+        drafts[b, :m] = am[b, :m]
+    j = _verify_case(zt, zd, drafts, 0.0, None, what="greedy planted")
+    assert j.tolist() == [min(b, G - 1) for b in range(B)]
+
+
+def test_verify_greedy_trained_block_size():
+    zt, zd = syn.logits_pair(16, 16, 151936, 3.0, syn.linear_noise_std(16, 0.5, 3.0), seed=13)
+    _verify_case(zt, zd, _drafts_from(zd, 0.0, None), 0.0, None, what="B=16 gamma=16 greedy")
+
+
+def test_verify_sampled_full_vocab():
+    zt, zd = syn.logits_pair(1, 8, 151936, 3.0, 1.5, seed=14)
+    s = syn.philox_seeds(1, 0)
+    _verify_case(zt, zd, _drafts_from(zd, 0.7, s), 0.7, s, what="V=151936 T=0.7")
+
+
+def test_verify_sampled_batched_serving():
+    zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=15)
+    s = syn.philox_seeds(32, 0)
+    _verify_case(zt, zd, _drafts_from(zd, 0.7, s), 0.7, s, what="B=32 T=0.7")
+
+
+def test_verify_sampled_without_draft_lse():
+    zt, zd = syn.logits_pair(4, 8, 20000, 2.0, 1.0, seed=16)
+    s = syn.philox_seeds(4, 2)
+    _verify_case(zt, zd, _drafts_from(zd, 0.7, s), 0.7, s, use_lse=False, what="no draft lse")
+
+
+def test_verify_sampled_equal_distributions_take_bonus():
+    zt, _ = syn.logits_pair(6, 8, 3000, 2.0, 1.0, seed=17)
+    s = syn.philox_seeds(6, 0)
+    d = _drafts_from(zt, 0.8, s)
+    j = _verify_case(zt, zt.clone(), d, 0.8, s, what="q == p")
+    assert (j == 7).all()
+
+
+def test_verify_sampled_disjoint_point_masses():
+    B, G, V = 3, 5, 1024
+    zt = torch.full((B, G, V), -1e4)
+    zd = torch.full((B, G, V), -1e4)
+    zt[:, :, 5] = 0.0
+    zd[:, :, 9] = 0.0
+    drafts = torch.full((B, G - 1), 9)
+    s = syn.philox_seeds(B, 0)
+    j = _verify_case(zt, zd, drafts, 1.0, s, what="point masses")
+    assert (j == 0).all()
