@@ -174,8 +174,8 @@ def cpu_baseline(wl, n_seq):
     dt = time.perf_counter() - t0
     return {"value": round(n_seq * (G - 1) / dt, 3), "unit": "drafted tokens/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"{n_seq} of {B} sequences, whole step (fuse 8 rows, 5 attention layers, "
-                      f"top-8 + draws, sampled verify), {dt:.1f} s"}
+            "sample": f"{n_seq} of {B} sequences of the step (each: fuse its 8 rows, 5 attention "
+                      f"layers, top-8 + draws, sampled verify), {dt:.1f} s"}
 
 
 def main():
@@ -183,8 +183,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seqs", type=int, default=2,
-                    help="sequences of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-seqs", type=int, default=B,
+                    help="sequences of the workload the CPU oracle baseline runs on "
+                         "(default: all of them, i.e. the whole step)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -254,7 +255,7 @@ def main():
             "fuse": "[256x25600]x[25600x5120] + RMSNorm + [256x5120]x[5120x10240]",
         },
         "roofline": {
-            "kernel": "block_attn_bf16_kernel",
+            "kernel": "dflash_block_attn (block_attn_bf16_kernel + attn_combine_kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -35,11 +35,13 @@
 namespace dfl {
 namespace {
 
-constexpr int kTile = 32;          // keys per wave iteration
-constexpr int kWaves = 4;          // waves per workgroup
-constexpr int kVtStride = kTile + 4;  // bf16 per V^T row in LDS (pad against bank conflicts)
-constexpr int kMaxNT = 4;          // query tiles (of 16 rows) per workgroup
+constexpr int TK = 64;             // keys per tile
+constexpr int kVtStride = TK + 4;  // bf16 per V^T row in LDS (8-byte aligned, spreads banks)
+constexpr int kMaxNW = 8;          // query tiles (waves) per workgroup
 constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kWGsPerCU = 2;       // resident attention workgroups per CU (LDS-limited)
+constexpr int kMinTilesPerSplit = 4;
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may trail the true max
 
 struct AttnArgs {
     const uint16_t* q;
@@ -52,52 +54,9 @@ struct AttnArgs {
     uint16_t* out;
     float* lse;
     float* part_o;   // [B*HKV][n_splits][n_qt*16][D]
-    float* part_ml;  // [B*HKV][n_splits][n_qt*16][2]  (max, sum), base 2
-    int B, G, HQ, HKV, W, group, nrows, n_qt, n_splits, nt_per_group;
+    float* part_ml;  // [B*HKV][n_splits][n_qt*16][2]  (reference max, sum), base 2
+    int B, G, HQ, HKV, W, group, nrows, n_qt, n_splits, nw;
 };
-
-__device__ __forceinline__ const uint16_t* key_row(const uint16_t* ring, const uint16_t* blk,
-                                                   int b, int kvh, int t, int n, int HKV,
-                                                   int W, int G, int D) {
-    return t < n ? ring + ((size_t)((size_t)b * HKV + kvh) * W + t) * D
-                 : blk + ((size_t)((size_t)b * G + (t - n)) * HKV + kvh) * D;
-}
-
-template <int D>
-struct TileRegs {
-    u32x4 k[2][D / 32];         // [16-key subtile][k-step]  A operand of S^T = K Q^T
-    u32x4 v[D / 64][4];         // [combo][token in group]   8 dims of 4 tokens
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const AttnArgs& a, int b, int kvh,
-                                          int n, int tb, int t1, int lane) {
-    const int g = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        const int t = tb + st * 16 + i16;
-        const bool ok = t < t1;
-        const uint16_t* row = key_row(a.kr, a.kb, b, kvh, ok ? t : 0, n, a.HKV, a.W, a.G, D);
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            r.k[st][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 32 + g * 8) : z;
-        }
-    }
-    const int tg = lane & 7;
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-        const int dg = (lane >> 3) + 8 * c;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = tb + 4 * tg + e;
-            const bool ok = t < t1;
-            const uint16_t* row = key_row(a.vr, a.vb, b, kvh, ok ? t : 0, n, a.HKV, a.W, a.G, D);
-            u32x4 z = {0u, 0u, 0u, 0u};
-            r.v[c][e] = ok ? *reinterpret_cast<const u32x4*>(row + dg * 8) : z;
-        }
-    }
-}
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -105,262 +64,245 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NT>
-__global__ void __launch_bounds__(256, 1) block_attn_bf16_kernel(AttnArgs a) {
-    constexpr int DT = D / 16;  // 16-dim tiles of O^T
-    constexpr int KS = D / 32;  // k-steps of S^T
-    __shared__ __attribute__((aligned(16))) unsigned char smem[
-        (kWaves * D * kVtStride * 2) > (2 * NT * 16 * D * 4 + kWaves * NT * 16 * 2 * 4)
-            ? (kWaves * D * kVtStride * 2)
-            : (2 * NT * 16 * D * 4 + kWaves * NT * 16 * 2 * 4)];
+template <int D>
+struct AttnSmem {
+    u32x4 k[2][TK * D / 8];               // K tiles, 16-byte chunks, XOR-swizzled per row
+    uint16_t vt[2][D * kVtStride];        // V tiles transposed: [dim][key]
+};
+
+// Block-draft attention, bf16.  Workgroup = NW waves; wave w owns query tile
+// blockIdx.z * NW + w (16 query rows of the GQA group) for every key of the
+// workgroup's split; all waves cooperatively stage each 64-key K/V tile into
+// LDS (double buffer), so every K/V byte is read from HBM once per
+// (sequence, KV head) and used by all query heads of the group.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
+    constexpr int CH = D / 8;                    // 16-byte chunks per row
+    constexpr int NT = 64 * NW;                  // threads
+    constexpr int KCH = TK * CH;                 // K chunks per tile
+    constexpr int KPT = (KCH + NT - 1) / NT;     // K chunks per thread
+    constexpr int VU = (TK / 4) * CH;            // V units (4 keys x 8 dims) per tile
+    constexpr int VPT = (VU + NT - 1) / NT;      // V units per thread
+    constexpr int DT = D / 16;                   // 16-dim tiles of O^T
+    constexpr int KS = D / 32;                   // k-steps of S^T
+    __shared__ AttnSmem<D> sm;
 
     const int split = blockIdx.x;
     const int bk = blockIdx.y;
     const int b = bk / a.HKV, kvh = bk % a.HKV;
-    const int qt0 = blockIdx.z * a.nt_per_group;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, i16 = lane & 15;
+    const int qt = blockIdx.z * NW + wave;
 
     const int64_t cl = a.ctx_len[b];
     const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
     const int total = n + a.G;
     int per = (total + a.n_splits - 1) / a.n_splits;
-    per = (per + kTile - 1) / kTile * kTile;
+    per = (per + TK - 1) / TK * TK;
     const int t0 = split * per;
     const int t1 = min(t0 + per, total);
 
-    // Q^T operands: B[k = dims of (s, g)][col = query row]
-    u32x4 qreg[NT][KS];
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-        const int j = (qt0 + qt) * 16 + i16;
-        const bool ok = (qt0 + qt) < a.n_qt && j < a.nrows;
+    const uint16_t* kring = a.kr + (size_t)bk * a.W * D;
+    const uint16_t* vring = a.vr + (size_t)bk * a.W * D;
+    const size_t blk_stride = (size_t)a.HKV * D;  // between block rows
+    const uint16_t* kblk = a.kb + ((size_t)b * a.G * a.HKV + kvh) * D;
+    const uint16_t* vblk = a.vb + ((size_t)b * a.G * a.HKV + kvh) * D;
+
+    // this wave's Q^T operand: B[k = dims (s, g)][col = query row]
+    u32x4 qreg[KS];
+    {
+        const int j = qt * 16 + i16;
+        const bool ok = qt < a.n_qt && j < a.nrows;
         const int r = ok ? j / a.group : 0, hl = ok ? j % a.group : 0;
         const uint16_t* qrow = a.q + ((size_t)((size_t)b * a.G + r) * a.HQ + kvh * a.group + hl) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[qt][s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
+            qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
         }
     }
 
-    f32x4 o[DT][NT];
-    float m[NT], l[NT];
+    // staging registers of the next tile
+    u32x4 kst[KPT];
+    u32x4 vst[VPT][4];
+    auto row_ptr = [&](const uint16_t* ring, const uint16_t* blk, int t) -> const uint16_t* {
+        return t < n ? ring + (size_t)t * D : blk + (size_t)(t - n) * blk_stride;
+    };
+    auto gload = [&](int tb) {
+        const bool fast = tb + TK <= n && tb + TK <= t1;  // whole tile in the ring
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-        m[qt] = -INFINITY;
-        l[qt] = 0.f;
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CH, ch = c % CH;
+            const int t = tb + r;
+            if (c < KCH) {
+                if (fast) kst[i] = *reinterpret_cast<const u32x4*>(kring + (size_t)t * D + ch * 8);
+                else kst[i] = t < t1 ? *reinterpret_cast<const u32x4*>(row_ptr(kring, kblk, t) + ch * 8) : z;
+            }
+        }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * D * kVtStride;
-
-    TileRegs<D> cur, nxt;
-    int tb = t0 + wave * kTile;
-    if (tb < t1) load_tile<D>(cur, a, b, kvh, n, tb, t1, lane);
-
-    for (; tb < t1; tb += kWaves * kTile) {
-        const int tbn = tb + kWaves * kTile;
-        if (tbn < t1) load_tile<D>(nxt, a, b, kvh, n, tbn, t1, lane);
-
-        // (3) V^T into this wave's LDS tile: dims 8*dg+i, tokens 4*tg..4*tg+3
-        wave_lds_sync();
-        {
-            const int tg = lane & 7;
+        for (int i = 0; i < VPT; ++i) {
+            const int u = tid + NT * i;
+            const int tg = u / CH, dg = u % CH;
 #pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
-                const int dg = (lane >> 3) + 8 * c;
+            for (int e = 0; e < 4; ++e) {
+                const int t = tb + 4 * tg + e;
+                if (u < VU) {
+                    if (fast) vst[i][e] = *reinterpret_cast<const u32x4*>(vring + (size_t)t * D + dg * 8);
+                    else vst[i][e] = t < t1 ? *reinterpret_cast<const u32x4*>(row_ptr(vring, vblk, t) + dg * 8) : z;
+                }
+            }
+        }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CH, ch = c % CH;
+            if (c < KCH) sm.k[buf][r * CH + (ch ^ (r % CH))] = kst[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int u = tid + NT * i;
+            const int tg = u / CH, dg = u % CH;
+            if (u < VU) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const uint32_t a0 = cur.v[c][0][w], a1 = cur.v[c][1][w];
-                    const uint32_t a2 = cur.v[c][2][w], a3 = cur.v[c][3][w];
+                    const uint32_t a0 = vst[i][0][w], a1 = vst[i][1][w];
+                    const uint32_t a2 = vst[i][2][w], a3 = vst[i][3][w];
                     u32x2 lo, hi;
                     lo[0] = (a0 & 0xffffu) | (a1 << 16);
                     lo[1] = (a2 & 0xffffu) | (a3 << 16);
                     hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
                     hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
                     const int d = dg * 8 + 2 * w;
-                    *reinterpret_cast<u32x2*>(vt + d * kVtStride + 4 * tg) = lo;
-                    *reinterpret_cast<u32x2*>(vt + (d + 1) * kVtStride + 4 * tg) = hi;
+                    *reinterpret_cast<u32x2*>(&sm.vt[buf][d * kVtStride + 4 * tg]) = lo;
+                    *reinterpret_cast<u32x2*>(&sm.vt[buf][(d + 1) * kVtStride + 4 * tg]) = hi;
                 }
             }
         }
+    };
 
-        // (4) S^T = K Q^T
-        f32x4 sacc[2][NT];
+    f32x4 o[DT];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int qt = 0; qt < NT; ++qt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, cur.k[st][s]),
-                        __builtin_bit_cast(bf16x8, qreg[qt][s]), acc, 0, 0, 0);
-                sacc[st][qt] = acc;
-            }
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running reference max of this lane's query column (base 2)
+    float l_run = 0.f;        // this lane's share of sum 2^(x - m_run)
 
-        // (5) online softmax per query column
-        bf16x8 pb[NT];
+    int buf = 0;
+    if (t0 < t1) {
+        gload(t0);
+        swrite(0);
+    }
+    __syncthreads();
+    for (int tb = t0; tb < t1; tb += TK) {
+        const bool more = tb + TK < t1;
+        if (more) gload(tb + TK);
+
+        // S^T = K Q^T for 4 subtiles of 16 keys
+        f32x4 sacc[4];
 #pragma unroll
-        for (int qt = 0; qt < NT; ++qt) {
-            float x[8];
+        for (int st = 0; st < 4; ++st) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int r = st * 16 + i16;
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tb + st * 16 + g * 4 + i;
-                    x[st * 4 + i] = t < t1 ? sacc[st][qt][i] * a.scale_log2 : -INFINITY;
-                }
-            float tmax = x[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-            const float mnew = fmaxf(m[qt], tmax);
-            const float muse = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = fast_exp2(m[qt] - muse);
-            float p[8], psum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = fast_exp2(x[i] - muse);
-                psum += p[i];
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 kv = sm.k[buf][r * CH + ((s * 4 + g) ^ (r % CH))];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                              __builtin_bit_cast(bf16x8, qreg[s]),
+                                                              acc, 0, 0, 0);
             }
-            l[qt] = l[qt] * alpha + psum;
-            m[qt] = mnew;
-            if (alpha != 1.f) {
+            sacc[st] = acc;
+        }
+        // online softmax with a lazily raised reference max
+        float x[16];
+        const bool tail = tb + TK > t1;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = sacc[st][e] * a.scale_log2;
+                x[st * 4 + e] = (tail && tb + st * 16 + g * 4 + e >= t1) ? -INFINITY : v;
             }
+        float tmax = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        if (__ballot(tmax > m_run + kRescaleSlack)) {
+            const float mnew = fmaxf(m_run, tmax);
+            const float alpha = fast_exp2(m_run - mnew);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            m_run = mnew;
+        }
+        float psum = 0.f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = fast_exp2(x[(2 * ks) * 4 + e] - m_run);
+                p[4 + e] = fast_exp2(x[(2 * ks + 1) * 4 + e] - m_run);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) psum += p[e];
             u32x4 pk;
             pk[0] = pack_bf16x2(p[0], p[1]);
             pk[1] = pack_bf16x2(p[2], p[3]);
             pk[2] = pack_bf16x2(p[4], p[5]);
             pk[3] = pack_bf16x2(p[6], p[7]);
-            pb[qt] = __builtin_bit_cast(bf16x8, pk);
+            pb[ks] = __builtin_bit_cast(bf16x8, pk);
         }
-
-        // (6) O^T += V^T P^T
-        wave_lds_sync();
+        l_run += psum;
+        // O^T += V^T P^T, two k-steps of 32 keys
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = vt + (dt * 16 + i16) * kVtStride;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
-            u32x4 av;
-            av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
-            const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+            const uint16_t* vrow = &sm.vt[buf][(dt * 16 + i16) * kVtStride];
 #pragma unroll
-            for (int qt = 0; qt < NT; ++qt)
-                o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[qt], o[dt][qt], 0, 0, 0);
-        }
-        cur = nxt;
-    }
-
-    // lane partial sums -> column sums (the 4 lane groups hold disjoint keys)
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-        l[qt] += __shfl_xor(l[qt], 16, kWave);
-        l[qt] += __shfl_xor(l[qt], 32, kWave);
-    }
-
-    // ---- merge the four waves (deterministic pairwise tree through LDS)
-    __syncthreads();
-    float* obuf = reinterpret_cast<float*>(smem);                      // [2][NT*16*D]
-    float* mlb = obuf + 2 * NT * 16 * D;                               // [4][NT*16][2]
-    if (g == 0) {
-#pragma unroll
-        for (int qt = 0; qt < NT; ++qt) {
-            mlb[(wave * NT * 16 + qt * 16 + i16) * 2 + 0] = m[qt];
-            mlb[(wave * NT * 16 + qt * 16 + i16) * 2 + 1] = l[qt];
-        }
-    }
-    __syncthreads();
-    float M[NT], L[NT];
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-        float mm = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, mlb[(w * NT * 16 + qt * 16 + i16) * 2]);
-        const float muse = mm == -INFINITY ? 0.f : mm;
-        float ll = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            ll += mlb[(w * NT * 16 + qt * 16 + i16) * 2 + 1] *
-                  fast_exp2(mlb[(w * NT * 16 + qt * 16 + i16) * 2] - muse);
-        M[qt] = mm;
-        L[qt] = ll;
-        const float f = fast_exp2(m[qt] - muse);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
-    }
-    // element index of (dt, qt, i) in a wave's O^T registers: lane-major
-    auto oidx = [&](int dt, int qt, int i) { return ((dt * NT + qt) * 4 + i) * 64 + lane; };
-    if (wave >= 2) {
-        float* dst = obuf + (wave - 2) * NT * 16 * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int qt = 0; qt < NT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[oidx(dt, qt, i)] = o[dt][qt][i];
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const float* src = obuf + wave * NT * 16 * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int qt = 0; qt < NT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[dt][qt][i] += src[oidx(dt, qt, i)];
-    }
-    __syncthreads();
-    if (wave == 1) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int qt = 0; qt < NT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) obuf[oidx(dt, qt, i)] = o[dt][qt][i];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < NT; ++qt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[dt][qt][i] += obuf[oidx(dt, qt, i)];
-
-    // ---- write: final output (one split) or the split's partial
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-        const int j = (qt0 + qt) * 16 + i16;
-        if ((qt0 + qt) >= a.n_qt || j >= a.nrows) continue;
-        if (a.n_splits == 1) {
-            const int r = j / a.group, h = kvh * a.group + j % a.group;
-            const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
-            const float inv = 1.f / L[qt];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                u32x2 w2;
-                w2[0] = pack_bf16x2(o[dt][qt][0] * inv, o[dt][qt][1] * inv);
-                w2[1] = pack_bf16x2(o[dt][qt][2] * inv, o[dt][qt][3] * inv);
-                *reinterpret_cast<u32x2*>(a.out + row * D + dt * 16 + g * 4) = w2;
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 32 + 4 * g);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 32 + 16 + 4 * g);
+                u32x4 av;
+                av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                pb[ks], o[dt], 0, 0, 0);
             }
-            if (a.lse && g == 0) a.lse[row] = (M[qt] + __log2f(L[qt])) * (float)kLn2;
-        } else {
-            const size_t prow = ((size_t)bk * a.n_splits + split) * (a.n_qt * 16) + j;
+        }
+        if (more) swrite(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // the 4 lane groups of a column hold disjoint keys: column sum
+    l_run += __shfl_xor(l_run, 16, kWave);
+    l_run += __shfl_xor(l_run, 32, kWave);
+
+    const int j = qt * 16 + i16;
+    if (qt >= a.n_qt || j >= a.nrows) return;
+    if (a.n_splits == 1) {
+        const int r = j / a.group, h = kvh * a.group + j % a.group;
+        const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
+        const float inv = 1.f / l_run;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4*>(a.part_o + prow * D + dt * 16 + g * 4) = o[dt][qt];
-            if (g == 0) {
-                a.part_ml[prow * 2 + 0] = M[qt];
-                a.part_ml[prow * 2 + 1] = L[qt];
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x2 w2;
+            w2[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+            w2[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+            *reinterpret_cast<u32x2*>(a.out + row * D + dt * 16 + g * 4) = w2;
+        }
+        if (a.lse && g == 0) a.lse[row] = (m_run + __log2f(l_run)) * (float)kLn2;
+    } else {
+        const size_t prow = ((size_t)bk * a.n_splits + split) * (a.n_qt * 16) + j;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<f32x4*>(a.part_o + prow * D + dt * 16 + g * 4) = o[dt];
+        if (g == 0) {
+            a.part_ml[prow * 2 + 0] = m_run;
+            a.part_ml[prow * 2 + 1] = l_run;
         }
     }
 }
@@ -423,12 +365,13 @@ struct Attn32Args {
 };
 
 constexpr int kMaxKeys32 = 4096 + 32;
+constexpr int kWaves32 = 4;
 
 __global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
-    __shared__ float sc[kWaves][kMaxKeys32];
-    __shared__ float qs[kWaves][128];
+    __shared__ float sc[kWaves32][kMaxKeys32];
+    __shared__ float qs[kWaves32][128];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int qi = blockIdx.x * kWaves + wave;  // (b, r, h) flattened
+    const int qi = blockIdx.x * kWaves32 + wave;  // (b, r, h) flattened
     if (qi >= a.B * a.G * a.HQ) return;
     const int h = qi % a.HQ, b = qi / (a.HQ * a.G);
     const int kvh = h / (a.HQ / a.HKV);
@@ -473,7 +416,7 @@ __global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
 
 // --------------------------------------------------------------- planning
 struct AttnPlan {
-    int n_qt, nt, n_qgroups, n_splits;
+    int n_qt, nw, n_qgroups, n_splits;
     size_t off_o, off_ml, bytes;
 };
 
@@ -482,17 +425,17 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     const int group = n_q / n_kv;
     const int nrows = group * gamma;
     p.n_qt = (nrows + 15) / 16;
-    p.n_qgroups = (p.n_qt + kMaxNT - 1) / kMaxNT;
-    p.nt = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
+    p.n_qgroups = (p.n_qt + kMaxNW - 1) / kMaxNW;
+    p.nw = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
     if (dtype != DFLASH_DTYPE_BF16) {
         p.n_splits = 1;
         p.bytes = 0;
         return p;
     }
     const long units = (long)batch * n_kv * p.n_qgroups;
-    const long want = kCUs;  // one resident workgroup per CU at this register footprint
+    const long want = (long)kCUs * kWGsPerCU;
     int splits = (int)((want + units - 1) / units);
-    const int max_splits = (window + gamma + kWaves * kTile - 1) / (kWaves * kTile);
+    const int max_splits = (window + gamma + TK * kMinTilesPerSplit - 1) / (TK * kMinTilesPerSplit);
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     p.n_splits = splits;
@@ -506,19 +449,23 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     return p;
 }
 
-template <int D, int NT>
+template <int D, int NW>
 void launch_bf16(const AttnArgs& a, int n_qgroups, hipStream_t st) {
     dim3 grid(a.n_splits, a.B * a.HKV, n_qgroups);
-    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NW>), grid, dim3(64 * NW), 0, st, a);
 }
 
 template <int D>
-void launch_bf16_nt(const AttnArgs& a, int nt, int n_qgroups, hipStream_t st) {
-    switch (nt) {
+void launch_bf16_nw(const AttnArgs& a, int nw, int n_qgroups, hipStream_t st) {
+    switch (nw) {
         case 1: launch_bf16<D, 1>(a, n_qgroups, st); break;
         case 2: launch_bf16<D, 2>(a, n_qgroups, st); break;
         case 3: launch_bf16<D, 3>(a, n_qgroups, st); break;
-        default: launch_bf16<D, 4>(a, n_qgroups, st); break;
+        case 4: launch_bf16<D, 4>(a, n_qgroups, st); break;
+        case 5: launch_bf16<D, 5>(a, n_qgroups, st); break;
+        case 6: launch_bf16<D, 6>(a, n_qgroups, st); break;
+        case 7: launch_bf16<D, 7>(a, n_qgroups, st); break;
+        default: launch_bf16<D, 8>(a, n_qgroups, st); break;
     }
 }
 
@@ -560,8 +507,8 @@ extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v
                      static_cast<const float*>(v_ring), ctx_len, scale,
                      static_cast<float*>(out), lse, batch, gamma, n_q, n_kv, window, d_head};
         const int nq = batch * gamma * n_q;
-        hipLaunchKernelGGL(block_attn_f32_kernel, dim3((nq + kWaves - 1) / kWaves), dim3(256), 0,
-                           st, a);
+        hipLaunchKernelGGL(block_attn_f32_kernel, dim3((nq + kWaves32 - 1) / kWaves32),
+                           dim3(64 * kWaves32), 0, st, a);
         return launch_status();
     }
     AttnArgs a{};
@@ -582,9 +529,9 @@ extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v
     a.nrows = a.group * gamma;
     a.n_qt = p.n_qt;
     a.n_splits = p.n_splits;
-    a.nt_per_group = p.nt;
-    if (d_head == 128) launch_bf16_nt<128>(a, p.nt, p.n_qgroups, st);
-    else launch_bf16_nt<64>(a, p.nt, p.n_qgroups, st);
+    a.nw = p.nw;
+    if (d_head == 128) launch_bf16_nw<128>(a, p.nw, p.n_qgroups, st);
+    else launch_bf16_nw<64>(a, p.nw, p.n_qgroups, st);
     int rc = launch_status();
     if (rc != DFLASH_OK || p.n_splits == 1) return rc;
     dim3 grid(batch * n_kv, p.n_qt);

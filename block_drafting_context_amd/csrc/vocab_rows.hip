@@ -61,29 +61,33 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ------------------------------------------------------- wave top-k state
-struct TopKState {
-    float* lv;   // [64] sorted list
-    int* li;
-    float* bv;   // [kCap + 64] candidate buffer
-    int* bi;
+// Per-wave state of the candidate search.  The LDS arrays are indexed
+// directly from the kernel's __shared__ declarations (never through generic
+// pointers), and the scalars live in registers, so every access is a ds_*
+// instruction with a compile-time address space.
+constexpr int kNPL = (64 + kBuf + 63) / 64;  // candidates per lane in a rebuild
+
+struct TopKRegs {
     int cnt;     // buffer fill (wave-uniform)
     int lcount;  // list length (wave-uniform)
     float tv;    // filter: an element passes if it ranks ahead of (tv, ti)
     int ti;
 };
 
-// Rebuild the sorted list from list + buffer: k rounds of wave-wide best.
-__device__ __noinline__ void topk_compact(TopKState& s, int k, int lane) {
+// Rebuild the sorted list of `wave` from list + buffer: k rounds of a
+// wave-wide (value desc, index asc) reduction.
+__device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (*li)[64],
+                                             float (*bv)[kBuf], int (*bi)[kBuf], int wave, int k,
+                                             int lane) {
     wave_lds_sync();
-    constexpr int NPL = (64 + kBuf + 63) / 64;
     const int N = s.lcount + s.cnt;
-    float cv[NPL];
-    int ci[NPL];
+    float cv[kNPL];
+    int ci[kNPL];
 #pragma unroll
-    for (int e = 0; e < NPL; ++e) {
+    for (int e = 0; e < kNPL; ++e) {
         const int at = e * 64 + lane;
-        if (at < s.lcount) { cv[e] = s.lv[at]; ci[e] = s.li[at]; }
-        else if (at < N) { cv[e] = s.bv[at - s.lcount]; ci[e] = s.bi[at - s.lcount]; }
+        if (at < s.lcount) { cv[e] = lv[wave][at]; ci[e] = li[wave][at]; }
+        else if (at < N) { cv[e] = bv[wave][at - s.lcount]; ci[e] = bi[wave][at - s.lcount]; }
         else { cv[e] = -INFINITY; ci[e] = -1; }
     }
     wave_lds_sync();
@@ -91,18 +95,18 @@ __device__ __noinline__ void topk_compact(TopKState& s, int k, int lane) {
     float lastv = -INFINITY;
     int lasti = -1;
     for (int r = 0; r < newcount; ++r) {
-        float bv = cv[0];
-        int bi = ci[0];
+        float b_v = cv[0];
+        int b_i = ci[0];
 #pragma unroll
-        for (int e = 1; e < NPL; ++e)
-            if (ranks_ahead(cv[e], ci[e], bv, bi)) { bv = cv[e]; bi = ci[e]; }
-        wave_best(bv, bi);
+        for (int e = 1; e < kNPL; ++e)
+            if (ranks_ahead(cv[e], ci[e], b_v, b_i)) { b_v = cv[e]; b_i = ci[e]; }
+        wave_best(b_v, b_i);
 #pragma unroll
-        for (int e = 0; e < NPL; ++e)
-            if (ci[e] == bi && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
-        if (lane == 0) { s.lv[r] = bv; s.li[r] = bi; }
-        lastv = bv;
-        lasti = bi;
+        for (int e = 0; e < kNPL; ++e)
+            if (ci[e] == b_i && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
+        if (lane == 0) { lv[wave][r] = b_v; li[wave][r] = b_i; }
+        lastv = b_v;
+        lasti = b_i;
     }
     wave_lds_sync();
     s.lcount = newcount;
@@ -113,14 +117,14 @@ __device__ __noinline__ void topk_compact(TopKState& s, int k, int lane) {
 
 // k-th largest of the 64 lane values (k <= 64): a safe first filter, since
 // k distinct elements are at least that large.
-__device__ float kth_of_lanes(float v, int k, int lane) {
+__device__ __forceinline__ float kth_of_lanes(float v, int k, int lane) {
     float kth = -INFINITY;
     for (int r = 0; r < k; ++r) {
-        float bv = v;
-        int bi = lane;
-        wave_best(bv, bi);
-        if (lane == bi) v = -INFINITY;
-        kth = bv;
+        float b_v = v;
+        int b_i = lane;
+        wave_best(b_v, b_i);
+        if (lane == b_i) v = -INFINITY;
+        kth = b_v;
     }
     return kth;
 }
@@ -142,12 +146,7 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
 
     float best_v = -INFINITY;
     int best_i = -1;
-    TopKState tk;
-    if (MODE & kTopK) {
-        tk.lv = s_lv[wave]; tk.li = s_li[wave];
-        tk.bv = s_bv[wave]; tk.bi = s_bi[wave];
-        tk.cnt = 0; tk.lcount = 0; tk.tv = -INFINITY; tk.ti = -1;
-    }
+    TopKRegs tk{0, 0, -INFINITY, -1};
 
     for (int seg = seg0; seg < seg1; ++seg) {
         float v[kIters][4];
@@ -220,14 +219,14 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                         if (mask) {
                             if (pass) {
                                 const int pos = tk.cnt + lanes_below(mask);
-                                tk.bv[pos] = v[it][c];
-                                tk.bi[pos] = idx;
+                                s_bv[wave][pos] = v[it][c];
+                                s_bi[wave][pos] = idx;
                             }
                             tk.cnt += __popcll(mask);
                         }
                     }
                     if (tk.cnt > kCap) {
-                        topk_compact(tk, a.k, lane);
+                        topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
                         lane_may = lane_m >= tk.tv;
                     }
                 }
@@ -241,17 +240,17 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
         if (lane == 0) { a.cand_v[cbase] = best_v; a.cand_i[cbase] = best_i; }
     }
     if (MODE & kTopK) {
-        if (tk.cnt > 0 || tk.lcount < a.k) topk_compact(tk, a.k, lane);
+        if (tk.cnt > 0 || tk.lcount < a.k) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
         if (lane < a.k) {
-            a.cand_v[cbase + lane] = lane < tk.lcount ? tk.lv[lane] : -INFINITY;
-            a.cand_i[cbase + lane] = lane < tk.lcount ? tk.li[lane] : -1;
+            a.cand_v[cbase + lane] = lane < tk.lcount ? s_lv[wave][lane] : -INFINITY;
+            a.cand_i[cbase + lane] = lane < tk.lcount ? s_li[wave][lane] : -1;
         }
     }
 }
 
 // ----------------------------------------------------------- draws
 // Merge a row's segment statistics: M = max m_s, S = sum s_s 2^((m_s - M) c2).
-__device__ void merge_row_stats(const float* sm, const double* ss, int nseg, float c2, int lane,
+__device__ __forceinline__ void merge_row_stats(const float* sm, const double* ss, int nseg, float c2, int lane,
                                 float& M, double& S) {
     float m = -INFINITY;
     for (int s = lane; s < nseg; s += 64) m = fmaxf(m, sm[s]);
@@ -267,7 +266,7 @@ __device__ void merge_row_stats(const float* sm, const double* ss, int nseg, flo
 // Falls back to the last positive-weight element of the segment when
 // rounding leaves no crossing.  Wave-wide; every lane returns the index.
 template <class WFn>
-__device__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int lane) {
+__device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int lane) {
     const int lo = seg * kSeg + lane * 32;
     float w[32];
     double mine = 0.0;
@@ -312,7 +311,7 @@ __device__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int l
 // segment's weight in the units of target.  Returns the segment and the
 // weight before it.
 template <class SegW>
-__device__ int find_segment(int nseg, double target, const SegW& seg_w, int lane, double& before) {
+__device__ __forceinline__ int find_segment(int nseg, double target, const SegW& seg_w, int lane, double& before) {
     double carry = 0.0;
     int last_pos_seg = -1;
     double before_last = 0.0;
@@ -339,7 +338,7 @@ __device__ int find_segment(int nseg, double target, const SegW& seg_w, int lane
 }
 
 // Draw from softmax(z / T) of one row using its segment statistics.
-__device__ int draw_softmax_row(const float* zr, int V, const float* sm, const double* ss,
+__device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const float* sm, const double* ss,
                                 int nseg, float c2, float M, double S, double u, int lane) {
     const double target = u * S;
     double before = 0.0;
@@ -541,7 +540,7 @@ struct ResidualW {
     }
 };
 
-__device__ ResidualW make_residual(const VerifyArgs& a, int b, int j) {
+__device__ __forceinline__ ResidualW make_residual(const VerifyArgs& a, int b, int j) {
     ResidualW w;
     const size_t row = (size_t)b * a.G + j;
     w.zpr = a.zp + row * a.V;

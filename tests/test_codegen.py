@@ -1,0 +1,40 @@
+"""Code-generation invariants of the gfx950 kernels, checked on the host.
+
+Every kernel addresses global memory with global_* instructions and LDS with
+ds_* instructions whose address space is known at compile time: no generic
+(flat_*) addressing, no private-segment (scratch_*) traffic and no device
+function calls.  The device assembly is produced by hipcc from the library's
+own sources (nothing prebuilt is read)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_drafting_context_amd import build as b
+
+SOURCES = [s for s in b.SOURCES if s.endswith(".hip")]
+
+
+def device_asm(src):
+    cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--offload-arch=gfx950", "-O3",
+           "-std=c++17", "-S", "--cuda-device-only", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", f"-I{b.INCLUDE}", f"-I{b.CSRC}", os.path.join(b.CSRC, src), "-o", "-"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return res.stdout
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_generic_or_private_addressing(src):
+    asm = device_asm(src)
+    bad = {}
+    fn = None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            fn = m.group(1)
+        ins = line.strip().split(" ")[0]
+        if ins.startswith(("flat_", "scratch_", "s_swappc")):
+            bad.setdefault(fn, set()).add(ins)
+    assert not bad, f"{src}: {bad}"
