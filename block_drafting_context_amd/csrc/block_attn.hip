@@ -36,11 +36,11 @@ namespace dfl {
 namespace {
 
 constexpr int TK = 64;             // keys per tile
-constexpr int kVtStride = TK + 4;  // bf16 per V^T row in LDS (8-byte aligned, spreads banks)
-constexpr int kMaxNW = 8;          // query tiles (waves) per workgroup
+constexpr int kStages = 4;         // LDS ring depth (tiles)
+constexpr int kMaxNC = 8;          // consumer waves (16-row query tiles) per workgroup
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kWGsPerCU = 2;       // resident attention workgroups per CU (LDS-limited)
-constexpr int kMinTilesPerSplit = 4;
+constexpr int kWGsPerCU = 1;       // resident attention workgroups per CU (LDS-limited)
+constexpr int kMinTilesPerSplit = 2;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may trail the true max
 
 struct AttnArgs {
@@ -64,35 +64,46 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
-struct AttnSmem {
-    u32x4 k[2][TK * D / 8];               // K tiles, 16-byte chunks, XOR-swizzled per row
-    uint16_t vt[2][D * kVtStride];        // V tiles transposed: [dim][key]
-};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define DFL_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define DFL_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 
-// Block-draft attention, bf16.  Workgroup = NW waves; wave w owns query tile
-// blockIdx.z * NW + w (16 query rows of the GQA group) for every key of the
-// workgroup's split; all waves cooperatively stage each 64-key K/V tile into
-// LDS (double buffer), so every K/V byte is read from HBM once per
-// (sequence, KV head) and used by all query heads of the group.
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
-    constexpr int CH = D / 8;                    // 16-byte chunks per row
-    constexpr int NT = 64 * NW;                  // threads
-    constexpr int KCH = TK * CH;                 // K chunks per tile
-    constexpr int KPT = (KCH + NT - 1) / NT;     // K chunks per thread
-    constexpr int VU = (TK / 4) * CH;            // V units (4 keys x 8 dims) per tile
-    constexpr int VPT = (VU + NT - 1) / NT;      // V units per thread
-    constexpr int DT = D / 16;                   // 16-dim tiles of O^T
-    constexpr int KS = D / 32;                   // k-steps of S^T
-    __shared__ AttnSmem<D> sm;
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    // s_waitcnt encoding on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block-draft attention, bf16.
+//
+// Workgroup = NC consumer waves + 2 producer waves.  Consumer wave w owns
+// query tile blockIdx.z * NC + w (16 rows of the GQA group: (block row, head)
+// pairs) for every key of the workgroup's split.  The two producer waves
+// stream the split's keys in 64-key tiles straight from HBM into a
+// kStages-deep LDS ring with global_load_lds_dwordx4 (no registers, no LDS
+// store instructions): the K producer places each 16-byte chunk c of key row
+// r at chunk c ^ (r % 16) (conflict-free ds_read_b128 of the S^T = K Q^T
+// operand), the V producer places each 32-byte double chunk d of row r at
+// d ^ (r % 8), which ds_read_b64_tr_b16 turns into the keys-by-dims operand of
+// O^T += V^T P^T.  Every K/V byte is read from HBM once per (sequence, KV head)
+// and used by all query heads of the group.
+template <int D, int NC>
+__global__ void __launch_bounds__(64 * (NC + 2)) block_attn_bf16_kernel(AttnArgs a) {
+    constexpr int ROWB = D * 2;               // bytes per key row
+    constexpr int CHR = ROWB / 16;            // 16-byte chunks per row
+    constexpr int TILEB = TK * ROWB;          // bytes of one K (or V) tile
+    constexpr int NI = TILEB / 1024;          // 1 KB load instructions per K (or V) tile
+    constexpr int RPI = 1024 / ROWB;          // rows per load instruction
+    constexpr int DT = D / 16;                // 16-dim tiles of O^T
+    constexpr int KS = D / 32;                // k-steps of S^T
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][TILEB];
 
     const int split = blockIdx.x;
     const int bk = blockIdx.y;
     const int b = bk / a.HKV, kvh = bk % a.HKV;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, i16 = lane & 15;
-    const int qt = blockIdx.z * NW + wave;
 
     const int64_t cl = a.ctx_len[b];
     const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
@@ -101,14 +112,50 @@ __global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
     per = (per + TK - 1) / TK * TK;
     const int t0 = split * per;
     const int t1 = min(t0 + per, total);
+    const int ntiles = t1 > t0 ? (t1 - t0 + TK - 1) / TK : 0;
 
-    const uint16_t* kring = a.kr + (size_t)bk * a.W * D;
-    const uint16_t* vring = a.vr + (size_t)bk * a.W * D;
-    const size_t blk_stride = (size_t)a.HKV * D;  // between block rows
-    const uint16_t* kblk = a.kb + ((size_t)b * a.G * a.HKV + kvh) * D;
-    const uint16_t* vblk = a.vb + ((size_t)b * a.G * a.HKV + kvh) * D;
+    if (wave >= NC) {
+        // ------------------------------------------------------ producers
+        const int kv = wave - NC;  // 0: K, 1: V
+        const uint16_t* ring = (kv == 0 ? a.kr : a.vr) + (size_t)bk * a.W * D;
+        const uint16_t* blk = (kv == 0 ? a.kb : a.vb) + ((size_t)b * a.G * a.HKV + kvh) * D;
+        const size_t blk_stride = (size_t)a.HKV * D;
+        const int rl = lane / CHR, p = lane % CHR;  // row within an instruction, physical chunk
+        auto issue = [&](int tile) {
+            const int tb = t0 + tile * TK;
+            unsigned char* dst = smem[tile % kStages][kv];
+#pragma unroll
+            for (int ins = 0; ins < NI; ++ins) {
+                const int r = ins * RPI + rl;
+                int t = tb + r;
+                if (t >= t1) t = t1 - 1;  // masked key: any valid row
+                int c;
+                if (kv == 0) c = p ^ (r % CHR);
+                else c = ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1);
+                const uint16_t* row = t < n ? ring + (size_t)t * D : blk + (size_t)(t - n) * blk_stride;
+                __builtin_amdgcn_global_load_lds(DFL_GLOBAL(row + c * 8), DFL_LDS(dst + ins * 1024),
+                                                 16, 0, 0);
+            }
+        };
+        const int pre = ntiles < kStages - 1 ? ntiles : kStages - 1;
+        for (int i = 0; i < pre; ++i) issue(i);
+        for (int i = 0; i < ntiles; ++i) {
+            const int ahead = min(kStages - 2, ntiles - 1 - i);  // tiles issued beyond tile i
+            if (ahead >= 2) wait_vmem<2 * NI>();
+            else if (ahead == 1) wait_vmem<NI>();
+            else wait_vmem<0>();
+            // tile i is in LDS; a bare barrier (a release fence here would also
+            // wait for the tiles still in flight)
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (i + kStages - 1 < ntiles) issue(i + kStages - 1);
+        }
+        return;
+    }
 
-    // this wave's Q^T operand: B[k = dims (s, g)][col = query row]
+    // ---------------------------------------------------------- consumers
+    const int qt = blockIdx.z * NC + wave;
     u32x4 qreg[KS];
     {
         const int j = qt * 16 + i16;
@@ -122,83 +169,17 @@ __global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    // staging registers of the next tile
-    u32x4 kst[KPT];
-    u32x4 vst[VPT][4];
-    auto row_ptr = [&](const uint16_t* ring, const uint16_t* blk, int t) -> const uint16_t* {
-        return t < n ? ring + (size_t)t * D : blk + (size_t)(t - n) * blk_stride;
-    };
-    auto gload = [&](int tb) {
-        const bool fast = tb + TK <= n && tb + TK <= t1;  // whole tile in the ring
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CH, ch = c % CH;
-            const int t = tb + r;
-            if (c < KCH) {
-                if (fast) kst[i] = *reinterpret_cast<const u32x4*>(kring + (size_t)t * D + ch * 8);
-                else kst[i] = t < t1 ? *reinterpret_cast<const u32x4*>(row_ptr(kring, kblk, t) + ch * 8) : z;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + NT * i;
-            const int tg = u / CH, dg = u % CH;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = tb + 4 * tg + e;
-                if (u < VU) {
-                    if (fast) vst[i][e] = *reinterpret_cast<const u32x4*>(vring + (size_t)t * D + dg * 8);
-                    else vst[i][e] = t < t1 ? *reinterpret_cast<const u32x4*>(row_ptr(vring, vblk, t) + dg * 8) : z;
-                }
-            }
-        }
-    };
-    auto swrite = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CH, ch = c % CH;
-            if (c < KCH) sm.k[buf][r * CH + (ch ^ (r % CH))] = kst[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + NT * i;
-            const int tg = u / CH, dg = u % CH;
-            if (u < VU) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t a0 = vst[i][0][w], a1 = vst[i][1][w];
-                    const uint32_t a2 = vst[i][2][w], a3 = vst[i][3][w];
-                    u32x2 lo, hi;
-                    lo[0] = (a0 & 0xffffu) | (a1 << 16);
-                    lo[1] = (a2 & 0xffffu) | (a3 << 16);
-                    hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                    hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-                    const int d = dg * 8 + 2 * w;
-                    *reinterpret_cast<u32x2*>(&sm.vt[buf][d * kVtStride + 4 * tg]) = lo;
-                    *reinterpret_cast<u32x2*>(&sm.vt[buf][(d + 1) * kVtStride + 4 * tg]) = hi;
-                }
-            }
-        }
-    };
-
     f32x4 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;  // running reference max of this lane's query column (base 2)
     float l_run = 0.f;        // this lane's share of sum 2^(x - m_run)
 
-    int buf = 0;
-    if (t0 < t1) {
-        gload(t0);
-        swrite(0);
-    }
-    __syncthreads();
-    for (int tb = t0; tb < t1; tb += TK) {
-        const bool more = tb + TK < t1;
-        if (more) gload(tb + TK);
+    for (int i = 0; i < ntiles; ++i) {
+        __syncthreads();
+        const int tb = t0 + i * TK;
+        const unsigned char* kt = smem[i % kStages][0];
+        const unsigned char* vt = smem[i % kStages][1];
 
         // S^T = K Q^T for 4 subtiles of 16 keys
         f32x4 sacc[4];
@@ -208,8 +189,9 @@ __global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
             const int r = st * 16 + i16;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4 kv = sm.k[buf][r * CH + ((s * 4 + g) ^ (r % CH))];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                const u32x4 kvv = *reinterpret_cast<const u32x4*>(
+                    kt + r * ROWB + (((s * 4 + g) ^ (r % CHR)) * 16));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kvv),
                                                               __builtin_bit_cast(bf16x8, qreg[s]),
                                                               acc, 0, 0, 0);
             }
@@ -227,7 +209,7 @@ __global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
             }
         float tmax = x[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
+        for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, x[k]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
         if (__ballot(tmax > m_run + kRescaleSlack)) {
@@ -242,40 +224,48 @@ __global__ void __launch_bounds__(64 * NW) block_attn_bf16_kernel(AttnArgs a) {
         bf16x8 pb[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            float p[8];
+            float pv[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                p[e] = fast_exp2(x[(2 * ks) * 4 + e] - m_run);
-                p[4 + e] = fast_exp2(x[(2 * ks + 1) * 4 + e] - m_run);
+                pv[e] = fast_exp2(x[(2 * ks) * 4 + e] - m_run);
+                pv[4 + e] = fast_exp2(x[(2 * ks + 1) * 4 + e] - m_run);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) psum += p[e];
+            for (int e = 0; e < 8; ++e) psum += pv[e];
             u32x4 pk;
-            pk[0] = pack_bf16x2(p[0], p[1]);
-            pk[1] = pack_bf16x2(p[2], p[3]);
-            pk[2] = pack_bf16x2(p[4], p[5]);
-            pk[3] = pack_bf16x2(p[6], p[7]);
+            pk[0] = pack_bf16x2(pv[0], pv[1]);
+            pk[1] = pack_bf16x2(pv[2], pv[3]);
+            pk[2] = pack_bf16x2(pv[4], pv[5]);
+            pk[3] = pack_bf16x2(pv[6], pv[7]);
             pb[ks] = __builtin_bit_cast(bf16x8, pk);
         }
         l_run += psum;
-        // O^T += V^T P^T, two k-steps of 32 keys
+        // O^T += V^T P^T: the A operand (16 dims x 8 keys per lane) comes from two
+        // transposing reads, keys 32ks+4g+{0..3} and 32ks+16+4g+{0..3}
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = &sm.vt[buf][(dt * 16 + i16) * kVtStride];
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 32 + 4 * g);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 32 + 16 + 4 * g);
+            for (int dt = 0; dt < DT; ++dt) {
+                v4i16 h[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = ks * 32 + hh * 16 + g * 4 + (i16 >> 2);
+                    const unsigned char* src =
+                        vt + r * ROWB + ((dt ^ (r % (CHR / 2))) * 32) + (i16 & 3) * 8;
+                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16*)(DFL_LDS(src)));
+                }
                 u32x4 av;
-                av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
+                av[0] = __builtin_bit_cast(u32x2, h[0])[0];
+                av[1] = __builtin_bit_cast(u32x2, h[0])[1];
+                av[2] = __builtin_bit_cast(u32x2, h[1])[0];
+                av[3] = __builtin_bit_cast(u32x2, h[1])[1];
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                                 pb[ks], o[dt], 0, 0, 0);
             }
         }
-        if (more) swrite(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
     }
+    // the last tile's buffer is not reused, so no trailing barrier is needed
 
     // the 4 lane groups of a column hold disjoint keys: column sum
     l_run += __shfl_xor(l_run, 16, kWave);
@@ -425,7 +415,7 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     const int group = n_q / n_kv;
     const int nrows = group * gamma;
     p.n_qt = (nrows + 15) / 16;
-    p.n_qgroups = (p.n_qt + kMaxNW - 1) / kMaxNW;
+    p.n_qgroups = (p.n_qt + kMaxNC - 1) / kMaxNC;
     p.nw = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
     if (dtype != DFLASH_DTYPE_BF16) {
         p.n_splits = 1;
@@ -449,10 +439,10 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     return p;
 }
 
-template <int D, int NW>
+template <int D, int NC>
 void launch_bf16(const AttnArgs& a, int n_qgroups, hipStream_t st) {
     dim3 grid(a.n_splits, a.B * a.HKV, n_qgroups);
-    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NW>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NC>), grid, dim3(64 * (NC + 2)), 0, st, a);
 }
 
 template <int D>
