@@ -113,52 +113,58 @@ __global__ void __launch_bounds__(256, 2) gemm_nt_bf16_kernel(GemmArgs g) {
 }
 
 // H_t[r] = bf16( g * y / sqrt(mean(y^2) + eps) ),  y = sum_s P1[s][r]
+// One workgroup per row; float4 loads of every split's partial row.
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* P, int S, int M, int N,
                                                       const float* gain, float eps,
                                                       uint16_t* H, uint16_t* h_out) {
-    extern __shared__ float y[];
+    extern __shared__ f32x4 y4[];
     __shared__ float red[4];
     const int r = blockIdx.x, tid = threadIdx.x;
+    const int N4 = N / 4;
     float ss = 0.f;
-    for (int n = tid; n < N; n += 256) {
-        float v = 0.f;
-        for (int s = 0; s < S; ++s) v += P[((size_t)s * M + r) * N + n];
-        y[n] = v;
-        ss += v * v;
+    for (int n4 = tid; n4 < N4; n4 += 256) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s)
+            v += *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * N + 4 * n4);
+        y4[n4] = v;
+        ss += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float inv = 1.f / sqrtf(tot / (float)N + eps);
-    for (int n = tid; n < N; n += 256) {
-        const uint16_t hb = f32_to_bf16_bits(y[n] * inv * gain[n]);
-        H[(size_t)r * N + n] = hb;
-        if (h_out) h_out[(size_t)r * N + n] = hb;
+    for (int n4 = tid; n4 < N4; n4 += 256) {
+        const f32x4 v = y4[n4];
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(gain + 4 * n4);
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0] * inv * gg[0], v[1] * inv * gg[1]);
+        w[1] = pack_bf16x2(v[2] * inv * gg[2], v[3] * inv * gg[3]);
+        *reinterpret_cast<u32x2*>(H + (size_t)r * N + 4 * n4) = w;
+        if (h_out) *reinterpret_cast<u32x2*>(h_out + (size_t)r * N + 4 * n4) = w;
     }
 }
 
-// kv_ring[i, t, seq, h, pos % W, d] = bf16(sum_s P2[s][r][c])
+// kv_ring[i, t, seq, h, pos % W, d..d+3] = bf16(sum_s P2[s][r][c..c+3])
 __global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int S, int M, int NC,
                                                         const int32_t* row_seq,
                                                         const int64_t* row_pos, uint16_t* ring,
                                                         int B, int NKV, int DH, int W) {
     const int r = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 2;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= NC) return;
-    float v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float* p = P + ((size_t)s * M + r) * NC + c;
-        v0 += p[0];
-        v1 += p[1];
-    }
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) v += *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * NC + c);
     const int seq = row_seq[r];
     const int64_t pos = row_pos[r];
     if (seq < 0 || seq >= B || pos < 0) return;  // violated precondition: row skipped
     const int64_t slot = pos % W;
     const int d = c % DH, h = (c / DH) % NKV, lt = c / (DH * NKV);  // lt = layer*2 + t
     const size_t at = ((((size_t)lt * B + seq) * NKV + h) * W + (size_t)slot) * DH + d;
-    *reinterpret_cast<uint32_t*>(ring + at) = pack_bf16x2(v0, v1);
+    u32x2 w;
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(ring + at) = w;
 }
 
 int pick_splits(int M, int N, int K) {
@@ -226,7 +232,7 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
         return DFLASH_ERR_NULL;
     const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
     if (kx % BK || d_model % BN || nkvc % BN || d_model > 8192 || kx > (1L << 30) ||
-        nkvc > (1L << 30) || d_head % 2)
+        nkvc > (1L << 30) || d_head % 4)
         return DFLASH_ERR_UNSUPPORTED;
     const FuseLayout L = fuse_layout(rows, (int)kx, d_model, (int)nkvc);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.bytes)
@@ -246,7 +252,7 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     launch_gemm(H, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
     rc = launch_status();
     if (rc) return rc;
-    dim3 grid((unsigned)((nkvc / 2 + 255) / 256), rows);
+    dim3 grid((unsigned)((nkvc / 4 + 255) / 256), rows);
     hipLaunchKernelGGL(kv_append_kernel, grid, dim3(256), 0, st, P2, L.s2, rows, (int)nkvc,
                        row_seq, row_pos, kv_ring, batch, n_kv, d_head, window);
     return launch_status();

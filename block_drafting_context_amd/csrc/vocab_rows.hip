@@ -262,19 +262,23 @@ __device__ __forceinline__ void merge_row_stats(const float* sm, const double* s
 }
 
 // Smallest element index of segment `seg` whose running weight (increasing
-// index) exceeds tgt; weights come from wfn(index) in fp32, summed in fp64.
+// index) exceeds tgt; wfn.w4(v) gives the fp32 weights of elements v..v+3
+// (the same arithmetic that produced the segment sums), summed in fp64.
 // Falls back to the last positive-weight element of the segment when
 // rounding leaves no crossing.  Wave-wide; every lane returns the index.
 template <class WFn>
 __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int lane) {
     const int lo = seg * kSeg + lane * 32;
     float w[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
+        if (lo + 4 * q < V) w4 = wfn.w4(lo + 4 * q);
+        w[4 * q + 0] = w4[0]; w[4 * q + 1] = w4[1]; w[4 * q + 2] = w4[2]; w[4 * q + 3] = w4[3];
+    }
     double mine = 0.0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        w[j] = (lo + j < V) ? wfn(lo + j) : 0.f;
-        mine += (double)w[j];
-    }
+    for (int j = 0; j < 32; ++j) mine += (double)w[j];
     const double incl = wave_inclusive_scan(mine);
     const double excl = incl - mine;
     const uint64_t hit = ballot(mine > 0.0 && incl > tgt);
@@ -285,6 +289,7 @@ __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const
         if (lane == src) {
             double acc = excl;
             int lastpos = -1;
+#pragma unroll
             for (int j = 0; j < 32; ++j) {
                 if (w[j] > 0.f) lastpos = lo + j;
                 acc += (double)w[j];
@@ -298,9 +303,11 @@ __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const
         if (pos) {
             const int src = 63 - __builtin_clzll(pos);
             int last = -1;
-            if (lane == src)
+            if (lane == src) {
+#pragma unroll
                 for (int j = 0; j < 32; ++j)
                     if (w[j] > 0.f) last = lo + j;
+            }
             result = __shfl(last, src, kWave);
         }
     }
@@ -337,6 +344,21 @@ __device__ __forceinline__ int find_segment(int nseg, double target, const SegW&
     return last_pos_seg;
 }
 
+// Weight 2^((z - m_s) * c2) of softmax(z / T) relative to a segment maximum.
+struct SoftmaxW {
+    const float* zr;
+    float ms, c2;
+    __device__ __forceinline__ f32x4 w4(int v) const {
+        const f32x4 z = *reinterpret_cast<const f32x4*>(zr + v);
+        f32x4 r;
+        r[0] = fast_exp2((z[0] - ms) * c2);
+        r[1] = fast_exp2((z[1] - ms) * c2);
+        r[2] = fast_exp2((z[2] - ms) * c2);
+        r[3] = fast_exp2((z[3] - ms) * c2);
+        return r;
+    }
+};
+
 // Draw from softmax(z / T) of one row using its segment statistics.
 __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const float* sm, const double* ss,
                                 int nseg, float c2, float M, double S, double u, int lane) {
@@ -350,7 +372,7 @@ __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const fl
     const float ms = sm[seg];
     const double f = (double)fast_exp2((ms - M) * c2);
     const double tgt = (target - before) / f;
-    auto wfn = [&](int v) -> float { return fast_exp2((zr[v] - ms) * c2); };
+    const SoftmaxW wfn{zr, ms, c2};
     return draw_in_segment(seg, V, tgt, wfn, lane);
 }
 
@@ -371,17 +393,36 @@ struct TopKFin {
     int32_t* draft;
 };
 
-__global__ void __launch_bounds__(64) topk_finalize_kernel(TopKFin a) {
+// One row per workgroup of two waves: wave 0 merges the waves' candidate
+// lists into the row's top-k (k rounds of a wave-wide reduction over LDS);
+// wave 1 merges the segment statistics into the log-normaliser and draws the
+// drafted token (T > 0).
+__global__ void __launch_bounds__(128) topk_finalize_kernel(TopKFin a) {
     __shared__ float cv[kMaxCand];
     __shared__ int ci[kMaxCand];
-    const int row = blockIdx.x, lane = threadIdx.x;
+    const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int b = row / a.G, r = row % a.G;
+    if (wave == 1) {
+        if (a.T == 0.f) return;
+        float M;
+        double S;
+        const float* sm = a.seg_m + (size_t)row * a.nseg;
+        const double* ss = a.seg_s + (size_t)row * a.nseg;
+        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+        if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
+        if (a.draft) {
+            const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
+            const int tok = draw_softmax_row(a.z + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M,
+                                             S, u, lane);
+            if (lane == 0) a.draft[row] = tok;
+        }
+        return;
+    }
     const int N = a.wpr * a.k;
     const float* src_v = a.cand_v + (size_t)row * N;
     const int* src_i = a.cand_i + (size_t)row * N;
     for (int e = lane; e < N; e += 64) { cv[e] = src_v[e]; ci[e] = src_i[e]; }
     wave_lds_sync();
-    int top0 = -1;
     for (int rr = 0; rr < a.k; ++rr) {
         float bv = -INFINITY;
         int bi = -1, bpos = -1;
@@ -395,27 +436,11 @@ __global__ void __launch_bounds__(64) topk_finalize_kernel(TopKFin a) {
         if (lane == 0) {
             a.topk_idx[(size_t)row * a.k + rr] = wi;
             a.topk_val[(size_t)row * a.k + rr] = wv;
+            if (rr == 0 && a.T == 0.f) {
+                if (a.lse) a.lse[row] = NAN;
+                if (a.draft) a.draft[row] = wi;
+            }
         }
-        if (rr == 0) top0 = wi;
-    }
-    if (a.T == 0.f) {
-        if (lane == 0) {
-            if (a.lse) a.lse[row] = NAN;
-            if (a.draft) a.draft[row] = top0;
-        }
-        return;
-    }
-    float M;
-    double S;
-    const float* sm = a.seg_m + (size_t)row * a.nseg;
-    const double* ss = a.seg_s + (size_t)row * a.nseg;
-    merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
-    if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
-    if (a.draft) {
-        const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
-        const int tok = draw_softmax_row(a.z + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S,
-                                         u, lane);
-        if (lane == 0) a.draft[row] = tok;
     }
 }
 
@@ -445,84 +470,100 @@ struct VerifyArgs {
 
 __device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >= V ? V - 1 : d); }
 
-__global__ void __launch_bounds__(64) verify_commit_kernel(VerifyArgs a) {
-    const int b = blockIdx.x, lane = threadIdx.x;
+constexpr int kCommitWaves = 4;
+
+// Verification of one sequence.  The block's rows are spread over the four
+// waves: each merges its rows' statistics with all 64 lanes (target argmax for
+// greedy; max and fp64 exp-sum for sampled), gathers p and q at the draft and
+// takes the fp64 accept decision.  Wave 0 then forms the accepted prefix and,
+// when every draft survived, draws the bonus token from the target's last row.
+__global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(VerifyArgs a) {
+    __shared__ int s_acc[32], s_tok[32];
+    __shared__ float s_M[32];
+    __shared__ double s_S[32], s_lsep[32], s_lseq[32];
+    const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = a.G;
-    const int r = lane;
-    const bool is_row = r < G, is_draft = r < G - 1;
-    const int d = is_draft ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : 0;
-    bool acc = false;
-    int tgt_tok = -1;
-    double lsep = 0.0, lseq = 0.0;
-    if (a.T == 0.f) {
-        if (is_row) {
+    const double Td = (double)a.T;
+    for (int r = wave; r < G; r += kCommitWaves) {
+        const bool is_draft = r < G - 1;
+        const int d = is_draft ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : 0;
+        if (a.T == 0.f) {
             const size_t cb = ((size_t)b * G + r) * a.wpr;
             float bv = -INFINITY;
             int bi = -1;
-            for (int w = 0; w < a.wpr; ++w)
+            for (int w = lane; w < a.wpr; w += 64)
                 if (ranks_ahead(a.cand_v[cb + w], a.cand_i[cb + w], bv, bi)) {
                     bv = a.cand_v[cb + w];
                     bi = a.cand_i[cb + w];
                 }
-            tgt_tok = bi;
+            wave_best(bv, bi);
+            if (lane == 0) {
+                s_tok[r] = bi;
+                s_acc[r] = is_draft && d == bi;
+            }
+            continue;
         }
-        acc = is_draft && d == tgt_tok;
-    } else if (is_row) {
         const size_t rb = ((size_t)b * G + r) * a.nseg;
-        float M = -INFINITY;
-        for (int s = 0; s < a.nseg; ++s) M = fmaxf(M, a.p_seg_m[rb + s]);
-        double S = 0.0;
-        for (int s = 0; s < a.nseg; ++s)
-            if (a.p_seg_m[rb + s] != -INFINITY)
-                S += a.p_seg_s[rb + s] * (double)fast_exp2((a.p_seg_m[rb + s] - M) * a.c2);
-        const double Td = (double)a.T;
-        lsep = (double)M / Td + log(S);
+        float M;
+        double S;
+        merge_row_stats(a.p_seg_m + rb, a.p_seg_s + rb, a.nseg, a.c2, lane, M, S);
+        const double lsep = (double)M / Td + log(S);
+        double lseq = 0.0;
         if (is_draft) {
             if (a.draft_lse) {
                 lseq = a.draft_lse[(size_t)b * G + r];
             } else {
-                float Mq = -INFINITY;
-                for (int s = 0; s < a.nseg; ++s) Mq = fmaxf(Mq, a.q_seg_m[rb + s]);
-                double Sq = 0.0;
-                for (int s = 0; s < a.nseg; ++s)
-                    if (a.q_seg_m[rb + s] != -INFINITY)
-                        Sq += a.q_seg_s[rb + s] * (double)fast_exp2((a.q_seg_m[rb + s] - Mq) * a.c2);
+                float Mq;
+                double Sq;
+                merge_row_stats(a.q_seg_m + rb, a.q_seg_s + rb, a.nseg, a.c2, lane, Mq, Sq);
                 lseq = (double)Mq / Td + log(Sq);
             }
-            const size_t off = ((size_t)b * G + r) * a.V + d;
-            const double ratio = exp(((double)a.zp[off] - (double)a.zq[off]) / Td - lsep + lseq);
-            const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
-            acc = u < (ratio < 1.0 ? ratio : 1.0);
+        }
+        if (lane == 0) {
+            int acc = 0;
+            if (is_draft) {
+                const size_t off = ((size_t)b * G + r) * a.V + d;
+                const double ratio = exp(((double)a.zp[off] - (double)a.zq[off]) / Td - lsep + lseq);
+                const double u =
+                    philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
+                acc = u < (ratio < 1.0 ? ratio : 1.0);
+            }
+            s_acc[r] = acc;
+            s_M[r] = M;
+            s_S[r] = S;
+            s_lsep[r] = lsep;
+            s_lseq[r] = lseq;
         }
     }
+    __syncthreads();
+    if (wave != 0) return;
+    const int r = lane;
+    const bool is_row = r < G, is_draft = r < G - 1;
+    const bool acc = is_draft && s_acc[r];
     const uint64_t accmask = ballot(acc);
-    const int j = __builtin_ctzll(~accmask) < G - 1 ? __builtin_ctzll(~accmask) : G - 1;
+    const int lead = __builtin_ctzll(~accmask);
+    const int j = lead < G - 1 ? lead : G - 1;
     if (is_draft && a.accepted) a.accepted[(size_t)b * (G - 1) + r] = acc ? 1 : 0;
     int final_tok = -1;
     bool final_known = true;
     if (a.T == 0.f) {
-        final_tok = __shfl(tgt_tok, j, kWave);
+        final_tok = s_tok[j];
     } else if (j == G - 1) {
-        // bonus token from the target's last row
         const int row = b * G + (G - 1);
-        const float* sm = a.p_seg_m + (size_t)row * a.nseg;
-        const double* ss = a.p_seg_s + (size_t)row * a.nseg;
-        float M;
-        double S;
-        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
         const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
-        final_tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+        final_tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, a.p_seg_m + (size_t)row * a.nseg,
+                                     a.p_seg_s + (size_t)row * a.nseg, a.nseg, a.c2, s_M[G - 1],
+                                     s_S[G - 1], u, lane);
     } else {
         final_known = false;  // correction drawn by the residual kernels
-        const double lp = __shfl(lsep, j, kWave), lq = __shfl(lseq, j, kWave);
-        if (lane == 0) { a.seq_lse[2 * b] = lp; a.seq_lse[2 * b + 1] = lq; }
+        if (lane == 0) { a.seq_lse[2 * b] = s_lsep[j]; a.seq_lse[2 * b + 1] = s_lseq[j]; }
     }
     if (lane == 0) {
         a.accept_len[b] = j;
         a.seq_j[b] = final_known ? -1 : j;
     }
     if (is_row) {
-        int tok = r < j ? d : -1;
+        int tok = r < j ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : -1;
         if (r == j) tok = final_known ? final_tok : -1;
         a.out_tokens[(size_t)b * G + r] = tok;
     }
@@ -533,10 +574,17 @@ struct ResidualW {
     const float* zpr;
     const float* zqr;
     float Rp, Rq, Fp, Fq, c2;
-    __device__ float operator()(int v) const {
-        const float p = fast_exp2((zpr[v] - Rp) * c2) * Fp;
-        const float q = fast_exp2((zqr[v] - Rq) * c2) * Fq;
-        return fmaxf(p - q, 0.f);
+    __device__ __forceinline__ f32x4 w4(int v) const {
+        const f32x4 zp = *reinterpret_cast<const f32x4*>(zpr + v);
+        const f32x4 zq = *reinterpret_cast<const f32x4*>(zqr + v);
+        f32x4 r;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
+            const float q = fast_exp2((zq[c] - Rq) * c2) * Fq;
+            r[c] = fmaxf(p - q, 0.f);
+        }
+        return r;
     }
 };
 
@@ -565,17 +613,17 @@ __global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
     if (j < 0) return;
     const ResidualW w = make_residual(a, b, j);
     const int base = seg * kSeg + 4 * lane;
+    f32x4 t4[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int e = base + it * 256;
+        t4[it] = e < a.V ? w.w4(e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     double s = 0.0;
 #pragma unroll
     for (int h = 0; h < kIters / 2; ++h) {
-        float t[8];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int e = base + (2 * h + q) * 256;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) t[q * 4 + c] = e < a.V ? w(e + c) : 0.f;
-        }
-        s += (double)(((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7])));
+        const f32x4 x = t4[2 * h], y = t4[2 * h + 1];
+        s += (double)(((x[0] + x[1]) + (x[2] + x[3])) + ((y[0] + y[1]) + (y[2] + y[3])));
     }
     s = wave_sum(s);
     if (lane == 0) a.resid_s[(size_t)b * a.nseg + seg] = s;
@@ -716,7 +764,7 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
     if (rc) return rc;
     TopKFin f{logits, batch, gamma, vocab, L.sp.nseg, L.sp.wpr, k, temperature, c2, seeds, step,
               s.seg_m, s.seg_s, s.cand_v, s.cand_i, topk_idx, topk_val, lse, draft};
-    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(64), 0, st, f);
+    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(128), 0, st, f);
     return launch_status();
 }
 
@@ -773,7 +821,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     }
     int rc = launch_status();
     if (rc) return rc;
-    hipLaunchKernelGGL(verify_commit_kernel, dim3(batch), dim3(64), 0, st, v);
+    hipLaunchKernelGGL(verify_commit_kernel, dim3(batch), dim3(64 * kCommitWaves), 0, st, v);
     rc = launch_status();
     if (rc || temperature == 0.f) return rc;
     const long waves = (long)batch * L.sp.nseg;

@@ -204,7 +204,7 @@ int spec_verify(const float* target_logits, const float* draft_logits,
  *   kv_ring  [n_layers, 2, batch, n_kv, window, d_head] bf16, in/out
  *   h_t_out  [rows, d_model] bf16, or NULL
  * Supported: d_model % 128 == 0, (n_taps*d_tgt) % 64 == 0,
- *   (n_layers*2*n_kv*d_head) % 128 == 0, d_head even, rows >= 1, d_model <= 8192.
+ *   (n_layers*2*n_kv*d_head) % 128 == 0, d_head % 4 == 0, rows >= 1, d_model <= 8192.
  * Accuracy: bf16 products, fp32 accumulation; H_t is rounded to bf16 before
  * the K/V projection.
  * ------------------------------------------------------------------------ */

@@ -133,7 +133,7 @@ def test_fuse_validation():
     assert fuse(eps=-1.0) == -2
     assert fuse(dm=5100) == -3
     assert fuse(dm=16384) == -3
-    assert fuse(dh=127) == -3
+    assert fuse(dh=126) == -3
     assert fuse() == -4
 
 
