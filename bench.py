@@ -148,6 +148,41 @@ def traffic_from_profile(kernel_src):
     return rec.get("hbm_bytes_per_launch")
 
 
+def fuse_512_rows(dev, warmup, steps):
+    """Secondary figure: dflash_context_fuse for the full drafter step of 64
+    sequences x 8 newly verified tokens (512 rows), timed with HIP events on
+    the launching stream.  Reports the whole call's time and its bf16 MFMA
+    rate (W_c GEMM 134.2 GFLOP + K/V GEMM 53.7 GFLOP)."""
+    Bf, rows = 64, 512
+    fz = syn.fuse_inputs(rows, N_TAPS, D_TGT, D_MODEL, LAYERS, HKV, D, SEED + 1, device=dev)
+    ring = torch.zeros((LAYERS, 2, Bf, HKV, W, D), dtype=torch.bfloat16, device=dev)
+    row_seq = torch.arange(Bf, device=dev, dtype=torch.int32).repeat_interleave(G)
+    row_pos = (W + torch.arange(G, device=dev)).repeat(Bf).to(torch.int64)
+    ws = torch.empty(dfl.dflash_context_fuse_workspace_size(rows, N_TAPS, D_TGT, D_MODEL, LAYERS,
+                                                            HKV, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        dfl.dflash_context_fuse(fz["x"], fz["w_c"], fz["gain"], 1e-6, fz["w_kv"], row_seq,
+                                row_pos, ring, N_TAPS, workspace=ws, stream=stream)
+    for _ in range(max(1, warmup)):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    flops = 2.0 * rows * N_TAPS * D_TGT * D_MODEL + 2.0 * rows * D_MODEL * LAYERS * 2 * HKV * D
+    del ring, ws, fz
+    torch.cuda.empty_cache()
+    return {"rows": rows, "us_per_call": round(us, 2), "gflop": round(flops / 1e9, 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac_of_2500": round(flops / (us * 1e-6) / 2.5e15, 4)}
+
+
 def cpu_baseline(wl, n_seq):
     """The fp64 oracle, as it stands, on `n_seq` sequences of the same workload:
     their 8 fused rows, 5 attention layers, top-k/draws and sampled verify."""
@@ -230,6 +265,8 @@ def main():
     traffic = traffic_from_profile(kernel_src)
     acc = wl["verify_out"]["accept_len"].float().mean().item() + 1.0
 
+    fuse512 = fuse_512_rows(dev, args.warmup, args.steps)
+
     log("[bench] cpu baseline")
     cpu = cpu_baseline(wl, args.cpu_seqs) if args.cpu_seqs > 0 else None
 
@@ -270,6 +307,7 @@ def main():
         "attn_topk_verify_tok_s": round(drafted / ((LAYERS * attn_us + op_us["topk"] +
                                                     op_us["spec_verify"]) * 1e-6), 1),
         "mean_tau": round(acc, 3),
+        "context_fuse_512_rows": fuse512,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -23,92 +23,134 @@
 namespace dfl {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 256, BN = 128, BK = 64;   // workgroup tile and K stage
+constexpr int kGStages = 3;                  // LDS ring depth (2 stages in flight)
+constexpr int kGConsumers = 8;               // 4 x 2 waves of 64 x 64, two per SIMD
+constexpr int kGProducers = 3;               // A rows 0-127, A rows 128-255, B rows
 constexpr int kCUs = 256;
+constexpr int kXCDs = 8;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define DFL_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define DFL_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 struct GemmArgs {
     const uint16_t* A;  // [M, K]
     const uint16_t* B;  // [N, K]
     float* C;           // [S, M, N]
-    int M, N, K, kps;   // kps = K per split
+    int M, N, K, S, n_mt, n_nt, pairs;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// Split-K "NT" GEMM, C[s] = A[:, Ks] B[:, Ks]^T, bf16 in, fp32 partials.
+// Three producer waves stream 64-wide K stages of the 256 x 128 workgroup tile
+// straight into a kGStages-deep LDS ring with global_load_lds_dwordx4 (each
+// 16-byte chunk c of a 128-byte row r placed at chunk c ^ (r % 8)); eight
+// consumer waves (two per SIMD, so one's MFMAs cover the other's LDS waits)
+// each accumulate a 64 x 64 block with 16 x 16 x 32 MFMAs.  Workgroup L runs
+// on XCD L % 8; the M tiles that share a B slice and K range are given to the
+// same XCD so the slice is fetched from HBM once.
+__global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16_kernel(GemmArgs g) {
+    constexpr int ROWB = BK * 2;  // 128 bytes per tile row and stage
+    __shared__ __attribute__((aligned(1024))) unsigned char sa[kGStages][BM * ROWB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb[kGStages][BN * ROWB];
 
-__global__ void __launch_bounds__(256, 2) gemm_nt_bf16_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) u32x4 sa[2][BM * 8];
-    __shared__ __attribute__((aligned(16))) u32x4 sb[2][BN * 8];
+    const int L = blockIdx.x;
+    const int xcd = L % kXCDs, q = L / kXCDs;
+    const int pair = xcd + kXCDs * (q / g.n_mt);
+    const int mt = q % g.n_mt;
+    if (pair >= g.pairs) return;
+    const int nt = pair / g.S, split = pair % g.S;
+    const int m0 = mt * BM, n0 = nt * BN;
+    const int ktiles = g.K / BK;
+    const int kt0 = (int)((long)split * ktiles / g.S), kt1 = (int)((long)(split + 1) * ktiles / g.S);
+    const int nst = kt1 - kt0;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    if (wave >= kGConsumers) {
+        const int pw = wave - kGConsumers;  // 0, 1: A halves; 2: B
+        const int rl = lane >> 3, p = lane & 7;  // row within an instruction, physical chunk
+        auto issue = [&](int st) {
+            const int k0 = (kt0 + st) * BK;
+            unsigned char* dst = pw < 2 ? sa[st % kGStages] + pw * 128 * ROWB : sb[st % kGStages];
+#pragma unroll
+            for (int ins = 0; ins < 16; ++ins) {
+                const int r = ins * 8 + rl;  // row within this producer's 128
+                const int c = p ^ (r % 8);
+                const uint16_t* src;
+                if (pw < 2) {
+                    int m = m0 + pw * 128 + r;
+                    if (m >= g.M) m = g.M - 1;  // rows beyond M: any valid row, never stored
+                    src = g.A + (size_t)m * g.K + k0 + c * 8;
+                } else {
+                    int n = n0 + r;
+                    if (n >= g.N) n = g.N - 1;  // columns beyond N: any valid row, never stored
+                    src = g.B + (size_t)n * g.K + k0 + c * 8;
+                }
+                __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0, 0);
+            }
+        };
+        const int pre = nst < kGStages - 1 ? nst : kGStages - 1;
+        for (int i = 0; i < pre; ++i) issue(i);
+        for (int i = 0; i < nst; ++i) {
+            const int ahead = min(kGStages - 2, nst - 1 - i);
+            if (ahead >= 1) wait_vmem<16>();
+            else wait_vmem<0>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (i + kGStages - 1 < nst) issue(i + kGStages - 1);
+        }
+        return;
+    }
+
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
-    const int kbeg = split * g.kps, kend = kbeg + g.kps;
     const int i16 = lane & 15, grp = lane >> 4;
-
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i, row = id >> 3, ch = id & 7;
-            const int m = m0 + row;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            ra[i] = m < g.M ? *reinterpret_cast<const u32x4*>(g.A + (size_t)m * g.K + k0 + ch * 8) : z;
-            rb[i] = *reinterpret_cast<const u32x4*>(g.B + (size_t)(n0 + row) * g.K + k0 + ch * 8);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i, row = id >> 3, ch = id & 7;
-            sa[buf][swz(row, ch)] = ra[i];
-            sb[buf][swz(row, ch)] = rb[i];
-        }
-    };
-
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    gload(kbeg);
-    sstore(0);
-    __syncthreads();
-    int buf = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
-        const bool more = k0 + BK < kend;
-        if (more) gload(k0 + BK);
+    for (int i = 0; i < nst; ++i) {
+        __syncthreads();
+        const unsigned char* A = sa[i % kGStages];
+        const unsigned char* Bt = sb[i % kGStages];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
+            const int c = s * 4 + grp;
             bf16x8 fa[4], fb[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ra_row = wm * 64 + i * 16 + i16;
-                const int rb_row = wn * 64 + i * 16 + i16;
-                fa[i] = __builtin_bit_cast(bf16x8, sa[buf][swz(ra_row, s * 4 + grp)]);
-                fb[i] = __builtin_bit_cast(bf16x8, sb[buf][swz(rb_row, s * 4 + grp)]);
+            for (int t = 0; t < 4; ++t) {
+                const int ra = wm * 64 + t * 16 + i16;
+                fa[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + ra * ROWB + ((c ^ (ra % 8)) * 16)));
+                const int rb = wn * 64 + t * 16 + i16;
+                fb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bt + rb * ROWB + ((c ^ (rb % 8)) * 16)));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            sstore(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
+                for (int tj = 0; tj < 4; ++tj)
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ti], fb[tj], acc[ti][tj], 0, 0, 0);
         }
     }
-    // acc[i][j]: rows m0+wm*64+i*16+4*grp+e, column n0+wn*64+j*16+i16
+    // acc[i][j]: rows m0 + wm*64 + i*16 + 4*grp + e, column n0 + wn*64 + j*16 + i16
     float* C = g.C + (size_t)split * g.M * g.N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int m = m0 + wm * 64 + i * 16 + 4 * grp + e;
+            const int m = m0 + wm * 64 + ti * 16 + 4 * grp + e;
             if (m >= g.M) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) C[(size_t)m * g.N + n0 + wn * 64 + j * 16 + i16] = acc[i][j][e];
+            for (int tj = 0; tj < 4; ++tj) {
+                const int n = n0 + wn * 64 + tj * 16 + i16;
+                if (n < g.N) C[(size_t)m * g.N + n] = acc[ti][tj][e];
+            }
         }
 }
 
@@ -167,14 +209,22 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int S, i
     *reinterpret_cast<u32x2*>(ring + at) = w;
 }
 
+// Split-K count from a two-term time model: workgroup waves of one CU each
+// times one workgroup's MFMA time, plus writing and re-reading the fp32
+// partials at HBM speed (at most 16 splits).  (Rates are round planning figures for one MI355X
+// CU and for HBM; only their ratio matters.)
 int pick_splits(int M, int N, int K) {
-    const long tiles = (long)((M + BM - 1) / BM) * (N / BN);
+    const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int kt = K / BK;
+    const double cu_rate = 1.25e15 / kCUs;  // sustained bf16 MFMA flop/s of one CU
+    const double hbm = 5.0e12;              // sustained HBM bytes/s
     int best = 1;
-    for (int s = 1; s <= 32 && s <= kt; ++s) {
-        if (kt % s) continue;
-        best = s;
-        if (tiles * s >= 2L * kCUs) break;
+    double best_t = 1e30;
+    for (int s = 1; s <= 16 && s <= kt; ++s) {
+        const long waves = (tiles * s + kCUs - 1) / kCUs;
+        const double wg_time = 2.0 * BM * BN * ((double)K / s) / cu_rate;
+        const double t = waves * wg_time + (s > 1 ? 2.0 * s * (double)M * N * 4 / hbm : 0.0);
+        if (t < best_t * (1.0 - 1e-9)) { best_t = t; best = s; }
     }
     return best;
 }
@@ -198,9 +248,11 @@ FuseLayout fuse_layout(int rows, int kx, int d_model, int nkvc) {
 
 void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K, int S,
                  hipStream_t st) {
-    GemmArgs g{A, B, C, M, N, K, K / S};
-    dim3 grid(N / BN, (M + BM - 1) / BM, S);
-    hipLaunchKernelGGL(gemm_nt_bf16_kernel, grid, dim3(256), 0, st, g);
+    GemmArgs g{A, B, C, M, N, K, S, (M + BM - 1) / BM, (N + BN - 1) / BN, 0};
+    g.pairs = g.n_nt * S;
+    const int pairs_pad = (g.pairs + kXCDs - 1) / kXCDs * kXCDs;
+    hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(pairs_pad * g.n_mt),
+                       dim3(64 * (kGConsumers + kGProducers)), 0, st, g);
 }
 
 }  // namespace
@@ -214,7 +266,7 @@ extern "C" size_t dflash_context_fuse_workspace_size(int rows, int n_taps, int d
         d_head < 1)
         return 0;
     const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
-    if (kx % BK || d_model % BN || d_model % BK || nkvc % BN) return 0;
+    if (kx % 64 || d_model % 128 || nkvc % 128) return 0;
     return fuse_layout(rows, (int)kx, d_model, (int)nkvc).bytes;
 }
 
@@ -231,7 +283,7 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     if (!taps || !w_c || !rms_gain || !w_kv || !row_seq || !row_pos || !kv_ring)
         return DFLASH_ERR_NULL;
     const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
-    if (kx % BK || d_model % BN || nkvc % BN || d_model > 8192 || kx > (1L << 30) ||
+    if (kx % 64 || d_model % 128 || nkvc % 128 || d_model > 8192 || kx > (1L << 30) ||
         nkvc > (1L << 30) || d_head % 4)
         return DFLASH_ERR_UNSUPPORTED;
     const FuseLayout L = fuse_layout(rows, (int)kx, d_model, (int)nkvc);

@@ -148,20 +148,18 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
     int best_i = -1;
     TopKRegs tk{0, 0, -INFINITY, -1};
 
-    for (int seg = seg0; seg < seg1; ++seg) {
-        float v[kIters][4];
+    // the 32 elements of this lane in segment `seg`: base + it*256 + c
+    auto load = [&](f32x4 (&vv)[kIters], int seg) {
         const int base = seg * kSeg + 4 * lane;
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             const int e = base + it * 256;
-            if (e < a.V) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(zr + e);
-                v[it][0] = x[0]; v[it][1] = x[1]; v[it][2] = x[2]; v[it][3] = x[3];
-            } else {
-                v[it][0] = v[it][1] = v[it][2] = v[it][3] = -INFINITY;
-            }
+            const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            vv[it] = e < a.V ? *reinterpret_cast<const f32x4*>(zr + e) : ninf;
         }
-
+    };
+    auto process = [&](const f32x4 (&v)[kIters], int seg) {
+        const int base = seg * kSeg + 4 * lane;
         if (MODE & kArgmax) {
 #pragma unroll
             for (int it = 0; it < kIters; ++it)
@@ -169,18 +167,18 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                 for (int c = 0; c < 4; ++c)
                     if (v[it][c] > best_v) { best_v = v[it][c]; best_i = base + it * 256 + c; }
         }
-
+        float gmax[kIters];
         float lane_m = -INFINITY;
         if (MODE & (kSumExp | kTopK)) {
 #pragma unroll
-            for (int it = 0; it < kIters; ++it)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) lane_m = fmaxf(lane_m, v[it][c]);
+            for (int it = 0; it < kIters; ++it) {
+                gmax[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3]));
+                lane_m = fmaxf(lane_m, gmax[it]);
+            }
         }
-
         if (MODE & kSumExp) {
             const float m = wave_max(lane_m);
-            double s = 0.0;
+            double sacc = 0.0;
             if (m != -INFINITY) {
 #pragma unroll
                 for (int h = 0; h < kIters / 2; ++h) {
@@ -191,30 +189,29 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                         for (int c = 0; c < 4; ++c)
                             w[q * 4 + c] = fast_exp2((v[2 * h + q][c] - m) * a.c2);
                     const float t = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
-                    s += (double)t;
+                    sacc += (double)t;
                 }
             }
-            s = wave_sum(s);
+            sacc = wave_sum(sacc);
             if (lane == 0) {
                 a.seg_m[(size_t)row * a.nseg + seg] = m;
-                a.seg_s[(size_t)row * a.nseg + seg] = s;
+                a.seg_s[(size_t)row * a.nseg + seg] = sacc;
             }
         }
-
         if (MODE & kTopK) {
             if (tk.lcount == 0 && tk.cnt == 0) {
                 tk.tv = kth_of_lanes(lane_m, a.k, lane);
                 tk.ti = -1;  // ties with the filter value pass
             }
-            bool lane_may = lane_m >= tk.tv;
-            if (ballot(lane_may)) {
+            if (ballot(lane_m >= tk.tv)) {
 #pragma unroll
                 for (int it = 0; it < kIters; ++it) {
+                    // skip a load group in which no lane holds a candidate
+                    if (!ballot(gmax[it] >= tk.tv)) continue;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int idx = base + it * 256 + c;
-                        const bool pass = lane_may && idx < a.V &&
-                                          ranks_ahead(v[it][c], idx, tk.tv, tk.ti);
+                        const bool pass = idx < a.V && ranks_ahead(v[it][c], idx, tk.tv, tk.ti);
                         const uint64_t mask = ballot(pass);
                         if (mask) {
                             if (pass) {
@@ -225,12 +222,22 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                             tk.cnt += __popcll(mask);
                         }
                     }
-                    if (tk.cnt > kCap) {
-                        topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
-                        lane_may = lane_m >= tk.tv;
-                    }
+                    if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
                 }
             }
+        }
+    };
+
+    // two segments per trip, each one's loads issued before the other is processed
+    f32x4 va[kIters], vb[kIters];
+    if (seg0 < seg1) load(va, seg0);
+    for (int seg = seg0; seg < seg1; seg += 2) {
+        const bool has_b = seg + 1 < seg1;
+        if (has_b) load(vb, seg + 1);
+        process(va, seg);
+        if (has_b) {
+            if (seg + 2 < seg1) load(va, seg + 2);
+            process(vb, seg + 1);
         }
     }
 
