@@ -183,6 +183,18 @@ def fuse_512_rows(dev, warmup, steps):
             "mfma_frac_of_2500": round(flops / (us * 1e-6) / 2.5e15, 4)}
 
 
+def copy_probe():
+    """Three copies of 2^28 fp32 (1 GiB read + 1 GiB written each): the
+    calibration kernel for the HBM byte counters."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("[bench] copy probe: 3 x 1 GiB copied")
+
+
 def cpu_baseline(wl, n_seq):
     """The fp64 oracle, as it stands, on `n_seq` sequences of the same workload:
     their 8 fused rows, 5 attention layers, top-k/draws and sampled verify."""
@@ -221,7 +233,13 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=B,
                     help="sequences of the workload the CPU oracle baseline runs on "
                          "(default: all of them, i.e. the whole step)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three plain 1 GiB device-to-device copies (reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no "
