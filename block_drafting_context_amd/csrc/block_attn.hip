@@ -6,26 +6,23 @@
 // block's own keys.  "Beam 1.0 DFlash2", "Model": 40 query heads share 8 KV
 // heads of dimension 128; the window holds the last 4,096 context tokens.
 //
-// bf16 path.  One workgroup (4 waves) owns one (sequence, KV head, key split,
-// query-tile group).  The key sequence of a (sequence, KV head) is virtual:
-// index t < n_b reads ring slot t, t >= n_b reads block row t - n_b, so the
-// block keys are streamed like the window keys.  Every query row of the GQA
-// group (group * gamma rows, padded to 16) is a column of one MFMA tile, so
-// each K/V byte is fetched once and used by all query heads of its group.
+// bf16 path.  One workgroup owns one (sequence, KV head, key split, group of
+// query tiles).  The key sequence of a (sequence, KV head) is virtual: index
+// t < n_b reads ring slot t, t >= n_b reads block row t - n_b, so the block
+// keys are streamed like the window keys.  Every query row of the GQA group
+// (group * gamma rows, padded to 16) is a column of one MFMA tile, so each
+// K/V byte is fetched from HBM once and used by all query heads of its group.
 //
-// Per 32-key tile a wave
-//   1. has the tile's K rows in registers, already in the A-operand layout of
-//      v_mfma_f32_16x16x32_bf16 (each lane reads 64 contiguous bytes of rows),
-//      and the tile's V rows in registers (4 tokens x 8 dims per lane);
-//   2. issues the loads of its next tile (register double buffer);
-//   3. writes V transposed into its private LDS tile (8-byte stores);
-//   4. computes S^T = K Q^T (keys x query rows) with MFMA, fp32;
-//   5. runs the online softmax in base 2 (column max across the 4 lane
-//      groups, rescale of the running sum and of O^T);
-//   6. packs P^T to bf16 straight from the S^T accumulator layout and
-//      accumulates O^T += V^T P^T with MFMA, reading V^T from LDS.
-// The four waves of a workgroup take interleaved tiles and are merged
-// through LDS at the end; key splits are merged by a second kernel.
+// Four waves per workgroup, one per SIMD, split the keys: each wave streams
+// its own 32-key K and V tiles into two private LDS stages with non-temporal
+// global_load_lds (HBM to LDS, no registers), so loads and compute overlap
+// without any barrier between waves.  A wave computes all query tiles of its
+// group (up to three 16-column MFMA tiles), so every K/V operand it reads
+// from LDS serves all of them: S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16, V^T read with LDS transpose loads, online softmax
+// in base 2 with a lazily raised reference max.  The waves' partial softmax
+// states are merged through LDS; key splits (only when the grid would not
+// fill the GPU) are merged by a second kernel.
 //
 // fp32 path (small shapes): one wave per query, scores in LDS, exact expf.
 #include <cmath>
@@ -35,12 +32,12 @@
 namespace dfl {
 namespace {
 
-constexpr int TK = 64;             // keys per tile
-constexpr int kStages = 4;         // LDS ring depth (tiles)
-constexpr int kMaxNC = 8;          // consumer waves (16-row query tiles) per workgroup
+constexpr int TK = 32;             // keys per tile
+constexpr int kWaves = 4;          // waves per workgroup, one per SIMD
+constexpr int kMaxNCT = 3;         // 16-column query tiles per wave
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kWGsPerCU = 1;       // resident attention workgroups per CU (LDS-limited)
-constexpr int kMinTilesPerSplit = 2;
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kMinKeysPerSplit = 512;  // at least 4 tiles per wave in every key split
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may trail the true max
 
 struct AttnArgs {
@@ -55,7 +52,7 @@ struct AttnArgs {
     float* lse;
     float* part_o;   // [B*HKV][n_splits][n_qt*16][D]
     float* part_ml;  // [B*HKV][n_splits][n_qt*16][2]  (reference max, sum), base 2
-    int B, G, HQ, HKV, W, group, nrows, n_qt, n_splits, nw;
+    int B, G, HQ, HKV, W, group, nrows, n_qt, n_splits;
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -77,19 +74,20 @@ __device__ __forceinline__ void wait_vmem() {
 
 // Block-draft attention, bf16.
 //
-// Workgroup = NC consumer waves + 2 producer waves.  Consumer wave w owns
-// query tile blockIdx.z * NC + w (16 rows of the GQA group: (block row, head)
-// pairs) for every key of the workgroup's split.  The two producer waves
-// stream the split's keys in 64-key tiles straight from HBM into a
-// kStages-deep LDS ring with global_load_lds_dwordx4 (no registers, no LDS
-// store instructions): the K producer places each 16-byte chunk c of key row
-// r at chunk c ^ (r % 16) (conflict-free ds_read_b128 of the S^T = K Q^T
-// operand), the V producer places each 32-byte double chunk d of row r at
-// d ^ (r % 8), which ds_read_b64_tr_b16 turns into the keys-by-dims operand of
-// O^T += V^T P^T.  Every K/V byte is read from HBM once per (sequence, KV head)
-// and used by all query heads of the group.
-template <int D, int NC>
-__global__ void __launch_bounds__(64 * (NC + 2)) block_attn_bf16_kernel(AttnArgs a) {
+// Workgroup = 4 waves (one per SIMD) for one (sequence, KV head, key split,
+// group of up to NCT query tiles).  Wave w takes the 32-key tiles w, w+4,
+// w+8, ... of the split and streams each into its own two LDS stages with
+// non-temporal global_load_lds_dwordx4 (HBM to LDS, no registers): the next
+// tile is in flight while the current one is computed, and no wave ever
+// waits for another inside the key loop.  K rows are stored with 16-byte
+// chunk c of row r at chunk c ^ (r % 16) (conflict-free ds_read_b128 of the
+// S^T = K Q^T operand); V rows with 32-byte double chunk d of row r at
+// d ^ (r % 8), which ds_read_b64_tr_b16 turns into the dims-by-keys operand
+// of O^T += V^T P^T.  Every K/V operand read from LDS serves all NCT query
+// tiles of the wave.  The four waves' softmax states (max, sum, O) are merged
+// through LDS at the end.
+template <int D, int NCT>
+__global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
     constexpr int ROWB = D * 2;               // bytes per key row
     constexpr int CHR = ROWB / 16;            // 16-byte chunks per row
     constexpr int TILEB = TK * ROWB;          // bytes of one K (or V) tile
@@ -97,7 +95,11 @@ __global__ void __launch_bounds__(64 * (NC + 2)) block_attn_bf16_kernel(AttnArgs
     constexpr int RPI = 1024 / ROWB;          // rows per load instruction
     constexpr int DT = D / 16;                // 16-dim tiles of O^T
     constexpr int KS = D / 32;                // k-steps of S^T
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][TILEB];
+    constexpr int OSTR = 17;                  // padded row stride of the merge buffer
+    static_assert(2 * NI <= 63, "vmcnt");
+    static_assert(kWaves * 2 * 2 * TILEB >= (kWaves * NCT * D * OSTR + 2 * kWaves * NCT * 16) * 4,
+                  "merge buffer fits in the ring");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kWaves][2][2][TILEB];
 
     const int split = blockIdx.x;
     const int bk = blockIdx.y;
@@ -113,186 +115,221 @@ __global__ void __launch_bounds__(64 * (NC + 2)) block_attn_bf16_kernel(AttnArgs
     const int t0 = split * per;
     const int t1 = min(t0 + per, total);
     const int ntiles = t1 > t0 ? (t1 - t0 + TK - 1) / TK : 0;
+    const int mine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;  // tiles of this wave
 
-    if (wave >= NC) {
-        // ------------------------------------------------------ producers
-        const int kv = wave - NC;  // 0: K, 1: V
-        const uint16_t* ring = (kv == 0 ? a.kr : a.vr) + (size_t)bk * a.W * D;
-        const uint16_t* blk = (kv == 0 ? a.kb : a.vb) + ((size_t)b * a.G * a.HKV + kvh) * D;
-        const size_t blk_stride = (size_t)a.HKV * D;
-        const int rl = lane / CHR, p = lane % CHR;  // row within an instruction, physical chunk
-        auto issue = [&](int tile) {
-            const int tb = t0 + tile * TK;
-            unsigned char* dst = smem[tile % kStages][kv];
+    // ---- loads of this wave's j-th tile (tile wave + 4 j of the split) into stage j % 2
+    const uint16_t* kring = a.kr + (size_t)bk * a.W * D;
+    const uint16_t* vring = a.vr + (size_t)bk * a.W * D;
+    const size_t blk_off = ((size_t)b * a.G * a.HKV + kvh) * D;
+    const size_t blk_stride = (size_t)a.HKV * D;
+    const int rl = lane / CHR, p = lane % CHR;  // row within an instruction, physical chunk
+    auto issue = [&](int j) {
+        const int tb = t0 + (wave + kWaves * j) * TK;
+        unsigned char* kd = smem[wave][j & 1][0];
+        unsigned char* vd = smem[wave][j & 1][1];
 #pragma unroll
-            for (int ins = 0; ins < NI; ++ins) {
-                const int r = ins * RPI + rl;
-                int t = tb + r;
-                if (t >= t1) t = t1 - 1;  // masked key: any valid row
-                int c;
-                if (kv == 0) c = p ^ (r % CHR);
-                else c = ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1);
-                const uint16_t* row = t < n ? ring + (size_t)t * D : blk + (size_t)(t - n) * blk_stride;
-                __builtin_amdgcn_global_load_lds(DFL_GLOBAL(row + c * 8), DFL_LDS(dst + ins * 1024),
-                                                 16, 0, 0);
-            }
-        };
-        const int pre = ntiles < kStages - 1 ? ntiles : kStages - 1;
-        for (int i = 0; i < pre; ++i) issue(i);
-        for (int i = 0; i < ntiles; ++i) {
-            const int ahead = min(kStages - 2, ntiles - 1 - i);  // tiles issued beyond tile i
-            if (ahead >= 2) wait_vmem<2 * NI>();
-            else if (ahead == 1) wait_vmem<NI>();
-            else wait_vmem<0>();
-            // tile i is in LDS; a bare barrier (a release fence here would also
-            // wait for the tiles still in flight)
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (i + kStages - 1 < ntiles) issue(i + kStages - 1);
+        for (int ins = 0; ins < NI; ++ins) {
+            const int r = ins * RPI + rl;
+            int t = tb + r;
+            if (t >= t1) t = t1 - 1;  // masked key: any valid row
+            const size_t roff = t < n ? (size_t)t * D : blk_off + (size_t)(t - n) * blk_stride;
+            const uint16_t* kr = (t < n ? kring : a.kb) + roff;
+            const uint16_t* vr = (t < n ? vring : a.vb) + roff;
+            const int ck = p ^ (r % CHR);
+            const int cv = ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1);
+            __builtin_amdgcn_global_load_lds(DFL_GLOBAL(kr + ck * 8), DFL_LDS(kd + ins * 1024), 16, 0,
+                                             kLoadStream);
+            __builtin_amdgcn_global_load_lds(DFL_GLOBAL(vr + cv * 8), DFL_LDS(vd + ins * 1024), 16, 0,
+                                             kLoadStream);
         }
-        return;
-    }
+    };
+    if (mine > 0) issue(0);
 
-    // ---------------------------------------------------------- consumers
-    const int qt = blockIdx.z * NC + wave;
-    u32x4 qreg[KS];
-    {
-        const int j = qt * 16 + i16;
-        const bool ok = qt < a.n_qt && j < a.nrows;
+    // ---- Q^T operands of the wave's query tiles (columns = (block row, head) pairs)
+    u32x4 qreg[NCT][KS];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int j = (blockIdx.z * NCT + ct) * 16 + i16;
+        const bool ok = j < a.nrows;
         const int r = ok ? j / a.group : 0, hl = ok ? j % a.group : 0;
         const uint16_t* qrow = a.q + ((size_t)((size_t)b * a.G + r) * a.HQ + kvh * a.group + hl) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[ct][s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
         }
     }
 
-    f32x4 o[DT];
+    f32x4 o[NCT][DT];
+    float m_run[NCT], l_run[NCT];  // running reference max (base 2) and this lane's share of the sum
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running reference max of this lane's query column (base 2)
-    float l_run = 0.f;        // this lane's share of sum 2^(x - m_run)
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[ct] = -INFINITY;
+        l_run[ct] = 0.f;
+    }
 
-    for (int i = 0; i < ntiles; ++i) {
-        __syncthreads();
-        const int tb = t0 + i * TK;
-        const unsigned char* kt = smem[i % kStages][0];
-        const unsigned char* vt = smem[i % kStages][1];
+    for (int j = 0; j < mine; ++j) {
+        wait_vmem<0>();  // tile j is in LDS (and the Q loads have returned)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (j + 1 < mine) issue(j + 1);  // into the stage of tile j - 1, read completely
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const int tb = t0 + (wave + kWaves * j) * TK;
+        const unsigned char* kt = smem[wave][j & 1][0];
+        const unsigned char* vt = smem[wave][j & 1][1];
 
-        // S^T = K Q^T for 4 subtiles of 16 keys
-        f32x4 sacc[4];
+        // S^T = K Q^T: 2 subtiles of 16 keys x NCT query tiles
+        f32x4 sacc[NCT][2];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int r = st * 16 + i16;
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+            for (int st = 0; st < 2; ++st) sacc[ct][st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int r = st * 16 + i16;
                 const u32x4 kvv = *reinterpret_cast<const u32x4*>(
                     kt + r * ROWB + (((s * 4 + g) ^ (r % CHR)) * 16));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kvv),
-                                                              __builtin_bit_cast(bf16x8, qreg[s]),
-                                                              acc, 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    sacc[ct][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, kvv), __builtin_bit_cast(bf16x8, qreg[ct][s]),
+                        sacc[ct][st], 0, 0, 0);
             }
-            sacc[st] = acc;
-        }
-        // online softmax with a lazily raised reference max
-        float x[16];
+
+        // online softmax per query tile, P^T packed to bf16 in the B-operand layout:
+        // k position 8g + e holds key 4g + e, 8g + 4 + e holds key 16 + 4g + e
         const bool tail = tb + TK > t1;
+        bf16x8 pb[NCT];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+        for (int ct = 0; ct < NCT; ++ct) {
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = sacc[st][e] * a.scale_log2;
-                x[st * 4 + e] = (tail && tb + st * 16 + g * 4 + e >= t1) ? -INFINITY : v;
-            }
-        float tmax = x[0];
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, x[k]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        if (__ballot(tmax > m_run + kRescaleSlack)) {
-            const float mnew = fmaxf(m_run, tmax);
-            const float alpha = fast_exp2(m_run - mnew);
-            l_run *= alpha;
+                for (int e = 0; e < 4; ++e) {
+                    const float v = sacc[ct][st][e];
+                    x[st * 4 + e] = (tail && tb + st * 16 + g * 4 + e >= t1) ? -INFINITY : v;
+                }
+            float tmax = x[0];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-            m_run = mnew;
-        }
-        float psum = 0.f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+            for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
+            tmax = xor32_max(xor16_max(tmax)) * a.scale_log2;
+            const bool raise = __ballot(tmax > m_run[ct] + kRescaleSlack) != 0;  // wave-uniform
+            const float mnew = raise ? fmaxf(m_run[ct], tmax) : m_run[ct];
             float pv[8];
+            float psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pv[e] = fast_exp2(x[(2 * ks) * 4 + e] - m_run);
-                pv[4 + e] = fast_exp2(x[(2 * ks + 1) * 4 + e] - m_run);
+            for (int k = 0; k < 8; ++k) {
+                pv[k] = fast_exp2(fmaf(x[k], a.scale_log2, -mnew));
+                psum += pv[k];
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) psum += pv[e];
             u32x4 pk;
             pk[0] = pack_bf16x2(pv[0], pv[1]);
             pk[1] = pack_bf16x2(pv[2], pv[3]);
             pk[2] = pack_bf16x2(pv[4], pv[5]);
             pk[3] = pack_bf16x2(pv[6], pv[7]);
-            pb[ks] = __builtin_bit_cast(bf16x8, pk);
-        }
-        l_run += psum;
-        // O^T += V^T P^T: the A operand (16 dims x 8 keys per lane) comes from two
-        // transposing reads, keys 32ks+4g+{0..3} and 32ks+16+4g+{0..3}
+            pb[ct] = __builtin_bit_cast(bf16x8, pk);
+            if (raise) {
+                const float alpha = fast_exp2(m_run[ct] - mnew);
+                l_run[ct] *= alpha;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                v4i16 h[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int r = ks * 32 + hh * 16 + g * 4 + (i16 >> 2);
-                    const unsigned char* src =
-                        vt + r * ROWB + ((dt ^ (r % (CHR / 2))) * 32) + (i16 & 3) * 8;
-                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4i16*)(DFL_LDS(src)));
-                }
-                u32x4 av;
-                av[0] = __builtin_bit_cast(u32x2, h[0])[0];
-                av[1] = __builtin_bit_cast(u32x2, h[0])[1];
-                av[2] = __builtin_bit_cast(u32x2, h[1])[0];
-                av[3] = __builtin_bit_cast(u32x2, h[1])[1];
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                pb[ks], o[dt], 0, 0, 0);
+                for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+                m_run[ct] = mnew;
             }
+            l_run[ct] += psum;
         }
-    }
-    // the last tile's buffer is not reused, so no trailing barrier is needed
 
-    // the 4 lane groups of a column hold disjoint keys: column sum
-    l_run += __shfl_xor(l_run, 16, kWave);
-    l_run += __shfl_xor(l_run, 32, kWave);
-
-    const int j = qt * 16 + i16;
-    if (qt >= a.n_qt || j >= a.nrows) return;
-    if (a.n_splits == 1) {
-        const int r = j / a.group, h = kvh * a.group + j % a.group;
-        const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
-        const float inv = 1.f / l_run;
+        // O^T += V^T P^T; the V^T operand (16 dims x 8 keys per lane) comes from two
+        // transposing reads, keys 4g + {0..3} and 16 + 4g + {0..3}
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            u32x2 w2;
-            w2[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-            w2[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-            *reinterpret_cast<u32x2*>(a.out + row * D + dt * 16 + g * 4) = w2;
+            v4i16 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r = hh * 16 + g * 4 + (i16 >> 2);
+                const unsigned char* src = vt + r * ROWB + ((dt ^ (r % (CHR / 2))) * 32) + (i16 & 3) * 8;
+                h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16*)(DFL_LDS(src)));
+            }
+            u32x4 av;
+            av[0] = __builtin_bit_cast(u32x2, h[0])[0];
+            av[1] = __builtin_bit_cast(u32x2, h[0])[1];
+            av[2] = __builtin_bit_cast(u32x2, h[1])[0];
+            av[3] = __builtin_bit_cast(u32x2, h[1])[1];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb[ct],
+                                                                    o[ct][dt], 0, 0, 0);
         }
-        if (a.lse && g == 0) a.lse[row] = (m_run + __log2f(l_run)) * (float)kLn2;
-    } else {
-        const size_t prow = ((size_t)bk * a.n_splits + split) * (a.n_qt * 16) + j;
+    }
+
+    // ---- merge the four waves: M = max m_w, O = sum O_w 2^(m_w - M), L likewise
+    // the 4 lane groups of a column hold disjoint keys: column sums
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) l_run[ct] = xor32_sum(xor16_sum(l_run[ct]));
+    __syncthreads();  // every wave is done with its stages
+    float* mb = reinterpret_cast<float*>(&smem[0][0][0][0]);  // [wave][ct][16]
+    float* lb = mb + kWaves * NCT * 16;                        // [wave][ct][16]
+    float* ob = lb + kWaves * NCT * 16;                        // [wave][ct][D][OSTR]
+    if (g == 0) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mb[(wave * NCT + ct) * 16 + i16] = m_run[ct];
+    }
+    __syncthreads();
+    float M[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        M[ct] = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M[ct] = fmaxf(M[ct], mb[(w * NCT + ct) * 16 + i16]);
+        const float f = m_run[ct] == -INFINITY ? 0.f : fast_exp2(m_run[ct] - M[ct]);
+        if (g == 0) lb[(wave * NCT + ct) * 16 + i16] = l_run[ct] * f;
+        float* od = ob + (size_t)(wave * NCT + ct) * D * OSTR;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<f32x4*>(a.part_o + prow * D + dt * 16 + g * 4) = o[dt];
-        if (g == 0) {
-            a.part_ml[prow * 2 + 0] = m_run;
-            a.part_ml[prow * 2 + 1] = l_run;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) od[(dt * 16 + g * 4 + e) * OSTR + i16] = o[ct][dt][e] * f;
+    }
+    __syncthreads();
+    // wave w finishes the 16-dim tiles dt = w, w + 4, ...
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int j = (blockIdx.z * NCT + ct) * 16 + i16;
+        if (j >= a.nrows) continue;
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) L += lb[(w * NCT + ct) * 16 + i16];
+        const int r = j / a.group, h = kvh * a.group + j % a.group;
+        const size_t row = ((size_t)b * a.G + r) * a.HQ + h;
+        const size_t prow = ((size_t)bk * a.n_splits + split) * (a.n_qt * 16) + j;
+        for (int dt = wave; dt < DT; dt += kWaves) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float* od = ob + (size_t)(w * NCT + ct) * D * OSTR;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += od[(dt * 16 + g * 4 + e) * OSTR + i16];
+            }
+            if (a.n_splits == 1) {
+                const float inv = 1.f / L;
+                u32x2 w2;
+                w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                *reinterpret_cast<u32x2*>(a.out + row * D + dt * 16 + g * 4) = w2;
+            } else {
+                *reinterpret_cast<f32x4*>(a.part_o + prow * D + dt * 16 + g * 4) = acc;
+            }
+        }
+        if (wave == 0 && g == 0) {
+            if (a.n_splits == 1) {
+                if (a.lse) a.lse[row] = (M[ct] + __log2f(L)) * (float)kLn2;
+            } else {
+                a.part_ml[prow * 2 + 0] = M[ct];
+                a.part_ml[prow * 2 + 1] = L;
+            }
         }
     }
 }
@@ -406,7 +443,7 @@ __global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
 
 // --------------------------------------------------------------- planning
 struct AttnPlan {
-    int n_qt, nw, n_qgroups, n_splits;
+    int n_qt, nct, n_qgroups, n_splits;
     size_t off_o, off_ml, bytes;
 };
 
@@ -415,17 +452,20 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     const int group = n_q / n_kv;
     const int nrows = group * gamma;
     p.n_qt = (nrows + 15) / 16;
-    p.n_qgroups = (p.n_qt + kMaxNC - 1) / kMaxNC;
-    p.nw = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
+    p.n_qgroups = (p.n_qt + kMaxNCT - 1) / kMaxNCT;
+    p.nct = (p.n_qt + p.n_qgroups - 1) / p.n_qgroups;
     if (dtype != DFLASH_DTYPE_BF16) {
         p.n_splits = 1;
         p.bytes = 0;
         return p;
     }
+    // split the keys only as far as needed to give every CU a workgroup
+    const int wg_lds = kWaves * 2 * 2 * TK * d_head * 2;
+    const long per_cu = kLdsPerCU / wg_lds;
     const long units = (long)batch * n_kv * p.n_qgroups;
-    const long want = (long)kCUs * kWGsPerCU;
+    const long want = (long)kCUs * per_cu;
     int splits = (int)((want + units - 1) / units);
-    const int max_splits = (window + gamma + TK * kMinTilesPerSplit - 1) / (TK * kMinTilesPerSplit);
+    const int max_splits = (window + gamma + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     p.n_splits = splits;
@@ -439,23 +479,18 @@ AttnPlan plan_attn(int batch, int gamma, int n_q, int n_kv, int d_head, int wind
     return p;
 }
 
-template <int D, int NC>
+template <int D, int NCT>
 void launch_bf16(const AttnArgs& a, int n_qgroups, hipStream_t st) {
     dim3 grid(a.n_splits, a.B * a.HKV, n_qgroups);
-    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NC>), grid, dim3(64 * (NC + 2)), 0, st, a);
+    hipLaunchKernelGGL((block_attn_bf16_kernel<D, NCT>), grid, dim3(64 * kWaves), 0, st, a);
 }
 
 template <int D>
-void launch_bf16_nw(const AttnArgs& a, int nw, int n_qgroups, hipStream_t st) {
-    switch (nw) {
+void launch_bf16_nct(const AttnArgs& a, int nct, int n_qgroups, hipStream_t st) {
+    switch (nct) {
         case 1: launch_bf16<D, 1>(a, n_qgroups, st); break;
         case 2: launch_bf16<D, 2>(a, n_qgroups, st); break;
-        case 3: launch_bf16<D, 3>(a, n_qgroups, st); break;
-        case 4: launch_bf16<D, 4>(a, n_qgroups, st); break;
-        case 5: launch_bf16<D, 5>(a, n_qgroups, st); break;
-        case 6: launch_bf16<D, 6>(a, n_qgroups, st); break;
-        case 7: launch_bf16<D, 7>(a, n_qgroups, st); break;
-        default: launch_bf16<D, 8>(a, n_qgroups, st); break;
+        default: launch_bf16<D, 3>(a, n_qgroups, st); break;
     }
 }
 
@@ -519,9 +554,8 @@ extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v
     a.nrows = a.group * gamma;
     a.n_qt = p.n_qt;
     a.n_splits = p.n_splits;
-    a.nw = p.nw;
-    if (d_head == 128) launch_bf16_nw<128>(a, p.nw, p.n_qgroups, st);
-    else launch_bf16_nw<64>(a, p.nw, p.n_qgroups, st);
+    if (d_head == 128) launch_bf16_nct<128>(a, p.nct, p.n_qgroups, st);
+    else launch_bf16_nct<64>(a, p.nct, p.n_qgroups, st);
     int rc = launch_status();
     if (rc != DFLASH_OK || p.n_splits == 1) return rc;
     dim3 grid(batch * n_kv, p.n_qt);

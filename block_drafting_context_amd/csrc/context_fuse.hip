@@ -81,17 +81,21 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
             for (int ins = 0; ins < 16; ++ins) {
                 const int r = ins * 8 + rl;  // row within this producer's 128
                 const int c = p ^ (r % 8);
-                const uint16_t* src;
                 if (pw < 2) {
+                    // activations: re-read by every column block, keep them cached
                     int m = m0 + pw * 128 + r;
                     if (m >= g.M) m = g.M - 1;  // rows beyond M: any valid row, never stored
-                    src = g.A + (size_t)m * g.K + k0 + c * 8;
+                    const uint16_t* src = g.A + (size_t)m * g.K + k0 + c * 8;
+                    __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0,
+                                                     kLoadDefault);
                 } else {
+                    // weights (the default policy measured faster here than non-temporal)
                     int n = n0 + r;
                     if (n >= g.N) n = g.N - 1;  // columns beyond N: any valid row, never stored
-                    src = g.B + (size_t)n * g.K + k0 + c * 8;
+                    const uint16_t* src = g.B + (size_t)n * g.K + k0 + c * 8;
+                    __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0,
+                                                     kLoadDefault);
                 }
-                __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0, 0);
             }
         };
         const int pre = nst < kGStages - 1 ? nst : kGStages - 1;

@@ -155,7 +155,8 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
         for (int it = 0; it < kIters; ++it) {
             const int e = base + it * 256;
             const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            vv[it] = e < a.V ? *reinterpret_cast<const f32x4*>(zr + e) : ninf;
+            // logits rows are streamed once: non-temporal loads
+            vv[it] = e < a.V ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zr + e)) : ninf;
         }
     };
     auto process = [&](const f32x4 (&v)[kIters], int seg) {

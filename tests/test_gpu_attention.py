@@ -75,13 +75,23 @@ def test_bf16_workload_distribution_and_v_shift():
     _check(a, 1 / np.sqrt(128), what="bf16 V mean 100")
 
 
-def test_bf16_gamma16_two_query_groups():
+def test_bf16_gamma16_five_query_tiles():
     """Trained block size: 16 positions x 5 heads = 80 query rows per KV head."""
     a = syn.attention_inputs(2, 16, 40, 8, 128, 4096, [4096, 3000], seed=6,
                              q_mult=3 * np.sqrt(128), k_std=1.0)
     _check(a, 1 / np.sqrt(128), what="bf16 gamma 16")
 
 
+@pytest.mark.gpu
+def test_bf16_gamma32_two_query_groups():
+    """32 positions x 5 heads = 160 query rows = 10 tiles: more than one workgroup
+    per KV head (each re-streams the keys), plus a ragged short context."""
+    a = syn.attention_inputs(2, 32, 40, 8, 128, 1024, [1024, 70], seed=12,
+                             q_mult=3 * np.sqrt(128), k_std=1.0)
+    _check(a, 1 / np.sqrt(128), what="bf16 gamma 32")
+
+
+@pytest.mark.gpu
 def test_bf16_needle_in_window():
     a = syn.attention_inputs(1, 8, 40, 8, 128, 4096, [3000], seed=7)
     q = a["q"].float()
