@@ -12,10 +12,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdflash.so")
 SOURCES = ["block_attn.hip", "vocab_rows.hip", "context_fuse.hip", "status.cpp"]
 
-# No packed-fp32 instructions anywhere in the device code (the host pass of
-# hipcc prints a harmless "not a recognized feature" warning for this flag).
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+# Device code generation: no packed-fp32 instructions anywhere (the host pass
+# of hipcc prints a harmless "not a recognized feature" warning for this flag),
+# and MFMA results in ordinary VGPRs rather than AGPRs, which keeps the
+# attention kernel's softmax (vector ALU work on the MFMA results) free of
+# register-class copies.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", *DEVICE_FLAGS,
          "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -65,6 +65,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define DFL_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define DFL_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 
+// Wait until every LDS operation of this wave has completed.
+__device__ __forceinline__ void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -96,15 +101,17 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
     constexpr int DT = D / 16;                // 16-dim tiles of O^T
     constexpr int KS = D / 32;                // k-steps of S^T
     constexpr int OSTR = 17;                  // padded row stride of the merge buffer
-    static_assert(2 * NI <= 63, "vmcnt");
+    static_assert(4 * NI <= 63, "vmcnt");
     static_assert(kWaves * 2 * 2 * TILEB >= (kWaves * NCT * D * OSTR + 2 * kWaves * NCT * 16) * 4,
                   "merge buffer fits in the ring");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kWaves][2][2][TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char sq[NCT * 16 * ROWB];
 
     const int split = blockIdx.x;
     const int bk = blockIdx.y;
     const int b = bk / a.HKV, kvh = bk % a.HKV;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int g = lane >> 4, i16 = lane & 15;
 
     const int64_t cl = a.ctx_len[b];
@@ -123,42 +130,68 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
     const size_t blk_off = ((size_t)b * a.G * a.HKV + kvh) * D;
     const size_t blk_stride = (size_t)a.HKV * D;
     const int rl = lane / CHR, p = lane % CHR;  // row within an instruction, physical chunk
-    auto issue = [&](int j) {
+    // The swizzle of instruction ins depends on (ins * RPI + rl) % CHR, which repeats
+    // every NPAT instructions: per-lane byte offsets of the first NPAT instructions.
+    constexpr int NPAT = CHR > RPI ? CHR / RPI : 1;
+    uint32_t koff[NPAT], voff[NPAT];
+#pragma unroll
+    for (int q = 0; q < NPAT; ++q) {
+        const int r = q * RPI + rl;
+        const int ck = p ^ (r % CHR);
+        const int cv = ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1);
+        koff[q] = (uint32_t)((r * D + ck * 8) * 2);
+        voff[q] = (uint32_t)((r * D + cv * 8) * 2);
+    }
+    // loads of this wave's j-th tile (tile wave + 4 j of the split), K (kv = 0) or V (kv = 1)
+    // half, into stage j % 2
+    auto issue = [&](int j, int kv) {
         const int tb = t0 + (wave + kWaves * j) * TK;
-        unsigned char* kd = smem[wave][j & 1][0];
-        unsigned char* vd = smem[wave][j & 1][1];
+        unsigned char* dst = smem[wave][j & 1][kv];
+        const uint16_t* ring = kv ? vring : kring;
+        if (tb + TK <= min(n, t1)) {
+            // whole tile inside the ring: wave-uniform base + per-lane offset
+            const unsigned char* base = reinterpret_cast<const unsigned char*>(ring + (size_t)tb * D);
+#pragma unroll
+            for (int ins = 0; ins < NI; ++ins) {
+                const int q = ins % NPAT, hi = (ins / NPAT) * NPAT * 1024;
+                __builtin_amdgcn_global_load_lds(DFL_GLOBAL(base + hi + (kv ? voff[q] : koff[q])),
+                                                 DFL_LDS(dst + ins * 1024), 16, 0, kLoadStream);
+            }
+            return;
+        }
+        // tile with block rows or past the end of the split: row by row
+        const uint16_t* blk = kv ? a.vb : a.kb;
 #pragma unroll
         for (int ins = 0; ins < NI; ++ins) {
             const int r = ins * RPI + rl;
             int t = tb + r;
             if (t >= t1) t = t1 - 1;  // masked key: any valid row
-            const size_t roff = t < n ? (size_t)t * D : blk_off + (size_t)(t - n) * blk_stride;
-            const uint16_t* kr = (t < n ? kring : a.kb) + roff;
-            const uint16_t* vr = (t < n ? vring : a.vb) + roff;
-            const int ck = p ^ (r % CHR);
-            const int cv = ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1);
-            __builtin_amdgcn_global_load_lds(DFL_GLOBAL(kr + ck * 8), DFL_LDS(kd + ins * 1024), 16, 0,
-                                             kLoadStream);
-            __builtin_amdgcn_global_load_lds(DFL_GLOBAL(vr + cv * 8), DFL_LDS(vd + ins * 1024), 16, 0,
+            const uint16_t* row = t < n ? ring + (size_t)t * D : blk + blk_off + (size_t)(t - n) * blk_stride;
+            const int c = kv ? ((((p >> 1) ^ (r % (CHR / 2)))) << 1) | (p & 1) : p ^ (r % CHR);
+            __builtin_amdgcn_global_load_lds(DFL_GLOBAL(row + c * 8), DFL_LDS(dst + ins * 1024), 16, 0,
                                              kLoadStream);
         }
     };
-    if (mine > 0) issue(0);
-
-    // ---- Q^T operands of the wave's query tiles (columns = (block row, head) pairs)
-    u32x4 qreg[NCT][KS];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int j = (blockIdx.z * NCT + ct) * 16 + i16;
-        const bool ok = j < a.nrows;
-        const int r = ok ? j / a.group : 0, hl = ok ? j % a.group : 0;
-        const uint16_t* qrow = a.q + ((size_t)((size_t)b * a.G + r) * a.HQ + kvh * a.group + hl) * D;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[ct][s] = ok ? *reinterpret_cast<const u32x4*>(qrow + s * 32 + g * 8) : z;
-        }
+    // two tiles in flight per wave: K and V of tiles 0 and 1
+    for (int j = 0; j < 2 && j < mine; ++j) {
+        issue(j, 0);
+        issue(j, 1);
     }
+
+    // ---- the workgroup's query rows (columns of S^T: (block row, head) pairs) in LDS,
+    // 16-byte chunk c of row q at chunk c ^ (q % CHR); rows past the group are zero
+    for (int idx = tid; idx < NCT * 16 * CHR; idx += 64 * kWaves) {
+        const int qr = idx / CHR, c = idx % CHR;
+        const int j = blockIdx.z * NCT * 16 + qr;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j < a.nrows) {
+            const int r = j / a.group, hl = j % a.group;
+            v = *reinterpret_cast<const u32x4*>(
+                a.q + ((size_t)((size_t)b * a.G + r) * a.HQ + kvh * a.group + hl) * D + c * 8);
+        }
+        *reinterpret_cast<u32x4*>(sq + qr * ROWB + ((c ^ (qr % CHR)) * 16)) = v;
+    }
+    __syncthreads();
 
     f32x4 o[NCT][DT];
     float m_run[NCT], l_run[NCT];  // running reference max (base 2) and this lane's share of the sum
@@ -170,23 +203,29 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
         l_run[ct] = 0.f;
     }
 
-    for (int j = 0; j < mine; ++j) {
-        wait_vmem<0>();  // tile j is in LDS (and the Q loads have returned)
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (j + 1 < mine) issue(j + 1);  // into the stage of tile j - 1, read completely
+    // S^T of this wave's tile j (waits for it, starts the loads of tile j + 1);
+    // sx = raw scores with keys past the split masked, tmax = column max in base 2
+    f32x4 sx[NCT][2];
+    float tmax[NCT];
+    auto scores = [&](int j) {
+        // loads are issued in the order K(j) V(j) K(j+1) V(j+1): wait for the first two
+        if (j + 1 < mine) wait_vmem<2 * NI>();
+        else wait_vmem<0>();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const int tb = t0 + (wave + kWaves * j) * TK;
         const unsigned char* kt = smem[wave][j & 1][0];
-        const unsigned char* vt = smem[wave][j & 1][1];
-
-        // S^T = K Q^T: 2 subtiles of 16 keys x NCT query tiles
-        f32x4 sacc[NCT][2];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) sacc[ct][st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < 2; ++st) sx[ct][st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            u32x4 qv[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int qr = ct * 16 + i16;
+                qv[ct] = *reinterpret_cast<const u32x4*>(sq + qr * ROWB + (((s * 4 + g) ^ (qr % CHR)) * 16));
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const int r = st * 16 + i16;
@@ -194,56 +233,61 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
                     kt + r * ROWB + (((s * 4 + g) ^ (r % CHR)) * 16));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-                    sacc[ct][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kvv), __builtin_bit_cast(bf16x8, qreg[ct][s]),
-                        sacc[ct][st], 0, 0, 0);
+                    sx[ct][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, kvv), __builtin_bit_cast(bf16x8, qv[ct]), sx[ct][st],
+                        0, 0, 0);
             }
-
-        // online softmax per query tile, P^T packed to bf16 in the B-operand layout:
-        // k position 8g + e holds key 4g + e, 8g + 4 + e holds key 16 + 4g + e
-        const bool tail = tb + TK > t1;
+        }
+        // K(j) has been read: refill its stage with K(j + 2)
+        wait_lds();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (j + 2 < mine) issue(j + 2, 0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (tb + TK > t1) {  // the split's last, partial tile
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (tb + st * 16 + g * 4 + e >= t1) sx[ct][st][e] = -INFINITY;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float mx = sx[ct][0][0];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sx[ct][st][e]);
+            tmax[ct] = xor32_max(xor16_max(mx)) * a.scale_log2;
+        }
+    };
+    // P^T = 2^(S^T scale - m_run) packed to bf16 in the B-operand layout (k position
+    // 8g + e holds key 4g + e, 8g + 4 + e holds key 16 + 4g + e), then O^T += V^T P^T
+    auto accumulate = [&](int j) {
+        const unsigned char* vt = smem[wave][j & 1][1];
         bf16x8 pb[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            float x[8];
+            float pv[8];
+            float psum = 0.f;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = sacc[ct][st][e];
-                    x[st * 4 + e] = (tail && tb + st * 16 + g * 4 + e >= t1) ? -INFINITY : v;
+                    pv[st * 4 + e] = fast_exp2(fmaf(sx[ct][st][e], a.scale_log2, -m_run[ct]));
+                    psum += pv[st * 4 + e];
                 }
-            float tmax = x[0];
-#pragma unroll
-            for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
-            tmax = xor32_max(xor16_max(tmax)) * a.scale_log2;
-            const bool raise = __ballot(tmax > m_run[ct] + kRescaleSlack) != 0;  // wave-uniform
-            const float mnew = raise ? fmaxf(m_run[ct], tmax) : m_run[ct];
-            float pv[8];
-            float psum = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                pv[k] = fast_exp2(fmaf(x[k], a.scale_log2, -mnew));
-                psum += pv[k];
-            }
             u32x4 pk;
             pk[0] = pack_bf16x2(pv[0], pv[1]);
             pk[1] = pack_bf16x2(pv[2], pv[3]);
             pk[2] = pack_bf16x2(pv[4], pv[5]);
             pk[3] = pack_bf16x2(pv[6], pv[7]);
             pb[ct] = __builtin_bit_cast(bf16x8, pk);
-            if (raise) {
-                const float alpha = fast_exp2(m_run[ct] - mnew);
-                l_run[ct] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-                m_run[ct] = mnew;
-            }
             l_run[ct] += psum;
         }
-
-        // O^T += V^T P^T; the V^T operand (16 dims x 8 keys per lane) comes from two
-        // transposing reads, keys 4g + {0..3} and 16 + 4g + {0..3}
+        // the V^T operand (16 dims x 8 keys per lane) comes from two transposing
+        // reads, keys 4g + {0..3} and 16 + 4g + {0..3}
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             v4i16 h[2];
@@ -264,6 +308,40 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
                 o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb[ct],
                                                                     o[ct][dt], 0, 0, 0);
         }
+        // V(j) has been read: refill its stage with V(j + 2)
+        wait_lds();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (j + 2 < mine) issue(j + 2, 1);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    // The reference max m_run is raised only when a tile's max exceeds it by more
+    // than kRescaleSlack (then O and the sum are rescaled).  That rare step sits
+    // outside the key loop, so the loop touches O only through the matrix cores.
+    int j = 0;
+    while (j < mine) {
+        bool raise = false;
+        for (; j < mine; ++j) {
+            scores(j);
+            bool r = false;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) r = r || (tmax[ct] > m_run[ct] + kRescaleSlack);
+            raise = __ballot(r) != 0;  // wave-uniform
+            if (raise) break;
+            accumulate(j);
+        }
+        if (!raise) break;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float mnew = fmaxf(m_run[ct], tmax[ct]);
+            const float alpha = fast_exp2(m_run[ct] - mnew);
+            l_run[ct] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+            m_run[ct] = mnew;
+        }
+        accumulate(j);
+        ++j;
     }
 
     // ---- merge the four waves: M = max m_w, O = sum O_w 2^(m_w - M), L likewise

@@ -18,8 +18,8 @@ SOURCES = [s for s in b.SOURCES if s.endswith(".hip")]
 
 def device_asm(src):
     cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--offload-arch=gfx950", "-O3",
-           "-std=c++17", "-S", "--cuda-device-only", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", f"-I{b.INCLUDE}", f"-I{b.CSRC}", os.path.join(b.CSRC, src), "-o", "-"]
+           "-std=c++17", "-S", "--cuda-device-only", *b.DEVICE_FLAGS, f"-I{b.INCLUDE}",
+           f"-I{b.CSRC}", os.path.join(b.CSRC, src), "-o", "-"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return res.stdout
