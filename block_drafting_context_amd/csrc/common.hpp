@@ -51,40 +51,98 @@ constexpr int kLoadStream = 2;
 constexpr int kLoadDefault = 0;
 
 // ------------------------------------------------------------ wave helpers
-// v_permlane16_swap / v_permlane32_swap (gfx950) with both operands = v give
-// each lane {v, v of lane l ^ 16} (resp. l ^ 32) in some order, through the
-// VALU instead of an LDS permute; max and sum of the pair are symmetric.
-__device__ __forceinline__ float xor16_max(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// Cross-lane exchange without LDS round trips.  Within a row of 16 lanes, DPP
+// moves (gfx9 controls: quad_perm [1,0,3,2] = lane ^ 1, quad_perm [2,3,0,1] =
+// lane ^ 2, row_half_mirror = 7 - lane within 8, row_mirror = 15 - lane
+// within 16) give each lane a partner whose partial result covers the other
+// half of a growing group; v_permlane16_swap / v_permlane32_swap (gfx950)
+// with both operands = v give each lane {v, v of lane l ^ 16 (resp. l ^ 32)}
+// in some order.  Every combine used with them is symmetric, so all lanes
+// end with bit-identical results.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float xor32_max(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
 }
-__device__ __forceinline__ float xor16_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = dpp_i<CTRL>((int)(unsigned)u), hi = dpp_i<CTRL>((int)(unsigned)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
-__device__ __forceinline__ float xor32_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// {v, partner's v} for partner = lane ^ 16 (W = 16) or lane ^ 32 (W = 32)
+template <int W>
+__device__ __forceinline__ void swap_pair(unsigned v, unsigned& r0, unsigned& r1) {
+    if (W == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        r0 = r[0]; r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        r0 = r[0]; r1 = r[1];
+    }
 }
+template <int W>
+__device__ __forceinline__ float swap_max(float v) {
+    unsigned r0, r1;
+    swap_pair<W>(__float_as_uint(v), r0, r1);
+    return fmaxf(__uint_as_float(r0), __uint_as_float(r1));
+}
+template <int W>
+__device__ __forceinline__ float swap_sum(float v) {
+    unsigned r0, r1;
+    swap_pair<W>(__float_as_uint(v), r0, r1);
+    return __uint_as_float(r0) + __uint_as_float(r1);
+}
+template <int W>
+__device__ __forceinline__ double swap_sum(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    unsigned l0, l1, h0, h1;
+    swap_pair<W>((unsigned)u, l0, l1);
+    swap_pair<W>((unsigned)(u >> 32), h0, h1);
+    const double a = __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0));
+    const double b = __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+    return a + b;
+}
+__device__ __forceinline__ float xor16_max(float v) { return swap_max<16>(v); }
+__device__ __forceinline__ float xor32_max(float v) { return swap_max<32>(v); }
+__device__ __forceinline__ float xor16_sum(float v) { return swap_sum<16>(v); }
+__device__ __forceinline__ float xor32_sum(float v) { return swap_sum<32>(v); }
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    return swap_max<32>(swap_max<16>(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return swap_sum<32>(swap_sum<16>(v));
 }
+__device__ __forceinline__ double wave_sum(double v) {
+    v += dpp_d<kDppXor1>(v);
+    v += dpp_d<kDppXor2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    v += dpp_d<kDppMirror>(v);
+    return swap_sum<32>(swap_sum<16>(v));
+}
+// value of lane `src` (wave-uniform) broadcast to every lane
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ double lane_value(double v, int src) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, src);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), src);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // inclusive prefix sum over the wave's lanes (lane order)
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -102,13 +160,29 @@ __device__ __forceinline__ bool ranks_ahead(float va, int ia, float vb, int ib) 
 }
 
 // wave-wide best (value desc, index asc); idx -1 = empty (ranks last via unsigned compare)
+__device__ __forceinline__ void best_of(float& v, int& i, float ov, int oi) {
+    if (ranks_ahead(ov, oi, v, i)) { v = ov; i = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& v, int& i) {
+    best_of(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
+}
+template <int W>
+__device__ __forceinline__ void best_swap(float& v, int& i) {
+    unsigned v0, v1, i0, i1;
+    swap_pair<W>(__float_as_uint(v), v0, v1);
+    swap_pair<W>((unsigned)i, i0, i1);
+    v = __uint_as_float(v0);
+    i = (int)i0;
+    best_of(v, i, __uint_as_float(v1), (int)i1);
+}
 __device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        float ov = __shfl_xor(v, m, kWave);
-        int oi = __shfl_xor(i, m, kWave);
-        if (ranks_ahead(ov, oi, v, i)) { v = ov; i = oi; }
-    }
+    best_dpp<kDppXor1>(v, i);
+    best_dpp<kDppXor2>(v, i);
+    best_dpp<kDppHalfMirror>(v, i);
+    best_dpp<kDppMirror>(v, i);
+    best_swap<16>(v, i);
+    best_swap<32>(v, i);
 }
 
 // ------------------------------------------------------------------ Philox

@@ -12,10 +12,11 @@
 //
 // The GEMM is "NT": both operands are K-contiguous (weights stored one row
 // per output feature), so global loads and the MFMA operand layout agree.
-// Workgroup tile 128 x 128, K-tile 64, four waves of 64 x 64 built from
-// v_mfma_f32_16x16x32_bf16; LDS double buffer with an XOR swizzle of the
-// 16-byte chunks of each 128-byte row (conflict-free ds_read_b128); split-K
-// across workgroups to fill the 256 CUs when M is only a few hundred rows.
+// Workgroup tile 256 x 160, K-tile 64, eight waves of 64 x 80 built from
+// v_mfma_f32_16x16x32_bf16, fed by three producer waves through a 3-stage LDS
+// ring (XOR swizzle of the 16-byte chunks of each 128-byte row, so the
+// ds_read_b128 operand fetches are conflict-free); split-K across workgroups
+// to fill the 256 CUs when M is only a few hundred rows.
 #include <cmath>
 
 #include "common.hpp"
@@ -23,9 +24,10 @@
 namespace dfl {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;   // workgroup tile and K stage
+constexpr int BM = 256, BN = 160, BK = 64;   // workgroup tile and K stage
+constexpr int WN = BN / 2 / 16;              // 16-column MFMA tiles per consumer wave
 constexpr int kGStages = 3;                  // LDS ring depth (2 stages in flight)
-constexpr int kGConsumers = 8;               // 4 x 2 waves of 64 x 64, two per SIMD
+constexpr int kGConsumers = 8;               // 4 x 2 waves of 64 x 80, two per SIMD
 constexpr int kGProducers = 3;               // A rows 0-127, A rows 128-255, B rows
 constexpr int kCUs = 256;
 constexpr int kXCDs = 8;
@@ -43,53 +45,64 @@ struct GemmArgs {
     const uint16_t* A;  // [M, K]
     const uint16_t* B;  // [N, K]
     float* C;           // [S, M, N]
-    int M, N, K, S, n_mt, n_nt, pairs;
+    int M, N, K, S, n_mt, n_nt;
 };
 
 // Split-K "NT" GEMM, C[s] = A[:, Ks] B[:, Ks]^T, bf16 in, fp32 partials.
-// Three producer waves stream 64-wide K stages of the 256 x 128 workgroup tile
+// Three producer waves stream 64-wide K stages of the 256 x 160 workgroup tile
 // straight into a kGStages-deep LDS ring with global_load_lds_dwordx4 (each
 // 16-byte chunk c of a 128-byte row r placed at chunk c ^ (r % 8)); eight
 // consumer waves (two per SIMD, so one's MFMAs cover the other's LDS waits)
-// each accumulate a 64 x 64 block with 16 x 16 x 32 MFMAs.  Workgroup L runs
-// on XCD L % 8; the M tiles that share a B slice and K range are given to the
-// same XCD so the slice is fetched from HBM once.
+// each accumulate a 64 x 80 block with 16 x 16 x 32 MFMAs.
+//
+// Tile order: workgroup L runs on XCD L % 8.  The split count S divides 8 and
+// split s is computed only on the XCDs x with x % S == s, so each XCD's L2
+// holds a single K slice of A (re-read by every column block of that XCD),
+// and the M tiles of one column block run on one XCD, sharing its B slice.
 __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16_kernel(GemmArgs g) {
     constexpr int ROWB = BK * 2;  // 128 bytes per tile row and stage
+    constexpr int NIB = BN / 8;   // 1 KB load instructions per B stage
     __shared__ __attribute__((aligned(1024))) unsigned char sa[kGStages][BM * ROWB];
     __shared__ __attribute__((aligned(1024))) unsigned char sb[kGStages][BN * ROWB];
 
     const int L = blockIdx.x;
     const int xcd = L % kXCDs, q = L / kXCDs;
-    const int pair = xcd + kXCDs * (q / g.n_mt);
-    const int mt = q % g.n_mt;
-    if (pair >= g.pairs) return;
-    const int nt = pair / g.S, split = pair % g.S;
+    const int mt = q % g.n_mt, r8 = q / g.n_mt;
+    const int split = xcd % g.S;
+    const int nt = r8 * (kXCDs / g.S) + xcd / g.S;
+    if (nt >= g.n_nt) return;
     const int m0 = mt * BM, n0 = nt * BN;
     const int ktiles = g.K / BK;
     const int kt0 = (int)((long)split * ktiles / g.S), kt1 = (int)((long)(split + 1) * ktiles / g.S);
     const int nst = kt1 - kt0;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     if (wave >= kGConsumers) {
         const int pw = wave - kGConsumers;  // 0, 1: A halves; 2: B
         const int rl = lane >> 3, p = lane & 7;  // row within an instruction, physical chunk
         auto issue = [&](int st) {
             const int k0 = (kt0 + st) * BK;
-            unsigned char* dst = pw < 2 ? sa[st % kGStages] + pw * 128 * ROWB : sb[st % kGStages];
+            if (pw < 2) {
+                // activations: re-read by every column block, keep them cached
+                unsigned char* dst = sa[st % kGStages] + pw * 128 * ROWB;
 #pragma unroll
-            for (int ins = 0; ins < 16; ++ins) {
-                const int r = ins * 8 + rl;  // row within this producer's 128
-                const int c = p ^ (r % 8);
-                if (pw < 2) {
-                    // activations: re-read by every column block, keep them cached
+                for (int ins = 0; ins < 16; ++ins) {
+                    const int r = ins * 8 + rl;  // row within this producer's 128
+                    const int c = p ^ (r % 8);
                     int m = m0 + pw * 128 + r;
                     if (m >= g.M) m = g.M - 1;  // rows beyond M: any valid row, never stored
                     const uint16_t* src = g.A + (size_t)m * g.K + k0 + c * 8;
                     __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0,
                                                      kLoadDefault);
-                } else {
-                    // weights (the default policy measured faster here than non-temporal)
+                }
+            } else {
+                // weights (the default policy measured faster here than non-temporal)
+                unsigned char* dst = sb[st % kGStages];
+#pragma unroll
+                for (int ins = 0; ins < NIB; ++ins) {
+                    const int r = ins * 8 + rl;
+                    const int c = p ^ (r % 8);
                     int n = n0 + r;
                     if (n >= g.N) n = g.N - 1;  // columns beyond N: any valid row, never stored
                     const uint16_t* src = g.B + (size_t)n * g.K + k0 + c * 8;
@@ -102,8 +115,12 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
         for (int i = 0; i < pre; ++i) issue(i);
         for (int i = 0; i < nst; ++i) {
             const int ahead = min(kGStages - 2, nst - 1 - i);
-            if (ahead >= 1) wait_vmem<16>();
-            else wait_vmem<0>();
+            if (ahead >= 1) {
+                if (pw < 2) wait_vmem<16>();
+                else wait_vmem<NIB>();
+            } else {
+                wait_vmem<0>();
+            }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -114,11 +131,11 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
 
     const int wm = wave >> 1, wn = wave & 1;
     const int i16 = lane & 15, grp = lane >> 4;
-    f32x4 acc[4][4];
+    f32x4 acc[4][WN];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int i = 0; i < nst; ++i) {
         __syncthreads();
@@ -127,22 +144,25 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int c = s * 4 + grp;
-            bf16x8 fa[4], fb[4];
+            bf16x8 fa[4], fb[WN];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int ra = wm * 64 + t * 16 + i16;
                 fa[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + ra * ROWB + ((c ^ (ra % 8)) * 16)));
-                const int rb = wn * 64 + t * 16 + i16;
+            }
+#pragma unroll
+            for (int t = 0; t < WN; ++t) {
+                const int rb = wn * (WN * 16) + t * 16 + i16;
                 fb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bt + rb * ROWB + ((c ^ (rb % 8)) * 16)));
             }
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
+                for (int tj = 0; tj < WN; ++tj)
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ti], fb[tj], acc[ti][tj], 0, 0, 0);
         }
     }
-    // acc[i][j]: rows m0 + wm*64 + i*16 + 4*grp + e, column n0 + wn*64 + j*16 + i16
+    // acc[i][j]: rows m0 + wm*64 + i*16 + 4*grp + e, column n0 + wn*80 + j*16 + i16
     float* C = g.C + (size_t)split * g.M * g.N;
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
@@ -151,12 +171,13 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
             const int m = m0 + wm * 64 + ti * 16 + 4 * grp + e;
             if (m >= g.M) continue;
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                const int n = n0 + wn * 64 + tj * 16 + i16;
+            for (int tj = 0; tj < WN; ++tj) {
+                const int n = n0 + wn * (WN * 16) + tj * 16 + i16;
                 if (n < g.N) C[(size_t)m * g.N + n] = acc[ti][tj][e];
             }
         }
 }
+
 
 // H_t[r] = bf16( g * y / sqrt(mean(y^2) + eps) ),  y = sum_s P1[s][r]
 // One workgroup per row; float4 loads of every split's partial row.
@@ -217,6 +238,10 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int S, i
 // times one workgroup's MFMA time, plus writing and re-reading the fp32
 // partials at HBM speed (at most 16 splits).  (Rates are round planning figures for one MI355X
 // CU and for HBM; only their ratio matters.)
+// Split-K factor S in {1, 2, 4, 8} (so that splits map onto whole XCDs): the
+// smallest modelled time, with each workgroup bounded by the slower of its
+// MFMA work and its share of the weight stream, plus the fp32 partial sums
+// written and read back once.
 int pick_splits(int M, int N, int K) {
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int kt = K / BK;
@@ -224,10 +249,14 @@ int pick_splits(int M, int N, int K) {
     const double hbm = 5.0e12;              // sustained HBM bytes/s
     int best = 1;
     double best_t = 1e30;
-    for (int s = 1; s <= 16 && s <= kt; ++s) {
-        const long waves = (tiles * s + kCUs - 1) / kCUs;
-        const double wg_time = 2.0 * BM * BN * ((double)K / s) / cu_rate;
-        const double t = waves * wg_time + (s > 1 ? 2.0 * s * (double)M * N * 4 / hbm : 0.0);
+    for (int s = 1; s <= kXCDs && s <= kt; s *= 2) {
+        const long wgs = tiles * s;
+        const long waves = (wgs + kCUs - 1) / kCUs;
+        const long active = wgs < kCUs ? wgs : kCUs;
+        const double mfma_t = 2.0 * BM * BN * ((double)K / s) / cu_rate;
+        const double load_t = 2.0 * BN * ((double)K / s) / (hbm / active);
+        const double t = waves * (mfma_t > load_t ? mfma_t : load_t) +
+                         (s > 1 ? 2.0 * s * (double)M * N * 4 / hbm : 0.0);
         if (t < best_t * (1.0 - 1e-9)) { best_t = t; best = s; }
     }
     return best;
@@ -252,10 +281,10 @@ FuseLayout fuse_layout(int rows, int kx, int d_model, int nkvc) {
 
 void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K, int S,
                  hipStream_t st) {
-    GemmArgs g{A, B, C, M, N, K, S, (M + BM - 1) / BM, (N + BN - 1) / BN, 0};
-    g.pairs = g.n_nt * S;
-    const int pairs_pad = (g.pairs + kXCDs - 1) / kXCDs * kXCDs;
-    hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(pairs_pad * g.n_mt),
+    GemmArgs g{A, B, C, M, N, K, S, (M + BM - 1) / BM, (N + BN - 1) / BN};
+    const int per_round = kXCDs / S;  // column blocks per round of 8 workgroups
+    const int rounds = (g.n_nt + per_round - 1) / per_round;
+    hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(kXCDs * rounds * g.n_mt),
                        dim3(64 * (kGConsumers + kGProducers)), 0, st, g);
 }
 

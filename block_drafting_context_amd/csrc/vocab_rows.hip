@@ -305,7 +305,7 @@ __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const
             }
             if (found < 0) found = lastpos;
         }
-        result = __shfl(found, src, kWave);
+        result = lane_value(found, src);
     } else {
         const uint64_t pos = ballot(mine > 0.0);
         if (pos) {
@@ -316,7 +316,7 @@ __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const
                 for (int j = 0; j < 32; ++j)
                     if (w[j] > 0.f) last = lo + j;
             }
-            result = __shfl(last, src, kWave);
+            result = lane_value(last, src);
         }
     }
     return result;
@@ -337,16 +337,16 @@ __device__ __forceinline__ int find_segment(int nseg, double target, const SegW&
         const uint64_t hit = ballot(w > 0.0 && carry + incl > target);
         if (hit) {
             const int src = __builtin_ctzll(hit);
-            before = carry + __shfl(incl - w, src, kWave);
+            before = carry + lane_value(incl - w, src);
             return s0 + src;
         }
         const uint64_t pos = ballot(w > 0.0);
         if (pos) {
             const int src = 63 - __builtin_clzll(pos);
             last_pos_seg = s0 + src;
-            before_last = carry + __shfl(incl - w, src, kWave);
+            before_last = carry + lane_value(incl - w, src);
         }
-        carry += __shfl(incl, 63, kWave);
+        carry += lane_value(incl, 63);
     }
     before = before_last;
     return last_pos_seg;
