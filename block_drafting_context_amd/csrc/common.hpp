@@ -42,11 +42,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
 
 // Cache-policy operand of global loads (gfx950 encoding: 1 = sc0, 2 = nt,
-// 16 = sc1).  Streams read once per step (context K/V rings, logits) are
-// loaded non-temporal: measured on MI355X, HBM-to-LDS streaming of the
-// 256 x 2 x 1 MB ring pattern runs at 6.9 TB/s with nt against 6.1 TB/s with
-// the default policy.  (The fusion GEMM's weight tiles measured slower with
-// nt and keep the default.)
+// 16 = sc1).  Streams read once per step (context K/V rings, logits, GEMM
+// weights) are loaded non-temporal: measured on MI355X, HBM-to-LDS streaming
+// of the 256 x 2 x 1 MB ring pattern runs at 6.9 TB/s with nt against
+// 6.1 TB/s with the default policy, and nt weight tiles leave the fusion
+// GEMM's re-read activation slice in L2.
 constexpr int kLoadStream = 2;
 constexpr int kLoadDefault = 0;
 

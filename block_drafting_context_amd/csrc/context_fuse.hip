@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
                                                      kLoadDefault);
                 }
             } else {
-                // weights (the default policy measured faster here than non-temporal)
+                // weights: streamed once, non-temporal so they do not evict the A slice
                 unsigned char* dst = sb[st % kGStages];
 #pragma unroll
                 for (int ins = 0; ins < NIB; ++ins) {
@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
                     if (n >= g.N) n = g.N - 1;  // columns beyond N: any valid row, never stored
                     const uint16_t* src = g.B + (size_t)n * g.K + k0 + c * 8;
                     __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0,
-                                                     kLoadDefault);
+                                                     kLoadStream);
                 }
             }
         };
