@@ -181,47 +181,73 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
 
 // H_t[r] = bf16( g * y / sqrt(mean(y^2) + eps) ),  y = sum_s P1[s][r]
 // One workgroup per row; float4 loads of every split's partial row.
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* P, int S, int M, int N,
-                                                      const float* gain, float eps,
-                                                      uint16_t* H, uint16_t* h_out) {
+// H_t row r = RMSNorm(sum_s P[s][r]) * g, one 1,024-thread workgroup per row.  The
+// S split-K partials of a thread's (at most two) float4 columns are loaded together
+// (S is a template argument, so every load is issued before the first add).
+constexpr int kNormThreads = 1024;
+constexpr int kNormChunks = 2;  // float4 columns per thread: d_model <= 8192
+template <int S>
+__global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* P, int M, int N,
+                                                             const float* gain, float eps,
+                                                             uint16_t* H, uint16_t* h_out) {
     extern __shared__ f32x4 y4[];
-    __shared__ float red[4];
+    __shared__ float red[kNormThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int N4 = N / 4;
-    float ss = 0.f;
-    for (int n4 = tid; n4 < N4; n4 += 256) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    f32x4 v[kNormChunks][S];
+#pragma unroll
+    for (int c = 0; c < kNormChunks; ++c) {
+        const int n4 = tid + c * kNormThreads;
+#pragma unroll
         for (int s = 0; s < S; ++s)
-            v += *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * N + 4 * n4);
-        y4[n4] = v;
-        ss += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
+            v[c][s] = n4 < N4 ? *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * N + 4 * n4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < kNormChunks; ++c) {
+        const int n4 = tid + c * kNormThreads;
+        f32x4 y = v[c][0];
+#pragma unroll
+        for (int s = 1; s < S; ++s) y += v[c][s];
+        if (n4 < N4) y4[n4] = y;
+        ss += (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
     const float inv = 1.f / sqrtf(tot / (float)N + eps);
-    for (int n4 = tid; n4 < N4; n4 += 256) {
-        const f32x4 v = y4[n4];
+#pragma unroll
+    for (int c = 0; c < kNormChunks; ++c) {
+        const int n4 = tid + c * kNormThreads;
+        if (n4 >= N4) continue;
+        const f32x4 y = y4[n4];
         const f32x4 gg = *reinterpret_cast<const f32x4*>(gain + 4 * n4);
         u32x2 w;
-        w[0] = pack_bf16x2(v[0] * inv * gg[0], v[1] * inv * gg[1]);
-        w[1] = pack_bf16x2(v[2] * inv * gg[2], v[3] * inv * gg[3]);
+        w[0] = pack_bf16x2(y[0] * inv * gg[0], y[1] * inv * gg[1]);
+        w[1] = pack_bf16x2(y[2] * inv * gg[2], y[3] * inv * gg[3]);
         *reinterpret_cast<u32x2*>(H + (size_t)r * N + 4 * n4) = w;
         if (h_out) *reinterpret_cast<u32x2*>(h_out + (size_t)r * N + 4 * n4) = w;
     }
 }
 
-// kv_ring[i, t, seq, h, pos % W, d..d+3] = bf16(sum_s P2[s][r][c..c+3])
-__global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int S, int M, int NC,
+template <int S>
+__global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int M, int NC,
                                                         const int32_t* row_seq,
                                                         const int64_t* row_pos, uint16_t* ring,
                                                         int B, int NKV, int DH, int W) {
     const int r = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= NC) return;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) v += *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * NC + c);
+    f32x4 p[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) p[s] = *reinterpret_cast<const f32x4*>(P + ((size_t)s * M + r) * NC + c);
+    f32x4 v = p[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += p[s];
     const int seq = row_seq[r];
     const int64_t pos = row_pos[r];
     if (seq < 0 || seq >= B || pos < 0) return;  // violated precondition: row skipped
@@ -279,6 +305,27 @@ FuseLayout fuse_layout(int rows, int kx, int d_model, int nkvc) {
     return L;
 }
 
+void launch_rmsnorm(int S, const float* P, int M, int N, const float* gain, float eps, uint16_t* H,
+                    uint16_t* h_out, hipStream_t st) {
+    const size_t lds = (size_t)N * sizeof(float);
+    switch (S) {
+        case 1: hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(M), dim3(kNormThreads), lds, st, P, M, N, gain, eps, H, h_out); break;
+        case 2: hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(M), dim3(kNormThreads), lds, st, P, M, N, gain, eps, H, h_out); break;
+        case 4: hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(M), dim3(kNormThreads), lds, st, P, M, N, gain, eps, H, h_out); break;
+        default: hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(M), dim3(kNormThreads), lds, st, P, M, N, gain, eps, H, h_out); break;
+    }
+}
+
+void launch_append(int S, dim3 grid, const float* P, int M, int NC, const int32_t* row_seq,
+                   const int64_t* row_pos, uint16_t* ring, int B, int NKV, int DH, int W, hipStream_t st) {
+    switch (S) {
+        case 1: hipLaunchKernelGGL(kv_append_kernel<1>, grid, dim3(256), 0, st, P, M, NC, row_seq, row_pos, ring, B, NKV, DH, W); break;
+        case 2: hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), 0, st, P, M, NC, row_seq, row_pos, ring, B, NKV, DH, W); break;
+        case 4: hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, st, P, M, NC, row_seq, row_pos, ring, B, NKV, DH, W); break;
+        default: hipLaunchKernelGGL(kv_append_kernel<8>, grid, dim3(256), 0, st, P, M, NC, row_seq, row_pos, ring, B, NKV, DH, W); break;
+    }
+}
+
 void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K, int S,
                  hipStream_t st) {
     GemmArgs g{A, B, C, M, N, K, S, (M + BM - 1) / BM, (N + BN - 1) / BN};
@@ -330,15 +377,14 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     launch_gemm(taps, w_c, P1, rows, d_model, (int)kx, L.s1, st);
     int rc = launch_status();
     if (rc) return rc;
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), (size_t)d_model * sizeof(float), st,
-                       P1, L.s1, rows, d_model, rms_gain, eps, H, h_t_out);
+    launch_rmsnorm(L.s1, P1, rows, d_model, rms_gain, eps, H, h_t_out, st);
     rc = launch_status();
     if (rc) return rc;
     launch_gemm(H, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
     rc = launch_status();
     if (rc) return rc;
     dim3 grid((unsigned)((nkvc / 4 + 255) / 256), rows);
-    hipLaunchKernelGGL(kv_append_kernel, grid, dim3(256), 0, st, P2, L.s2, rows, (int)nkvc,
-                       row_seq, row_pos, kv_ring, batch, n_kv, d_head, window);
+    launch_append(L.s2, grid, P2, rows, (int)nkvc, row_seq, row_pos, kv_ring, batch, n_kv, d_head,
+                  window, st);
     return launch_status();
 }
