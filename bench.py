@@ -18,7 +18,10 @@ N(0,1)/sqrt(128), target logits ~ N(0, 2^2), drafter = target + N(0, 1).
 
 Prints one JSON line: drafted tokens/s (value), the roofline of the dominant
 kernel (block attention, HBM-bound) measured with HIP events on its stream
-inside the timed region, and the CPU oracle timed on a bounded sample.
+inside the timed region, and the CPU oracle timed on a bounded sample.  Also
+reported: the same throughput with one attention layer instead of five, the
+512-row fusion call, a device-copy bandwidth (context for the 8 TB/s peak) and
+the oracle on a single host thread.
 """
 from __future__ import annotations
 
@@ -225,6 +228,38 @@ def cpu_baseline(wl, n_seq):
                       f"layers, top-8 + draws, sampled verify), {dt:.1f} s"}
 
 
+def cpu_baseline_one_thread(wl, n_seq):
+    """The same oracle sample on a single host thread (for the thread scaling of the
+    reported baseline)."""
+    import oracle
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        r = cpu_baseline(wl, n_seq)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": r["value"], "unit": r["unit"], "cores": 1, "sample": r["sample"]}
+
+
+def copy_bandwidth(dev):
+    """Device-to-device copy of 1 GiB (read + write), HIP events: context for the
+    8 TB/s peak the roofline is quoted against."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,9 +319,11 @@ def main():
     acc = wl["verify_out"]["accept_len"].float().mean().item() + 1.0
 
     fuse512 = fuse_512_rows(dev, args.warmup, args.steps)
+    copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
     cpu = cpu_baseline(wl, args.cpu_seqs) if args.cpu_seqs > 0 else None
+    cpu1 = cpu_baseline_one_thread(wl, min(2, args.cpu_seqs)) if args.cpu_seqs > 0 else None
 
     res = {
         "metric": "drafted tokens/s for block-attn+top-k+verify at B=32,γ=8,W=4096; % HBM peak",
@@ -324,9 +361,13 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "attn_topk_verify_tok_s": round(drafted / ((LAYERS * attn_us + op_us["topk"] +
                                                     op_us["spec_verify"]) * 1e-6), 1),
+        "attn1_topk_verify_tok_s": round(drafted / ((attn_us + op_us["topk"] +
+                                                     op_us["spec_verify"]) * 1e-6), 1),
+        "device_copy_gbs": copy_gbs,
         "mean_tau": round(acc, 3),
         "context_fuse_512_rows": fuse512,
         "cpu_baseline": cpu,
+        "cpu_baseline_1_thread": cpu1,
     }
     print(json.dumps(res), flush=True)
 
