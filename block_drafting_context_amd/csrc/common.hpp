@@ -143,14 +143,27 @@ __device__ __forceinline__ double lane_value(double v, int src) {
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// inclusive prefix sum over the wave's lanes (lane order)
+// inclusive prefix sum over the wave's lanes (lane order): DPP row_shr 1, 2, 4, 8
+// within rows of 16, then row_bcast15 (rows 1, 3 add lane 15 of the row before)
+// and row_bcast31 (rows 2, 3 add lane 31); lanes without a source add 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_scan_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_scan_d(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = dpp_scan_i<CTRL, ROWMASK>((int)(unsigned)u);
+    const int hi = dpp_scan_i<CTRL, ROWMASK>((int)(unsigned)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        double o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-    }
+    v += dpp_scan_d<0x111, 0xF>(v);
+    v += dpp_scan_d<0x112, 0xF>(v);
+    v += dpp_scan_d<0x114, 0xF>(v);
+    v += dpp_scan_d<0x118, 0xF>(v);
+    v += dpp_scan_d<0x142, 0xA>(v);
+    v += dpp_scan_d<0x143, 0xC>(v);
     return v;
 }
 

@@ -469,7 +469,7 @@ struct VerifyArgs {
     const float* cand_v;    // target rows' per-wave argmax
     const int* cand_i;
     int* seq_j;             // [B]
-    double* seq_lse;        // [B][2]: LSE_p, LSE_q of row j
+    f32x4* seq_w;           // [B]: residual weight constants (R_p, R_q, F_p, F_q) of row j
     double* resid_s;        // [B][nseg]
     int32_t* accept_len;
     int32_t* out_tokens;
@@ -478,7 +478,7 @@ struct VerifyArgs {
 
 __device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >= V ? V - 1 : d); }
 
-constexpr int kCommitWaves = 4;
+constexpr int kCommitWaves = 8;  // one wave per block row (gamma <= 8 in one round)
 
 // Verification of one sequence.  The block's rows are spread over the four
 // waves: each merges its rows' statistics with all 64 lanes (target argmax for
@@ -511,6 +511,13 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
             }
             continue;
         }
+        // the two logits at the draft are loaded before the row statistics are merged
+        float zpd = 0.f, zqd = 0.f;
+        if (is_draft && lane == 0) {
+            const size_t off = ((size_t)b * G + r) * a.V + d;
+            zpd = a.zp[off];
+            zqd = a.zq[off];
+        }
         const size_t rb = ((size_t)b * G + r) * a.nseg;
         float M;
         double S;
@@ -530,8 +537,7 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
         if (lane == 0) {
             int acc = 0;
             if (is_draft) {
-                const size_t off = ((size_t)b * G + r) * a.V + d;
-                const double ratio = exp(((double)a.zp[off] - (double)a.zq[off]) / Td - lsep + lseq);
+                const double ratio = exp(((double)zpd - (double)zqd) / Td - lsep + lseq);
                 const double u =
                     philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
                 acc = u < (ratio < 1.0 ? ratio : 1.0);
@@ -564,7 +570,13 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
                                      s_S[G - 1], u, lane);
     } else {
         final_known = false;  // correction drawn by the residual kernels
-        if (lane == 0) { a.seq_lse[2 * b] = s_lsep[j]; a.seq_lse[2 * b + 1] = s_lseq[j]; }
+        if (lane == 0) {
+            // 2^((z - R) c2) F = exp(z / T - LSE) with R = LSE T rounded to fp32, so that the
+            // exponent stays near zero; computed once here, loaded by the residual passes
+            const double lp = s_lsep[j], lq = s_lseq[j];
+            const float Rp = (float)(lp * Td), Rq = (float)(lq * Td);
+            a.seq_w[b] = f32x4{Rp, Rq, (float)exp((double)Rp / Td - lp), (float)exp((double)Rq / Td - lq)};
+        }
     }
     if (lane == 0) {
         a.accept_len[b] = j;
@@ -601,12 +613,11 @@ __device__ __forceinline__ ResidualW make_residual(const VerifyArgs& a, int b, i
     const size_t row = (size_t)b * a.G + j;
     w.zpr = a.zp + row * a.V;
     w.zqr = a.zq + row * a.V;
-    const double Td = (double)a.T;
-    const double lp = a.seq_lse[2 * b], lq = a.seq_lse[2 * b + 1];
-    w.Rp = (float)(lp * Td);
-    w.Rq = (float)(lq * Td);
-    w.Fp = (float)exp((double)w.Rp / Td - lp);
-    w.Fq = (float)exp((double)w.Rq / Td - lq);
+    const f32x4 c = a.seq_w[b];
+    w.Rp = c[0];
+    w.Rq = c[1];
+    w.Fp = c[2];
+    w.Fq = c[3];
     w.c2 = a.c2;
     return w;
 }
@@ -705,7 +716,7 @@ TopKLayout topk_layout(int batch, int gamma, int vocab, int k) {
 
 struct VerifyLayout {
     ScanPlan sp;
-    size_t p_m, p_s, q_m, q_s, cand_v, cand_i, seq_j, seq_lse, resid, bytes;
+    size_t p_m, p_s, q_m, q_s, cand_v, cand_i, seq_j, seq_w, resid, bytes;
 };
 
 VerifyLayout verify_layout(int batch, int gamma, int vocab) {
@@ -721,7 +732,7 @@ VerifyLayout verify_layout(int batch, int gamma, int vocab) {
     L.cand_v = c.take<float>((size_t)rows * L.sp.wpr);
     L.cand_i = c.take<int>((size_t)rows * L.sp.wpr);
     L.seq_j = c.take<int>((size_t)batch);
-    L.seq_lse = c.take<double>((size_t)batch * 2);
+    L.seq_w = c.take<f32x4>((size_t)batch);
     L.resid = c.take<double>((size_t)batch * L.sp.nseg);
     L.bytes = c.total();
     return L;
@@ -809,7 +820,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     v.cand_v = reinterpret_cast<float*>(ws + L.cand_v);
     v.cand_i = reinterpret_cast<int*>(ws + L.cand_i);
     v.seq_j = reinterpret_cast<int*>(ws + L.seq_j);
-    v.seq_lse = reinterpret_cast<double*>(ws + L.seq_lse);
+    v.seq_w = reinterpret_cast<f32x4*>(ws + L.seq_w);
     v.resid_s = reinterpret_cast<double*>(ws + L.resid);
     v.accept_len = accept_len; v.out_tokens = out_tokens; v.accepted = accepted;
     ScanArgs s{target_logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, 1, c2,
