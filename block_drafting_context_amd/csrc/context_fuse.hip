@@ -155,11 +155,14 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
                 const int rb = wn * (WN * 16) + t * 16 + i16;
                 fb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bt + rb * ROWB + ((c ^ (rb % 8)) * 16)));
             }
+            // the wave issuing MFMAs goes first on its SIMD (measured: 121 -> 117 us at 512 rows)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < WN; ++tj)
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ti], fb[tj], acc[ti][tj], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     // acc[i][j]: rows m0 + wm*64 + i*16 + 4*grp + e, column n0 + wn*80 + j*16 + i16

@@ -86,6 +86,8 @@ def _load():
                                     _I32, _I64, _U8, _D]),
         "orc_context_fuse": (c_int, [_D, _D, _D, c_dbl, _D, _I32, _I64] + [c_int] * 8 + [_D, _D]),
         "orc_position_weights": (c_int, [c_int, _D]),
+        "orc_select_path": (c_int, [_I64, _D, _D, _D, _D, _I64, c_int, c_int, c_int, c_i64, c_int,
+                                    _I64, _D]),
         "orc_num_threads": (c_int, []),
         "orc_set_num_threads": (None, [c_int]),
     }
@@ -205,10 +207,12 @@ def draft_rows(z, k, temperature, seeds=None, step=0):
 
 # ------------------------------------------------------------------------ verify
 def sampled_verify_seq_u(zp, zq, drafts, T, u_acc, u_draw):
-    """One sequence with explicit uniforms. zp, zq [G,V]; drafts [G-1];
-    u_acc [G-1]; u_draw [G] (u_draw[r] is used when the draw is from row r)."""
+    """One sequence with explicit uniforms. zp, zq [G,V] (zq None: deterministic
+    drafts, q = point mass); drafts [G-1]; u_acc [G-1]; u_draw [G] (u_draw[r] is
+    used when the draw is from row r)."""
     lib = _load()
-    zp, zq = _f64(zp), _f64(zq)
+    zp = _f64(zp)
+    zq = None if zq is None else _f64(zq)
     G, V = zp.shape
     d = _i64(drafts)
     ua = _f64(u_acc).reshape(-1)
@@ -245,6 +249,26 @@ def spec_verify(zp, zq, drafts, temperature, seeds=None, step=0):
     _check(rc, "spec_verify")
     return {"accept_len": j, "out_tokens": out, "accepted": acc[:, :G - 1],
             "ratio": ratio[:, :G - 1]}
+
+
+# -------------------------------------------------------------------- selector
+def select_path(cand, score, emb_a, emb_b, gate, anchor):
+    """Greedy walk of the candidate selector.  cand [B,G,k] ids; score [B,G,k] = U;
+    emb_a, emb_b [V,r]; gate [B,G,r]; anchor [B] -> dict(path [B,G], score [B,G])."""
+    lib = _load()
+    cand = _i64(cand)
+    B, G, k = cand.shape
+    score, emb_a, emb_b, gate = _f64(score), _f64(emb_a), _f64(emb_b), _f64(gate)
+    V, r = emb_a.shape
+    assert score.shape == (B, G, k) and emb_b.shape == (V, r) and gate.shape == (B, G, r)
+    anc = _i64(anchor).reshape(B)
+    path = np.zeros((B, G), dtype=np.int64)
+    ps = np.zeros((B, G), dtype=np.float64)
+    rc = lib.orc_select_path(_ptr(cand, _I64), _ptr(score, _D), _ptr(emb_a, _D), _ptr(emb_b, _D),
+                             _ptr(gate, _D), _ptr(anc, _I64), B, G, k, V, r, _ptr(path, _I64),
+                             _ptr(ps, _D))
+    _check(rc, "select_path")
+    return {"path": path, "score": ps}
 
 
 # ---------------------------------------------------------------------- fusion

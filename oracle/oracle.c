@@ -297,7 +297,11 @@ int orc_greedy_verify_seq(const double* zp, const int64_t* drafts, int G, int64_
  * ratio [G-1] (may be NULL) receives r = p(d)/q(d) at each draft, computed as
  * exp((zp[d] - zq[d])/T - LSE_p + LSE_q).  Reading: p and q are both at
  * temperature T; when the residual has no mass, the correction is drawn
- * from p. */
+ * from p.
+ * zq == NULL: the drafts are deterministic (chosen by the candidate selector,
+ * "The candidate selector"), so q is the point mass at each draft: the draft
+ * is accepted with probability p(d) and the residual [p - q]_+ is p with d
+ * removed. */
 int orc_sampled_verify_seq_u(const double* zp, const double* zq, const int64_t* drafts,
                              int G, int64_t V, double T,
                              const double* u_acc, const double* u_draw,
@@ -310,8 +314,13 @@ int orc_sampled_verify_seq_u(const double* zp, const double* zq, const int64_t* 
         const int64_t d = drafts[r];
         if (d < 0 || d >= V) return -2;
         const double Lp = orc_logsumexp(zp + (int64_t)r * V, V, T);
-        const double Lq = orc_logsumexp(zq + (int64_t)r * V, V, T);
-        const double rk = exp((zp[(int64_t)r * V + d] - zq[(int64_t)r * V + d]) / T - Lp + Lq);
+        double rk;
+        if (zq) {
+            const double Lq = orc_logsumexp(zq + (int64_t)r * V, V, T);
+            rk = exp((zp[(int64_t)r * V + d] - zq[(int64_t)r * V + d]) / T - Lp + Lq);
+        } else {
+            rk = exp(zp[(int64_t)r * V + d] / T - Lp);  /* p(d) / 1 */
+        }
         if (ratio) ratio[r] = rk;
         const double a = rk < 1.0 ? rk : 1.0;
         const int ok = u_acc[r] < a;
@@ -324,13 +333,20 @@ int orc_sampled_verify_seq_u(const double* zp, const double* zq, const int64_t* 
     const double Lp = orc_logsumexp(zpj, V, T);
     if (j < G - 1) {
         /* correction from the residual [p - q]_+ of the first rejected row */
-        const double* zqj = zq + (int64_t)j * V;
-        const double Lq = orc_logsumexp(zqj, V, T);
         double mass = 0.0;
-        for (int64_t v = 0; v < V; ++v) {
-            const double diff = exp(zpj[v] / T - Lp) - exp(zqj[v] / T - Lq);
-            w[v] = diff > 0.0 ? diff : 0.0;
-            mass += w[v];
+        if (zq) {
+            const double* zqj = zq + (int64_t)j * V;
+            const double Lq = orc_logsumexp(zqj, V, T);
+            for (int64_t v = 0; v < V; ++v) {
+                const double diff = exp(zpj[v] / T - Lp) - exp(zqj[v] / T - Lq);
+                w[v] = diff > 0.0 ? diff : 0.0;
+                mass += w[v];
+            }
+        } else {
+            for (int64_t v = 0; v < V; ++v) {
+                w[v] = v == drafts[j] ? 0.0 : exp(zpj[v] / T - Lp);
+                mass += w[v];
+            }
         }
         if (!(mass > 0.0))
             for (int64_t v = 0; v < V; ++v) w[v] = exp(zpj[v] / T - Lp);
@@ -349,7 +365,8 @@ int orc_sampled_verify_seq_u(const double* zp, const double* zq, const int64_t* 
 
 /* Batched verify.  T == 0: greedy (zq unused, may be NULL).  T > 0: sampled
  * with the uniforms of (seeds[b], step, b, row): purpose 1 for the accept
- * test of row r, purpose 2 for a correction or bonus drawn from row r.
+ * test of row r, purpose 2 for a correction or bonus drawn from row r;
+ * zq == NULL means deterministic drafts (point-mass q, see above).
  * zp, zq [B, G, V]; drafts [B, G-1]; accept_len [B]; out_tokens [B, G];
  * accepted [B, G-1] (may be NULL); ratio [B, G-1] (may be NULL, T > 0). */
 int orc_spec_verify(const double* zp, const double* zq, const int64_t* drafts,
@@ -357,7 +374,7 @@ int orc_spec_verify(const double* zp, const double* zq, const int64_t* drafts,
                     int32_t* accept_len, int64_t* out_tokens, uint8_t* accepted, double* ratio)
 {
     if (B < 0 || G < 1 || V < 1 || T < 0.0) return -2;
-    if (T > 0.0 && (!zq || !seeds)) return -2;
+    if (T > 0.0 && !seeds) return -2;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
@@ -373,13 +390,65 @@ int orc_spec_verify(const double* zp, const double* zq, const int64_t* drafts,
             if (!ua || !ud) { free(ua); free(ud); bad = 1; continue; }
             for (int r = 0; r < G - 1; ++r) ua[r] = orc_uniform(seeds[b], step, (uint64_t)b, (uint64_t)r, 1);
             for (int r = 0; r < G; ++r) ud[r] = orc_uniform(seeds[b], step, (uint64_t)b, (uint64_t)r, 2);
-            rc = orc_sampled_verify_seq_u(zpb, zq + (int64_t)b * G * V, db, G, V, T, ua, ud,
+            rc = orc_sampled_verify_seq_u(zpb, zq ? zq + (int64_t)b * G * V : NULL, db, G, V, T, ua, ud,
                                           accept_len + b, out_tokens + (int64_t)b * G, ab,
                                           ratio ? ratio + (int64_t)b * (G - 1) : NULL);
             free(ua);
             free(ud);
         }
         if (rc) bad = 1;
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Candidate selector.                                                         */
+/* [P3] "The candidate selector": each block position keeps the top-k draft   */
+/* candidates; a transition from candidate a at the preceding position to     */
+/* candidate b at position t scores                                           */
+/*     S_t(a, b) = U_t(b) + sum_i A(a)_i H(h_t)_i B(b)_i,                     */
+/* and one path is walked from the anchor.  Readings: U_t(b) is the drafter's */
+/* logit of b at position t (a per-position constant shift would not change   */
+/* the walk); A, B are token-embedding tables [V, r] and H(h_t) is given as   */
+/* its output gate vector g_t [r]; the walk is greedy ("a is the token        */
+/* selected at the preceding position"): position 0 follows the anchor, each  */
+/* later position follows the token just chosen; ties go to the candidate     */
+/* listed first.                                                              */
+/*                                                                            */
+/* cand [B, G, k] token ids   score [B, G, k] = U   emb_a, emb_b [V, r]       */
+/* gate [B, G, r]   anchor [B]   ->   path [B, G], path_score [B, G] (may be   */
+/* NULL) = S_t(prev, chosen).                                                 */
+/* ------------------------------------------------------------------------ */
+int orc_select_path(const int64_t* cand, const double* score, const double* emb_a,
+                    const double* emb_b, const double* gate, const int64_t* anchor,
+                    int B, int G, int k, int64_t V, int r, int64_t* path, double* path_score)
+{
+    if (B < 0 || G < 1 || k < 1 || V < 1 || r < 1) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < B; ++b) {
+        int64_t prev = anchor[b];
+        if (prev < 0 || prev >= V) { bad = 1; continue; }
+        for (int t = 0; t < G; ++t) {
+            const int64_t* ct = cand + ((int64_t)b * G + t) * k;
+            const double* ut = score + ((int64_t)b * G + t) * k;
+            const double* gt = gate + ((int64_t)b * G + t) * r;
+            const double* ea = emb_a + prev * r;
+            int best = -1;
+            double best_s = 0.0;
+            for (int j = 0; j < k; ++j) {
+                const int64_t c = ct[j];
+                if (c < 0 || c >= V) { bad = 1; break; }
+                const double* eb = emb_b + c * r;
+                double s = ut[j];
+                for (int i = 0; i < r; ++i) s += ea[i] * gt[i] * eb[i];
+                if (best < 0 || s > best_s) { best = j; best_s = s; }
+            }
+            if (best < 0) { bad = 1; break; }
+            path[(int64_t)b * G + t] = ct[best];
+            if (path_score) path_score[(int64_t)b * G + t] = best_s;
+            prev = ct[best];
+        }
     }
     return bad ? -2 : 0;
 }

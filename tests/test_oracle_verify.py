@@ -179,6 +179,96 @@ def test_enumeration_catches_planted_mistakes(mistake):
     assert err > 1e-4
 
 
+# ------------------------------------ sampled with deterministic drafts
+def _det_drafts(prefix, V, G):
+    """Deterministic drafts (what a selector would produce): a fixed function of the
+    context, unrelated to the target."""
+    h = zlib.crc32(repr(("sel",) + tuple(prefix)).encode())
+    return tuple((h >> (3 * i)) % V for i in range(G - 1))
+
+
+def _cycle_det(prefix, V, G, T, verify, keep_draft_in_residual=False):
+    """All outcomes of one cycle with deterministic drafts (q = point mass at each
+    draft), with exact probabilities built from the tables: accept with p(d),
+    correct from p without d."""
+    drafts = _det_drafts(prefix, V, G)
+    ps = [_p_target(tuple(prefix) + drafts[:r], V) for r in range(G)]
+    zp = T * np.log(np.array(ps))
+    a = [ps[r][drafts[r]] for r in range(G - 1)]
+    out = {}
+    for j in range(G):
+        pj = float(np.prod(a[:j])) * ((1.0 - a[j]) if j < G - 1 else 1.0)
+        if pj <= 0.0:
+            continue
+        u_acc = [a[r] / 2 if r < j else ((1.0 + a[r]) / 2 if r == j else 0.5) for r in range(G - 1)]
+        w = ps[j].copy()
+        if j < G - 1:
+            w[drafts[j]] = 0.0
+        c = np.cumsum(w)
+        for i in range(V):
+            if w[i] <= 0:
+                continue
+            u_draw = np.full(G, ((c[i] - w[i]) + c[i]) / 2 / c[-1])
+            res = verify(zp, None, np.array(drafts, dtype=np.int64), T, u_acc, u_draw)
+            tau = res["accept_len"] + 1
+            committed = tuple(int(t) for t in res["out_tokens"][:tau])
+            key = tuple(prefix) + committed
+            out[key] = out.get(key, 0.0) + pj * w[i] / c[-1]
+    return out
+
+
+def _committed_distribution_det(V, G, T, N, verify):
+    states = {(): 1.0}
+    done = {}
+    while states:
+        nxt = {}
+        for prefix, pr in states.items():
+            for key, p2 in _cycle_det(prefix, V, G, T, verify).items():
+                tgt = done if len(key) >= N else nxt
+                k2 = key[:N] if len(key) >= N else key
+                tgt[k2] = tgt.get(k2, 0.0) + pr * p2
+        states = nxt
+    return done
+
+
+@pytest.mark.parametrize("V,G,N,T", [(3, 3, 3, 0.7), (4, 4, 4, 1.0), (2, 5, 5, 1.3)])
+def test_deterministic_drafts_are_lossless_by_enumeration(V, G, N, T):
+    got = _committed_distribution_det(V, G, T, N, _oracle_verify)
+    ref = _target_distribution(V, N)
+    assert abs(sum(got.values()) - 1.0) < 1e-12
+    for seq, p in ref.items():
+        assert abs(got.get(seq, 0.0) - p) < 1e-12, (seq, got.get(seq, 0.0), p)
+
+
+def test_deterministic_enumeration_catches_a_residual_that_keeps_the_draft():
+    """A verifier that corrects from p itself (the rejected draft not removed) is
+    not lossless, and the enumeration sees it."""
+    def wrong(zp, zq, drafts, T, u_acc, u_draw):
+        res = oracle.sampled_verify_seq_u(zp, None, drafts, T, u_acc, u_draw)
+        j = res["accept_len"]
+        if j < zp.shape[0] - 1:
+            res["out_tokens"][j] = oracle.categorical(softmax(zp[j] / T), u_draw[j])
+        return res
+    got = _committed_distribution_det(3, 3, 0.7, 3, wrong)
+    ref = _target_distribution(3, 3)
+    assert max(abs(got.get(s, 0.0) - p) for s, p in ref.items()) > 1e-4
+
+
+def test_deterministic_draft_accepted_with_probability_p():
+    V = 4
+    p = np.array([0.1, 0.6, 0.2, 0.1])
+    zp = np.log(p)[None, None, :].repeat(2, 1)
+    n = 20000
+    res = [oracle.spec_verify(zp, None, np.array([[1]]), 1.0, seeds=np.array([9], np.uint64), step=s)
+           for s in range(n)]
+    acc = sum(r["accept_len"][0] for r in res)
+    sd = np.sqrt(n * 0.6 * 0.4)
+    assert abs(acc - n * 0.6) < 5 * sd
+    # a rejected draft is never the correction
+    assert all(r["out_tokens"][0, 0] != 1 for r in res if r["accept_len"][0] == 0)
+    assert np.allclose([r["ratio"][0, 0] for r in res[:3]], 0.6, rtol=1e-12)
+
+
 # ----------------------------------------------------- sampled: special cases
 def test_q_equal_p_accepts_everything():
     rng = np.random.default_rng(0)
