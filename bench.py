@@ -20,7 +20,8 @@ Prints one JSON line: drafted tokens/s (value), the roofline of the dominant
 kernel (block attention, HBM-bound) measured with HIP events on its stream
 inside the timed region, and the CPU oracle timed on a bounded sample.  Also
 reported: the same throughput with one attention layer instead of five, the
-512-row fusion call, a device-copy bandwidth (context for the 8 TB/s peak) and
+512-row fusion call, the candidate selector's walk and the verification of its
+deterministic drafts, a device-copy bandwidth (context for the 8 TB/s peak) and
 the oracle on a single host thread.
 """
 from __future__ import annotations
@@ -186,6 +187,62 @@ def fuse_512_rows(dev, warmup, steps):
             "mfma_frac_of_2500": round(flops / (us * 1e-6) / 2.5e15, 4)}
 
 
+def selector_figure(wl, dev, warmup, steps):
+    """NEXT row: the candidate selector's walk over top-16 candidates (r = 64 token
+    embeddings, synthetic) and verification of its deterministic drafts, at the
+    step's batch and block, timed with HIP events on the launching stream."""
+    k, r = 16, 64
+    tk = dfl.dflash_topk(wl["zd"], k, 0.0)
+    ea = syn.normal((V, r), SEED, "emb_a", std=1 / np.sqrt(r), dtype=torch.bfloat16, device=dev)
+    eb = syn.normal((V, r), SEED, "emb_b", std=1 / np.sqrt(r), dtype=torch.bfloat16, device=dev)
+    gate = syn.normal((B, G, r), SEED, "gate", std=1.0, dtype=torch.bfloat16, device=dev)
+    anchor = syn.uniform_int((B,), 0, V - 1, SEED, "anchor", device=dev).to(torch.int32)
+    out = {"path": torch.empty((B, G), dtype=torch.int32, device=dev),
+           "score": torch.empty((B, G), dtype=torch.float32, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def sel(st):
+        dfl.dflash_select_path(tk["idx"], tk["val"], ea, eb, gate, anchor, path=out["path"],
+                               path_score=out["score"], stream=st)
+
+    def ver(st):
+        dfl.spec_verify(wl["zt"], None, out["path"], T, seeds=wl["seeds"], step=0,
+                        outputs=wl["verify_out"], workspace=wl["ws_verify"], stream=st)
+
+    res = {"k": k, "r": r}
+    for name, fn in (("select_path_us", sel), ("verify_deterministic_us", ver)):
+        for _ in range(max(1, warmup)):
+            fn(stream)
+        torch.cuda.synchronize()
+        # the calls are captured in a HIP graph so that the figure is GPU time, not the
+        # host's launch rate (eager timing is kept if capture is unavailable)
+        timing = "graph"
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(steps):
+                    fn(None)
+            graph.replay()
+            torch.cuda.synchronize()
+            run = graph.replay
+        except Exception:  # noqa: BLE001
+            timing = "eager"
+            run = lambda: [fn(stream) for _ in range(steps)]  # noqa: E731
+        run()
+        torch.cuda.synchronize()
+        s0 = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s0)
+        run()
+        e1.record(s0)
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+        res[name.replace("_us", "_timing")] = timing
+    del ea, eb
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_probe():
     """Three copies of 2^28 fp32 (1 GiB read + 1 GiB written each): the
     calibration kernel for the HBM byte counters."""
@@ -319,6 +376,7 @@ def main():
     acc = wl["verify_out"]["accept_len"].float().mean().item() + 1.0
 
     fuse512 = fuse_512_rows(dev, args.warmup, args.steps)
+    selector = selector_figure(wl, dev, args.warmup, args.steps)
     copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
@@ -366,6 +424,7 @@ def main():
         "device_copy_gbs": copy_gbs,
         "mean_tau": round(acc, 3),
         "context_fuse_512_rows": fuse512,
+        "candidate_selector": selector,
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
     }

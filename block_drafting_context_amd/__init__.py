@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "dflash_topk_workspace_size", "dflash_topk",
     "spec_verify_workspace_size", "spec_verify",
     "dflash_context_fuse_workspace_size", "dflash_context_fuse",
+    "dflash_select_path",
 )
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
@@ -69,6 +70,7 @@ def load():
         "dflash_context_fuse_workspace_size": (_sz, [_i] * 7),
         "dflash_context_fuse": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp] + [_i] * 9 +
                                 [_vp, _sz, _vp]),
+        "dflash_select_path": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -202,9 +204,10 @@ def spec_verify_workspace_size(batch, gamma, vocab):
 
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=None, step=0,
                 draft_lse=None, outputs=None, workspace=None, stream=None):
-    """target_logits, draft_logits [B,G,V] fp32; draft_tokens [B,G] int32 (first G-1 used);
-    draft_lse [B,G] fp64 or None.  Returns dict(accept_len [B] int32, out_tokens [B,G] int32,
-    accepted [B,G-1] uint8)."""
+    """target_logits, draft_logits [B,G,V] fp32 (draft_logits None with temperature > 0:
+    deterministic drafts, e.g. from dflash_select_path); draft_tokens [B,G] int32 (first G-1
+    used); draft_lse [B,G] fp64 or None.  Returns dict(accept_len [B] int32, out_tokens [B,G]
+    int32, accepted [B,G-1] uint8)."""
     B, G, V = target_logits.shape
     dev = target_logits.device
     _need(target_logits, "target_logits", torch.float32, (B, G, V), dev)
@@ -224,6 +227,30 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=No
           _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
           _ptr(out_tok), _ptr(accepted), B, G, V, _ptr(ws), wsb, _stream(stream))
     return {"accept_len": acc_len, "out_tokens": out_tok, "accepted": accepted[:, :G - 1]}
+
+
+# ------------------------------------------------------------------- selector
+def dflash_select_path(cand_idx, cand_score, emb_a, emb_b, gate, anchor, path=None,
+                       path_score=None, stream=None):
+    """cand_idx [B,G,k] int32; cand_score [B,G,k] fp32; emb_a, emb_b [V,r] bf16; gate [B,G,r]
+    bf16; anchor [B] int32.  Returns dict(path [B,G] int32, score [B,G] fp32)."""
+    B, G, k = cand_idx.shape
+    V, r = emb_a.shape
+    dev = cand_idx.device
+    _need(cand_idx, "cand_idx", torch.int32, (B, G, k), dev)
+    _need(cand_score, "cand_score", torch.float32, (B, G, k), dev)
+    _need(emb_a, "emb_a", torch.bfloat16, (V, r), dev)
+    _need(emb_b, "emb_b", torch.bfloat16, (V, r), dev)
+    _need(gate, "gate", torch.bfloat16, (B, G, r), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    path = path if path is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
+    score = path_score if path_score is not None else torch.empty((B, G), dtype=torch.float32,
+                                                                  device=dev)
+    _need(path, "path", torch.int32, (B, G), dev)
+    _need(score, "path_score", torch.float32, (B, G), dev)
+    _call("dflash_select_path", _ptr(cand_idx), _ptr(cand_score), _ptr(emb_a), _ptr(emb_b),
+          _ptr(gate), _ptr(anchor), _ptr(path), _ptr(score), B, G, k, V, r, _stream(stream))
+    return {"path": path, "score": score}
 
 
 # --------------------------------------------------------------------- fusion

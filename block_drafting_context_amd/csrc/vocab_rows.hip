@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
         if (is_draft && lane == 0) {
             const size_t off = ((size_t)b * G + r) * a.V + d;
             zpd = a.zp[off];
-            zqd = a.zq[off];
+            if (a.zq) zqd = a.zq[off];
         }
         const size_t rb = ((size_t)b * G + r) * a.nseg;
         float M;
@@ -524,7 +524,7 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
         merge_row_stats(a.p_seg_m + rb, a.p_seg_s + rb, a.nseg, a.c2, lane, M, S);
         const double lsep = (double)M / Td + log(S);
         double lseq = 0.0;
-        if (is_draft) {
+        if (is_draft && a.zq) {
             if (a.draft_lse) {
                 lseq = a.draft_lse[(size_t)b * G + r];
             } else {
@@ -537,7 +537,9 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
         if (lane == 0) {
             int acc = 0;
             if (is_draft) {
-                const double ratio = exp(((double)zpd - (double)zqd) / Td - lsep + lseq);
+                // deterministic drafts (no draft logits): q is the point mass at d
+                const double ratio = a.zq ? exp(((double)zpd - (double)zqd) / Td - lsep + lseq)
+                                          : exp((double)zpd / Td - lsep);
                 const double u =
                     philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
                 acc = u < (ratio < 1.0 ? ratio : 1.0);
@@ -592,17 +594,26 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
 // Element weight of the residual [p - q]_+ at row j, from the row log-normalisers.
 struct ResidualW {
     const float* zpr;
-    const float* zqr;
+    const float* zqr;  // null: deterministic draft, q = point mass at dq
+    int dq;
     float Rp, Rq, Fp, Fq, c2;
     __device__ __forceinline__ f32x4 w4(int v) const {
         const f32x4 zp = *reinterpret_cast<const f32x4*>(zpr + v);
-        const f32x4 zq = *reinterpret_cast<const f32x4*>(zqr + v);
         f32x4 r;
+        if (zqr) {
+            const f32x4 zq = *reinterpret_cast<const f32x4*>(zqr + v);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
-            const float q = fast_exp2((zq[c] - Rq) * c2) * Fq;
-            r[c] = fmaxf(p - q, 0.f);
+            for (int c = 0; c < 4; ++c) {
+                const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
+                const float q = fast_exp2((zq[c] - Rq) * c2) * Fq;
+                r[c] = fmaxf(p - q, 0.f);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
+                r[c] = v + c == dq ? 0.f : p;  // p - 1 < 0 at the draft, p - 0 elsewhere
+            }
         }
         return r;
     }
@@ -612,7 +623,8 @@ __device__ __forceinline__ ResidualW make_residual(const VerifyArgs& a, int b, i
     ResidualW w;
     const size_t row = (size_t)b * a.G + j;
     w.zpr = a.zp + row * a.V;
-    w.zqr = a.zq + row * a.V;
+    w.zqr = a.zq ? a.zq + row * a.V : nullptr;
+    w.dq = a.zq ? -1 : clamp_tok(a.drafts[row], a.V);
     const f32x4 c = a.seq_w[b];
     w.Rp = c[0];
     w.Rq = c[1];
@@ -802,7 +814,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
     if (batch == 0) return DFLASH_OK;
     if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_ERR_NULL;
-    if (temperature > 0.f && (!draft_logits || !seeds)) return DFLASH_ERR_NULL;
+    if (temperature > 0.f && !seeds) return DFLASH_ERR_NULL;
     if (gamma > 32 || vocab % 4 != 0) return DFLASH_ERR_UNSUPPORTED;
     const VerifyLayout L = verify_layout(batch, gamma, vocab);
     if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
@@ -830,7 +842,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
         launch_scan<kArgmax>(s, st);
     } else {
         launch_scan<kSumExp>(s, st);
-        if (!draft_lse) {
+        if (!draft_lse && draft_logits) {
             ScanArgs q = s;
             q.z = draft_logits;
             q.seg_m = const_cast<float*>(v.q_seg_m);

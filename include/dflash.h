@@ -10,6 +10,8 @@
  *   dflash_topk          per-position top-k candidates, log-normaliser and
  *                        drafted token of the drafter's logits;
  *   spec_verify          lossless verification of one drafted block.
+ *   dflash_select_path   the candidate selector's walk through the top-k
+ *                        candidates of each block position.
  *
  * Sources (web pages, cited by title and section):
  *   "DFlash vs DFlash 2" (blog): "The problem: one expensive token at a time",
@@ -158,12 +160,17 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
  *   target_logits [batch, gamma, vocab] float32; row r is the target's
  *            distribution for the token after anchor + drafts 0..r-1;
  *            rows 0..gamma-2 verify, row gamma-1 gives the bonus.
- *   draft_logits  [batch, gamma, vocab] float32 (rows 0..gamma-2 are read;
- *            may be NULL when T == 0).
+ *   draft_logits  [batch, gamma, vocab] float32 (rows 0..gamma-2 are read),
+ *            or NULL.  NULL with T > 0 means deterministic drafts (chosen by
+ *            dflash_select_path, "The candidate selector"): q_r is the point
+ *            mass at the draft, so a draft survives with probability p_r(y)
+ *            and the correction is drawn from p_j with the rejected draft
+ *            removed (still lossless).  Unused when T == 0.
  *   draft_tokens  [batch, gamma] int32 (as written by dflash_topk); entries
  *            0..gamma-2 are the drafts, in [0, vocab) (precondition).
  *   draft_lse     [batch, gamma] float64 from dflash_topk at the same T;
- *            may be NULL (then recomputed from draft_logits).
+ *            may be NULL (then recomputed from draft_logits; unused with
+ *            deterministic drafts).
  *   seeds         [batch] uint64 (device); may be NULL when T == 0.
  *   accept_len    [batch] int32: j = accepted drafts (0..gamma-1);
  *                 tau = j + 1 tokens are committed.
@@ -216,6 +223,39 @@ int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, const float* 
                         int rows, int n_taps, int d_tgt, int d_model, int n_layers,
                         int n_kv, int d_head, int window, int batch,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_select_path -- the candidate selector.
+ *
+ * "DFlash vs DFlash 2", "The candidate selector": each block position keeps
+ * the top-k draft candidates and the transition from candidate a at the
+ * preceding position to candidate b at position t scores
+ *     S_t(a, b) = U_t(b) + sum_i A(a)_i * g_t,i * B(b)_i,
+ * with U_t(b) the drafter's logit of b, A and B compact token embeddings and
+ * g_t = H(h_t) the gate computed from the position's hidden state.  All
+ * transition scores are computed in parallel; the walk is greedy: position 0
+ * follows the anchor, each later position follows the token just chosen, and
+ * equal scores go to the candidate listed first.  The resulting path is a set
+ * of deterministic drafts for spec_verify with draft_logits == NULL.
+ *
+ *   cand_idx   [batch, gamma, k] int32 token ids (as dflash_topk writes)
+ *   cand_score [batch, gamma, k] float32 U_t(b) (dflash_topk's values)
+ *   emb_a, emb_b [vocab, r] bf16 (16-byte aligned)
+ *   gate       [batch, gamma, r] bf16 (16-byte aligned)
+ *   anchor     [batch] int32, the last verified token of each sequence
+ *   path       [batch, gamma] int32 out: the chosen token of each position
+ *   path_score [batch, gamma] float32 out or NULL: S_t(previous, chosen)
+ * Token ids outside [0, vocab) are clamped (precondition: they are in range).
+ * Supported: k <= 64, r % 8 == 0, r <= 4096.
+ * Accuracy: every term is a product of three bf16 values (exact in fp64) and
+ * the sum over i runs in increasing i in fp64, so the walk's choices are those
+ * of the exact scores up to fp64 rounding of that sum.
+ * All pointers are device memory owned by the caller; no workspace.
+ * ------------------------------------------------------------------------ */
+int dflash_select_path(const int32_t* cand_idx, const float* cand_score, const uint16_t* emb_a,
+                       const uint16_t* emb_b, const uint16_t* gate, const int32_t* anchor,
+                       int32_t* path, float* path_score, int batch, int gamma, int k, int vocab,
+                       int r, void* stream);
 
 #ifdef __cplusplus
 }

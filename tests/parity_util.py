@@ -25,12 +25,16 @@ def assert_close_scaled(got, ref, rel, abs_, what=""):
     return err, bound
 
 
-def draw_boundary_ok(z_row, T, u, got, ref, residual_q=None):
+def draw_boundary_ok(z_row, T, u, got, ref, residual_q=None, residual_exclude=None):
     """A categorical draw may differ from the oracle only when u * S lies within
-    1e-6 * S of a CDF boundary between the two indices (weights in fp64 by scipy)."""
+    1e-6 * S of a CDF boundary between the two indices (weights in fp64 by scipy).
+    residual_exclude: token removed from p (the residual of a deterministic draft)."""
     if got == ref:
         return True
-    if residual_q is None:
+    if residual_exclude is not None:
+        w = softmax(np.asarray(z_row, dtype=np.float64) / T)
+        w[int(residual_exclude)] = 0.0
+    elif residual_q is None:
         w = softmax(np.asarray(z_row, dtype=np.float64) / T)
     else:
         p = softmax(np.asarray(z_row, dtype=np.float64) / T)

@@ -105,7 +105,7 @@ def verify(**kw):
 
 def test_verify_validation():
     assert verify(zp=None) == -1
-    assert verify(zq=None) == -1
+    assert verify(zq=None) == -4  # no draft logits at T > 0: deterministic drafts; then workspace
     assert verify(seeds=None) == -1
     assert verify(j=None) == -1
     assert verify(G=0) == -2
@@ -114,6 +114,28 @@ def test_verify_validation():
     assert verify(V=1001) == -3
     assert verify() == -4
     assert verify(zq=None, seeds=None, T=0.0) == -4
+
+
+def select(**kw):
+    a = dict(c=P, u=P, ea=P, eb=P, g=P, anc=P, path=P, ps=None, B=32, G=8, k=16, V=151936, r=64,
+             st=None)
+    a.update(kw)
+    return dfl.load().dflash_select_path(a["c"], a["u"], a["ea"], a["eb"], a["g"], a["anc"],
+                                         a["path"], a["ps"], a["B"], a["G"], a["k"], a["V"], a["r"],
+                                         a["st"])
+
+
+def test_select_path_validation():
+    assert select(B=0) == 0
+    assert select(c=None) == -1
+    assert select(anc=None) == -1
+    assert select(path=None) == -1
+    assert select(G=0) == -2
+    assert select(k=0) == -2
+    assert select(r=0) == -2
+    assert select(k=65) == -3
+    assert select(r=60) == -3
+    assert select(ea=ctypes.c_void_p(0x1008)) == -3  # rows must be 16-byte aligned
 
 
 def fuse(**kw):
