@@ -88,6 +88,7 @@ def _load():
         "orc_position_weights": (c_int, [c_int, _D]),
         "orc_select_path": (c_int, [_I64, _D, _D, _D, _D, _I64, c_int, c_int, c_int, c_i64, c_int,
                                     _I64, _D]),
+        "orc_two_tap_conv": (c_int, [_D, _D, c_int, c_int, c_int, c_int, _D]),
         "orc_num_threads": (c_int, []),
         "orc_set_num_threads": (None, [c_int]),
     }
@@ -269,6 +270,20 @@ def select_path(cand, score, emb_a, emb_b, gate, anchor):
                              _ptr(ps, _D))
     _check(rc, "select_path")
     return {"path": path, "score": ps}
+
+
+# ------------------------------------------------------------- two-tap conv
+def two_tap_conv(x, kern):
+    """x [B,G,D]; kern [B,G,2,n_groups] -> y [B,G,D]."""
+    lib = _load()
+    x, kern = _f64(x), _f64(kern)
+    B, G, D = x.shape
+    n_groups = kern.shape[3]
+    assert kern.shape == (B, G, 2, n_groups)
+    y = np.zeros_like(x)
+    rc = lib.orc_two_tap_conv(_ptr(x, _D), _ptr(kern, _D), B, G, D, n_groups, _ptr(y, _D))
+    _check(rc, "two_tap_conv")
+    return y
 
 
 # ---------------------------------------------------------------------- fusion

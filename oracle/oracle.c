@@ -454,6 +454,37 @@ int orc_select_path(const int64_t* cand, const double* score, const double* emb_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Two-tap dynamic convolution.                                               */
+/* [P3] "The two-tap dynamic convolution": Conv_k(x)_t = k_{t,0} * x_t +      */
+/* k_{t,1} * x_{t-1}, depthwise, with a content-dependent kernel shared by a  */
+/* group of channels; it never crosses a block boundary and position 1 reads  */
+/* from the verified anchor.  Readings: block row 0 is the anchor's position, */
+/* so row t >= 1 reads row t - 1 and row 0 has no predecessor (zero); channel */
+/* c uses group c / (D / n_groups); the kernel values are an input (the small */
+/* network producing them from the content is outside the path).             */
+/*                                                                            */
+/* x [B, G, D]   kern [B, G, 2, n_groups]   ->   y [B, G, D]                   */
+/* ------------------------------------------------------------------------ */
+int orc_two_tap_conv(const double* x, const double* kern, int B, int G, int D, int n_groups,
+                     double* y)
+{
+    if (B < 0 || G < 1 || D < 1 || n_groups < 1 || D % n_groups) return -2;
+    const int gs = D / n_groups;
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < G; ++t) {
+            const double* xt = x + ((int64_t)b * G + t) * D;
+            const double* kt = kern + ((int64_t)b * G + t) * 2 * n_groups;
+            double* yt = y + ((int64_t)b * G + t) * D;
+            for (int c = 0; c < D; ++c) {
+                const int grp = c / gs;
+                const double prev = t > 0 ? xt[c - D] : 0.0;
+                yt[c] = kt[grp] * xt[c] + kt[n_groups + grp] * prev;
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Context fusion and context K/V injection.                                  */
 /* [P3] "Conditioning on the target model", equation for H_t: hidden states  */
 /* of five target layers are concatenated, projected by W_c and RMS-         */
