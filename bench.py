@@ -21,7 +21,7 @@ kernel (block attention, HBM-bound) measured with HIP events on its stream
 inside the timed region, and the CPU oracle timed on a bounded sample.  Also
 reported: the same throughput with one attention layer instead of five, the
 512-row fusion call, the candidate selector's walk and the verification of its
-deterministic drafts, a device-copy bandwidth (context for the 8 TB/s peak) and
+deterministic drafts, one two-tap dynamic convolution, a device-copy bandwidth (context for the 8 TB/s peak) and
 the oracle on a single host thread.
 """
 from __future__ import annotations
@@ -243,6 +243,35 @@ def selector_figure(wl, dev, warmup, steps):
     return res
 
 
+def conv_figure(dev, warmup, steps):
+    """NEXT row: one two-tap dynamic convolution over the step's block
+    representations (32 x 8 x 5120 bf16, 80 channel groups), graph-timed; the
+    drafter applies it before and after each attention and MLP sublayer."""
+    D, ng = 5120, 80
+    x = syn.normal((B, G, D), SEED, "conv_x", dtype=torch.bfloat16, device=dev)
+    k = syn.normal((B, G, 2, ng), SEED, "conv_k", device=dev)
+    y = torch.empty_like(x)
+    dfl.dflash_two_tap_conv(x, k, y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            dfl.dflash_two_tap_conv(x, k, y)
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s0)
+    graph.replay()
+    e1.record(s0)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    nbytes = 2 * x.numel() * 2 + k.numel() * 4
+    return {"d": D, "groups": ng, "us_per_call": round(us, 2),
+            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def copy_probe():
     """Three copies of 2^28 fp32 (1 GiB read + 1 GiB written each): the
     calibration kernel for the HBM byte counters."""
@@ -377,6 +406,7 @@ def main():
 
     fuse512 = fuse_512_rows(dev, args.warmup, args.steps)
     selector = selector_figure(wl, dev, args.warmup, args.steps)
+    conv = conv_figure(dev, args.warmup, args.steps)
     copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
@@ -425,6 +455,7 @@ def main():
         "mean_tau": round(acc, 3),
         "context_fuse_512_rows": fuse512,
         "candidate_selector": selector,
+        "two_tap_conv": conv,
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
     }

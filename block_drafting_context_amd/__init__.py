@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "dflash_topk_workspace_size", "dflash_topk",
     "spec_verify_workspace_size", "spec_verify",
     "dflash_context_fuse_workspace_size", "dflash_context_fuse",
-    "dflash_select_path",
+    "dflash_select_path", "dflash_two_tap_conv",
 )
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
@@ -71,6 +71,7 @@ def load():
         "dflash_context_fuse": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp] + [_i] * 9 +
                                 [_vp, _sz, _vp]),
         "dflash_select_path": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
+        "dflash_two_tap_conv": (_i, [_vp] * 3 + [_i] * 4 + [_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -251,6 +252,20 @@ def dflash_select_path(cand_idx, cand_score, emb_a, emb_b, gate, anchor, path=No
     _call("dflash_select_path", _ptr(cand_idx), _ptr(cand_score), _ptr(emb_a), _ptr(emb_b),
           _ptr(gate), _ptr(anchor), _ptr(path), _ptr(score), B, G, k, V, r, _stream(stream))
     return {"path": path, "score": score}
+
+
+# ------------------------------------------------------------- two-tap conv
+def dflash_two_tap_conv(x, kern, y=None, stream=None):
+    """x [B,G,D] bf16; kern [B,G,2,n_groups] fp32 -> y [B,G,D] bf16 (y must not be x)."""
+    B, G, D = x.shape
+    n_groups = kern.shape[3]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (B, G, D), dev)
+    _need(kern, "kern", torch.float32, (B, G, 2, n_groups), dev)
+    y = y if y is not None else torch.empty_like(x)
+    _need(y, "y", torch.bfloat16, (B, G, D), dev)
+    _call("dflash_two_tap_conv", _ptr(x), _ptr(kern), _ptr(y), B, G, D, n_groups, _stream(stream))
+    return y
 
 
 # --------------------------------------------------------------------- fusion

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["block_attn.hip", "vocab_rows.hip", "context_fuse.hip", "select_path.hip", "status.cpp"]
+SOURCES = ["block_attn.hip", "vocab_rows.hip", "context_fuse.hip", "select_path.hip", "two_tap_conv.hip",
+           "status.cpp"]
 
 # Device code generation: no packed-fp32 instructions anywhere (the host pass
 # of hipcc prints a harmless "not a recognized feature" warning for this flag),

@@ -12,6 +12,7 @@
  *   spec_verify          lossless verification of one drafted block.
  *   dflash_select_path   the candidate selector's walk through the top-k
  *                        candidates of each block position.
+ *   dflash_two_tap_conv  the two-tap dynamic convolution inside a block.
  *
  * Sources (web pages, cited by title and section):
  *   "DFlash vs DFlash 2" (blog): "The problem: one expensive token at a time",
@@ -256,6 +257,29 @@ int dflash_select_path(const int32_t* cand_idx, const float* cand_score, const u
                        const uint16_t* emb_b, const uint16_t* gate, const int32_t* anchor,
                        int32_t* path, float* path_score, int batch, int gamma, int k, int vocab,
                        int r, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_two_tap_conv -- the two-tap dynamic convolution.
+ *
+ * "DFlash vs DFlash 2", "The two-tap dynamic convolution": each block
+ * position mixes its representation with its immediate predecessor,
+ *     y[b,t,c] = kern[b,t,0,g(c)] * x[b,t,c] + kern[b,t,1,g(c)] * x[b,t-1,c],
+ * depthwise, with content-dependent kernel values shared by the channels of a
+ * group (g(c) = c / (d / n_groups)), never across a block boundary.  Row 0 of
+ * a block is the anchor's position: row t >= 1 reads row t - 1 (the first
+ * drafted position reads the anchor), row 0 has no predecessor (zero).
+ *
+ *   x     [batch, gamma, d] bf16 (16-byte aligned)
+ *   kern  [batch, gamma, 2, n_groups] float32 (computed from the content by
+ *         the caller's projection)
+ *   y     [batch, gamma, d] bf16 out (16-byte aligned; must not overlap x)
+ * Supported: d % n_groups == 0, (d / n_groups) % 8 == 0.
+ * Accuracy: fp32 arithmetic (one fused multiply-add per channel), output
+ * rounded to bf16, nearest even.
+ * All pointers are device memory owned by the caller; no workspace.
+ * ------------------------------------------------------------------------ */
+int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int batch, int gamma,
+                        int d, int n_groups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -138,6 +138,24 @@ def test_select_path_validation():
     assert select(ea=ctypes.c_void_p(0x1008)) == -3  # rows must be 16-byte aligned
 
 
+def conv(**kw):
+    a = dict(x=P, k=P, y=ctypes.c_void_p(0x2000), B=32, G=8, d=5120, ng=80, st=None)
+    a.update(kw)
+    return dfl.load().dflash_two_tap_conv(a["x"], a["k"], a["y"], a["B"], a["G"], a["d"], a["ng"],
+                                          a["st"])
+
+
+def test_two_tap_conv_validation():
+    assert conv(B=0) == 0
+    assert conv(x=None) == -1
+    assert conv(k=None) == -1
+    assert conv(G=0) == -2
+    assert conv(ng=3) == -2          # groups must divide the width
+    assert conv(y=P) == -2           # in place is not allowed
+    assert conv(ng=1024) == -3       # groups of 5 channels: not a multiple of 8
+    assert conv(x=ctypes.c_void_p(0x1008)) == -3
+
+
 def fuse(**kw):
     a = dict(x=P, wc=P, g=P, eps=1e-6, wkv=P, rs=P, rp=P, ring=P, h=None, rows=512, taps=5,
              dt=5120, dm=5120, nl=5, nkv=8, dh=128, W=4096, B=64, ws=None, wsb=0, st=None)
