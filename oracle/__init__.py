@@ -26,6 +26,10 @@ What each function follows (pages cited by title and section):
   model" (H_t equation and the context half of K_i, V_i).
 * ``position_weights`` -- "DFlash vs DFlash 2", "Training with anchors"
   (w_k equation).
+* ``lm_head_topk`` -- "Beam 1.0 DFlash2" model card, "Model" (the drafter
+  reuses the target's LM head) and "DFlash vs DFlash 2", "The candidate
+  selector" (top-k per position); the draft draw is exact softmax sampling
+  done in two inverse-CDF steps over 128-entry vocabulary segments.
 * ``philox4x64_10`` / ``uniform`` -- Salmon et al., SC'11.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against values
@@ -50,6 +54,7 @@ _I64 = ctypes.POINTER(ctypes.c_int64)
 _I32 = ctypes.POINTER(ctypes.c_int32)
 _U64 = ctypes.POINTER(ctypes.c_uint64)
 _U8 = ctypes.POINTER(ctypes.c_uint8)
+_U16 = ctypes.POINTER(ctypes.c_uint16)
 
 
 def build() -> str:
@@ -89,6 +94,8 @@ def _load():
         "orc_select_path": (c_int, [_I64, _D, _D, _D, _D, _I64, c_int, c_int, c_int, c_i64, c_int,
                                     _I64, _D]),
         "orc_two_tap_conv": (c_int, [_D, _D, c_int, c_int, c_int, c_int, _D]),
+        "orc_lm_head_topk": (c_int, [_U16, _U16, _I64, c_int, c_int, c_i64, c_int, c_int, c_dbl,
+                                     _U64, c_u64, _I64, _D, _D, _I64, _D]),
         "orc_num_threads": (c_int, []),
         "orc_set_num_threads": (None, [c_int]),
     }
@@ -204,6 +211,33 @@ def draft_rows(z, k, temperature, seeds=None, step=0):
                             _ptr(draft, _I64))
     _check(rc, "draft_rows")
     return {"idx": idx, "val": val, "lse": lse, "draft": draft}
+
+
+def lm_head_topk(h_bits, w_bits, gamma, k, temperature, seeds=None, step=0, row_id=None,
+                 want_draft=True, want_z=False):
+    """Drafter LM head.  h_bits [n, d] and w_bits [V, d] are bf16 bit patterns
+    (uint16); row_id [n] global row indices (default 0..n-1), row r belongs to
+    sequence r // gamma, block row r % gamma.  Returns dict(idx [n,k], val [n,k],
+    lse [n], draft [n] or None, z [n,V] or None)."""
+    lib = _load()
+    h = np.ascontiguousarray(np.asarray(h_bits, dtype=np.uint16))
+    w = np.ascontiguousarray(np.asarray(w_bits, dtype=np.uint16))
+    n, d = h.shape
+    V = w.shape[0]
+    assert w.shape == (V, d)
+    rid = None if row_id is None else _i64(row_id).reshape(n)
+    sd = None if seeds is None else np.ascontiguousarray(np.asarray(seeds, dtype=np.uint64))
+    idx = np.zeros((n, k), dtype=np.int64)
+    val = np.zeros((n, k), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    draft = np.zeros(n, dtype=np.int64) if want_draft else None
+    z = np.zeros((n, V), dtype=np.float64) if want_z else None
+    rc = lib.orc_lm_head_topk(_ptr(h, _U16), _ptr(w, _U16), _ptr(rid, _I64), n, int(gamma), V, d,
+                              int(k), float(temperature), _ptr(sd, _U64), int(step),
+                              _ptr(idx, _I64), _ptr(val, _D), _ptr(lse, _D), _ptr(draft, _I64),
+                              _ptr(z, _D))
+    _check(rc, "lm_head_topk")
+    return {"idx": idx, "val": val, "lse": lse, "draft": draft, "z": z}
 
 
 # ------------------------------------------------------------------------ verify
