@@ -20,6 +20,8 @@ __all__ = [
     "dflash_topk", "dflash_topk_workspace_size",
     "spec_verify", "spec_verify_workspace_size",
     "dflash_context_fuse", "dflash_context_fuse_workspace_size",
+    "dflash_select_path", "dflash_two_tap_conv",
+    "dflash_lm_head_topk", "dflash_lm_head_topk_workspace_size",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -34,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "spec_verify_workspace_size", "spec_verify",
     "dflash_context_fuse_workspace_size", "dflash_context_fuse",
     "dflash_select_path", "dflash_two_tap_conv",
+    "dflash_lm_head_topk_workspace_size", "dflash_lm_head_topk",
 )
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
@@ -72,6 +75,9 @@ def load():
                                 [_vp, _sz, _vp]),
         "dflash_select_path": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
         "dflash_two_tap_conv": (_i, [_vp] * 3 + [_i] * 4 + [_vp]),
+        "dflash_lm_head_topk_workspace_size": (_sz, [_i] * 4),
+        "dflash_lm_head_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp,
+                                     _vp, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -266,6 +272,45 @@ def dflash_two_tap_conv(x, kern, y=None, stream=None):
     _need(y, "y", torch.bfloat16, (B, G, D), dev)
     _call("dflash_two_tap_conv", _ptr(x), _ptr(kern), _ptr(y), B, G, D, n_groups, _stream(stream))
     return y
+
+
+# -------------------------------------------------------------------- LM head
+def dflash_lm_head_topk_workspace_size(rows, d_model, vocab, k):
+    return int(load().dflash_lm_head_topk_workspace_size(rows, d_model, vocab, k))
+
+
+def dflash_lm_head_topk(hidden, w_head, gamma, k, temperature, seeds=None, step=0,
+                        want_lse=True, want_draft=True, outputs=None, workspace=None,
+                        stream=None):
+    """Drafter LM head with fused top-k: hidden [rows, d] bf16; w_head [V, d] bf16 ->
+    dict(idx [rows,k] int32, val [rows,k] fp32, lse [rows] fp64 or None, draft [rows]
+    int32 or None).  Row r belongs to sequence r // gamma; seeds [ceil(rows/gamma)]
+    int64 (bits read as uint64)."""
+    rows, d = hidden.shape
+    V = w_head.shape[0]
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16, (rows, d), dev)
+    _need(w_head, "w_head", torch.bfloat16, (V, d), dev)
+    if seeds is not None:
+        _need(seeds, "seeds", torch.int64, ((rows + gamma - 1) // gamma,), dev)
+    o = outputs or {}
+    idx = o.get("idx") if o.get("idx") is not None else torch.empty((rows, k), dtype=torch.int32, device=dev)
+    val = o.get("val") if o.get("val") is not None else torch.empty((rows, k), dtype=torch.float32, device=dev)
+    lse = o.get("lse") if o.get("lse") is not None else (
+        torch.empty(rows, dtype=torch.float64, device=dev) if want_lse else None)
+    draft = o.get("draft") if o.get("draft") is not None else (
+        torch.empty(rows, dtype=torch.int32, device=dev) if want_draft else None)
+    _need(idx, "idx", torch.int32, (rows, k), dev)
+    _need(val, "val", torch.float32, (rows, k), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float64, (rows,), dev)
+    if draft is not None:
+        _need(draft, "draft", torch.int32, (rows,), dev)
+    ws, wsb = _workspace(dflash_lm_head_topk_workspace_size(rows, d, V, k), dev, workspace)
+    _call("dflash_lm_head_topk", _ptr(hidden), _ptr(w_head), rows, int(gamma), d, V, int(k),
+          float(temperature), _ptr(seeds), int(step), _ptr(idx), _ptr(val), _ptr(lse),
+          _ptr(draft), _ptr(ws), wsb, _stream(stream))
+    return {"idx": idx, "val": val, "lse": lse, "draft": draft}
 
 
 # --------------------------------------------------------------------- fusion

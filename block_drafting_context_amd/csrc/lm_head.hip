@@ -1,0 +1,719 @@
+// lm_head.hip -- the drafter's LM head with top-k, the row log-normaliser and
+// the draft draw fused into the GEMM epilogue, for gfx950.
+//
+// "Beam 1.0 DFlash2" model card, "Model": the drafter reuses the target's LM
+// head (151,936-entry vocabulary, hidden size 5,120).  "DFlash vs DFlash 2",
+// "The candidate selector": top-k candidates of every block position, and the
+// full-vocabulary LM-head pass is the costly part; "The problem: one
+// expensive token at a time": the drafter proposes y ~ q = softmax(z / T).
+//
+// The logits z = h W^T never reach HBM.  One persistent workgroup per CU owns
+// a run of consecutive 128-entry vocabulary segments and streams them as
+// tiles of 256 entries x (up to) 256 hidden rows, so every weight byte is read
+// once per pass.  K advances in stages of 64 through LDS (weights in a 3-slot
+// ring, two stages ahead; hidden rows in a 2-slot ring, one stage ahead; both
+// by global_load_lds_dwordx4 with the 16-byte chunk c of row r stored at
+// chunk c ^ (r % 8)).  Eight waves each accumulate one segment (128 entries)
+// x 64 rows with v_mfma_f32_16x16x32_bf16, the vocabulary as the MFMA row
+// operand: lane (g, i) of a 16 x 16 tile then holds entries 4g..4g+3 of
+// hidden row i, i.e. every lane ends with 32 logits of one row and the four
+// lanes i, i+16, i+32, i+48 share that row's segment.  The epilogue reduces
+// each (row, segment) in registers across those four lanes:
+//   * m = max z and s = sum 2^((z - m) log2(e)/T);
+//   * the entry drawn inside the segment: inverse CDF of its weights in
+//     vocabulary order at the uniform of purpose 3 + 256 * segment;
+//   * top-k candidates: theta = the smallest of the four lanes' ceil(k/4)-th
+//     largest values, so at least k distinct entries are >= theta and the
+//     segment's top k all are; up to 32 such entries go to the segment's
+//     slot, otherwise k exact selection rounds fill it.
+// A finalize kernel per row takes tau = the k-th largest segment maximum
+// (every top-k entry is >= tau, so only segments with m >= tau are read),
+// merges their slots, adds the segment masses in fp64 for the
+// log-normaliser, and picks the segment by the inverse CDF of the masses at
+// the row's purpose-0 uniform; the draft is that segment's drawn entry.
+// P(v) = (S_J / S) (w_v / S_J) = w_v / S: an exact draw from softmax(z / T).
+#include <climits>
+#include <cmath>
+
+#include "common.hpp"
+
+namespace dfl {
+namespace {
+
+constexpr int kSegW = 128;            // vocabulary segment: draw step and candidate slot
+constexpr int kHeadRows = 256;        // hidden rows per pass over the weights
+constexpr int kTileV = 2 * kSegW;     // vocabulary entries per workgroup tile
+constexpr int kHBK = 64;              // K stage
+constexpr int kHRowB = kHBK * 2;      // bytes per staged row
+constexpr int kWSlots = 3;            // weight ring: two stages in flight
+constexpr int kHSlots = 2;            // hidden-row ring: one stage in flight
+constexpr int kHWaves = 8;            // 2 segments x 4 row quarters
+constexpr int kLoadsPerWave = kTileV * kHRowB / 1024 / kHWaves;  // 1 KB DMA instructions per ring
+constexpr int kSlotCap = 32;          // candidates kept per (row, segment)
+constexpr int kHeadMaxK = 16;
+constexpr int kHeadCUs = 256;
+constexpr int kFinThreads = 256;
+constexpr int kNone = INT_MAX;
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw byte buffers on gfx9 parts
+
+static_assert(kLoadsPerWave == kHeadRows * kHRowB / 1024 / kHWaves, "both rings load alike");
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void bare_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct SegStat {
+    float m;     // segment maximum
+    float s;     // sum 2^((z - m) log2(e)/T) (0 when greedy)
+    int draw;    // entry drawn inside the segment (-1 when no draw)
+    int count;   // candidates in the segment's slot
+};
+
+struct HeadArgs {
+    const uint16_t* h;     // [rows, d] bf16
+    const uint16_t* w;     // [V, d] bf16
+    SegStat* stats;        // [rows][nseg]
+    u32x2* cand;           // [rows][nseg][kSlotCap]: (value bits, vocabulary index)
+    const uint64_t* seeds;
+    uint64_t step;
+    int M, row0, d, V, nseg, gamma, groups, k;
+    float c2;              // log2(e) / T (0 when greedy)
+    int want_exp, want_draw;
+};
+
+// {value of the lane with bit W of its index clear, value of the lane with it
+// set}, for the pair (lane, lane ^ W), W = 16 or 32 (v_permlane16/32_swap; the
+// layout was measured on gfx950).  Used where the order within a pair matters.
+template <int W>
+__device__ __forceinline__ void lo_hi(float v, float& lo, float& hi) {
+    unsigned r0, r1;
+    swap_pair<W>(__float_as_uint(v), r0, r1);
+    lo = __uint_as_float(r0);
+    hi = __uint_as_float(r1);
+}
+template <int W>
+__device__ __forceinline__ void lo_hi(int v, int& lo, int& hi) {
+    unsigned r0, r1;
+    swap_pair<W>((unsigned)v, r0, r1);
+    lo = (int)r0;
+    hi = (int)r1;
+}
+
+// Over the four lanes (grp = 0..3) sharing a row: the exclusive prefix of v in
+// grp order, and the total.  Every lane adds the same operands in the same
+// order, so the total is bit-identical across the four lanes.
+__device__ __forceinline__ float quad_scan(float v, int grp, float& total) {
+    float lo, hi;
+    lo_hi<16>(v, lo, hi);
+    const float pair = lo + hi;
+    const float in_pair = (grp & 1) ? lo : 0.f;
+    float plo, phi;
+    lo_hi<32>(pair, plo, phi);
+    total = plo + phi;
+    return in_pair + ((grp & 2) ? plo : 0.f);
+}
+__device__ __forceinline__ int quad_scan(int v, int grp, int& total) {
+    int lo, hi;
+    lo_hi<16>(v, lo, hi);
+    const int pair = lo + hi;
+    int plo, phi;
+    lo_hi<32>(pair, plo, phi);
+    total = plo + phi;
+    return ((grp & 1) ? lo : 0) + ((grp & 2) ? plo : 0);
+}
+__device__ __forceinline__ float quad_min(float v) {
+    float lo, hi;
+    lo_hi<16>(v, lo, hi);
+    v = fminf(lo, hi);
+    lo_hi<32>(v, lo, hi);
+    return fminf(lo, hi);
+}
+__device__ __forceinline__ float quad_max(float v) {
+    float lo, hi;
+    lo_hi<16>(v, lo, hi);
+    v = fmaxf(lo, hi);
+    lo_hi<32>(v, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ int quad_min(int v) {
+    int lo, hi;
+    lo_hi<16>(v, lo, hi);
+    v = min(lo, hi);
+    lo_hi<32>(v, lo, hi);
+    return min(lo, hi);
+}
+__device__ __forceinline__ int quad_max(int v) {
+    int lo, hi;
+    lo_hi<16>(v, lo, hi);
+    v = max(lo, hi);
+    lo_hi<32>(v, lo, hi);
+    return max(lo, hi);
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS at m0 + 16 * lane
+// (buffer_load_dwordx4 ... lds).  Written as inline assembly so that the
+// compiler, which cannot see which ring slot a DMA targets, does not guard the
+// operand fetches from the other slots with waits for every load in flight;
+// the kernel waits for its own loads explicitly.  NT: non-temporal.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    if (NT)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// raw byte buffer over [base, base + bytes)
+__device__ __forceinline__ i32x4 byte_buffer(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)p;
+    r[1] = (int)((uint32_t)(p >> 32) & 0xFFFFu);  // stride 0
+    r[2] = (int)bytes;
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);  // low half of the flat address = LDS offset
+}
+
+// TT = ceil(k / 4): per-lane depth of the top-k threshold.
+template <int TT>
+__global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char sw[kWSlots][kTileV * kHRowB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sh[kHSlots][kHeadRows * kHRowB];
+
+    const int gidx = blockIdx.x;
+    const int s0 = (int)((long)gidx * a.nseg / a.groups);
+    const int s1 = (int)((long)(gidx + 1) * a.nseg / a.groups);
+    const int ntile = (s1 - s0 + 1) / 2;
+    const int nk = a.d / kHBK;
+    const int total = ntile * nk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = wave >> 2, wr = wave & 3;   // segment of the tile, row quarter
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int rl = lane >> 3, pc = lane & 7;   // DMA: row within an instruction, physical chunk
+
+    // DMA: a buffer resource for the tile's weight rows or the pass's hidden
+    // rows, a per-lane byte offset (row, swizzled chunk) and the stage's K
+    // offset as the scalar offset.  Rows beyond the tile or the pass read a
+    // valid row (never used).
+    uint32_t h_off[kLoadsPerWave];
+#pragma unroll
+    for (int ins = 0; ins < kLoadsPerWave; ++ins) {
+        const int r = (wave * kLoadsPerWave + ins) * 8 + rl;
+        const int m = r < a.M ? r : a.M - 1;
+        h_off[ins] = (uint32_t)m * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
+    }
+    const i32x4 h_rsrc = byte_buffer(a.h + (size_t)a.row0 * a.d, (uint32_t)(a.M * a.d * 2));
+    auto issue_w = [&](int j) {
+        const int t = j / nk, kk = j - t * nk;
+        const int v0 = (s0 + 2 * t) * kSegW;
+        const int nv = min(min(s1 * kSegW, a.V), v0 + kTileV) - v0;  // valid rows of the tile
+        const i32x4 rsrc = byte_buffer(a.w + (size_t)v0 * a.d, (uint32_t)(nv * a.d * 2));
+        const uint32_t lds = lds_addr(sw[j % kWSlots]) + (uint32_t)(wave * kLoadsPerWave * 1024);
+#pragma unroll
+        for (int ins = 0; ins < kLoadsPerWave; ++ins) {
+            const int r = (wave * kLoadsPerWave + ins) * 8 + rl;
+            const int rr = r < nv ? r : nv - 1;
+            const uint32_t voff = (uint32_t)rr * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
+            dma16<true>(lds + ins * 1024, voff, rsrc, (uint32_t)(kk * kHBK * 2));
+        }
+    };
+    auto issue_h = [&](int j) {
+        const int kk = j % nk;
+        const uint32_t lds = lds_addr(sh[j % kHSlots]) + (uint32_t)(wave * kLoadsPerWave * 1024);
+#pragma unroll
+        for (int ins = 0; ins < kLoadsPerWave; ++ins)
+            dma16<false>(lds + ins * 1024, h_off[ins], h_rsrc, (uint32_t)(kk * kHBK * 2));
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const bool rows_live = wr * 64 < a.M;
+
+    auto compute = [&](int j) {
+        const unsigned char* Ws = sw[j % kWSlots];
+        const unsigned char* Hs = sh[j % kHSlots];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int c = s * 4 + grp;
+            bf16x8 fa[8], fb[4];
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                const int r = wv * kSegW + vb * 16 + i16;
+                fa[vb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        Ws + r * kHRowB + ((c ^ (r & 7)) * 16)));
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int r = wr * 64 + rb * 16 + i16;
+                fb[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        Hs + r * kHRowB + ((c ^ (r & 7)) * 16)));
+            }
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    acc[vb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[vb], fb[rb],
+                                                                          acc[vb][rb], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+        }
+    };
+
+    // Per-lane constants of the epilogue, fixed before the loop so that no
+    // 64-bit address is carried through it: the row this lane draws the
+    // segment uniform for (row wr*64 + grp*16 + i16) and its generator seed,
+    // and the pass-relative offsets of the lane's rows in the outputs.
+    uint64_t my_seed = 0;
+    int my_b = 0, my_g = 0;
+    if (a.want_draw) {
+        const int rloc = wr * 64 + grp * 16 + i16;
+        const int R = a.row0 + min(rloc, a.M - 1);
+        my_b = R / a.gamma;
+        my_g = R - my_b * a.gamma;
+        my_seed = a.seeds[my_b];
+    }
+    SegStat* const stats_p = a.stats + (size_t)a.row0 * a.nseg;
+    u32x2* const cand_p = a.cand + (size_t)a.row0 * a.nseg * kSlotCap;
+    const uint32_t lane_row_off = (uint32_t)(wr * 64 + i16) * (uint32_t)a.nseg;
+
+    // acc[vb][rb][e]: entry seg*128 + vb*16 + 4*grp + e, row wr*64 + rb*16 + i16
+    auto epilogue = [&](int t) {
+        const int seg = s0 + 2 * t + wv;
+        const int vseg = seg * kSegW;
+        const int nvalid = min(kSegW, a.V - vseg);
+        // Opaque copies: everything derived from them is computed here, per
+        // tile, instead of being hoisted out of the tile loop into registers
+        // that would then live through the whole K loop.
+        int g4 = grp << 2, li16 = i16, mb = my_b, mg = my_g;
+        uint32_t lro = lane_row_off;
+        uint64_t seed = my_seed;
+        asm volatile("" : "+v"(g4), "+v"(li16), "+v"(mb), "+v"(mg), "+v"(lro), "+v"(seed));
+        double u_mine = 0.0;
+        if (a.want_draw)
+            u_mine = philox_uniform(seed, a.step, (uint64_t)mb, (uint64_t)mg,
+                                    3 + 256 * (uint64_t)seg);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const bool live = wr * 64 + rb * 16 + li16 < a.M;
+            const uint32_t so = lro + (uint32_t)(rb * 16) * (uint32_t)a.nseg + (uint32_t)seg;
+            float z[32];
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = vb * 16 + g4 + e;
+                    z[vb * 4 + e] = o < nvalid ? acc[vb][rb][e] : -INFINITY;
+                }
+            float mx = z[0];
+#pragma unroll
+            for (int i = 1; i < 32; ++i) mx = fmaxf(mx, z[i]);
+            mx = quad_max(mx);
+
+            // top-k candidates: theta from the lanes' TT-th largest values
+            float top[TT];
+#pragma unroll
+            for (int q = 0; q < TT; ++q) top[q] = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+#pragma unroll
+                for (int q = TT - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], z[i]);
+                top[0] = fmaxf(top[0], z[i]);
+            }
+            const float th = quad_min(top[TT - 1]);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) cnt += (z[i] >= th && z[i] > -INFINITY) ? 1 : 0;
+            int C;
+            int at = quad_scan(cnt, grp, C);
+            u32x2* const slot = cand_p + (size_t)so * kSlotCap;
+            if (C <= kSlotCap) {
+                if (live) {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) {
+                        if (z[i] >= th && z[i] > -INFINITY) {
+                            u32x2 c;
+                            c[0] = __float_as_uint(z[i]);
+                            c[1] = (unsigned)(vseg + (i >> 2) * 16 + g4 + (i & 3));
+                            slot[at++] = c;
+                        }
+                    }
+                }
+            } else {
+                // more than a slot passes the threshold (many equal values):
+                // the exact top k by k rounds of (value desc, index asc) selection
+                uint32_t taken = 0;
+                for (int r = 0; r < a.k; ++r) {
+                    float bv = -INFINITY;
+                    int bi = -1;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) {
+                        const int ti = vseg + (i >> 2) * 16 + g4 + (i & 3);
+                        if (!((taken >> i) & 1) && z[i] > -INFINITY && ranks_ahead(z[i], ti, bv, bi)) {
+                            bv = z[i];
+                            bi = ti;
+                        }
+                    }
+                    best_swap<16>(bv, bi);
+                    best_swap<32>(bv, bi);
+                    if (live && grp == 0) {
+                        u32x2 c;
+                        c[0] = __float_as_uint(bv);
+                        c[1] = (unsigned)bi;
+                        slot[r] = c;
+                    }
+                    const int o = bi - vseg - g4;  // this lane's element, if it won
+                    if (o >= 0 && (o & 15) < 4) taken |= 1u << ((o >> 4) * 4 + (o & 3));
+                }
+                C = a.k;
+            }
+
+            // segment mass and the draw inside the segment (z becomes the weights)
+            float ssum = 0.f;
+            int drawn = -1;
+            if (a.want_exp) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) z[i] = fast_exp2((z[i] - mx) * a.c2);
+                float pre[8];
+                float base = 0.f;
+#pragma unroll
+                for (int vb = 0; vb < 8; ++vb) {
+                    const float q = ((z[vb * 4] + z[vb * 4 + 1]) + z[vb * 4 + 2]) + z[vb * 4 + 3];
+                    float tot;
+                    pre[vb] = base + quad_scan(q, grp, tot);
+                    base += tot;
+                }
+                ssum = base;
+                if (a.want_draw) {
+                    const double u = __shfl(u_mine, li16 + 16 * rb);
+                    const float tgt = (float)(u * (double)ssum);
+                    int first = kNone, last = -1;
+#pragma unroll
+                    for (int vb = 0; vb < 8; ++vb) {
+                        float cum = pre[vb];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float wi = z[vb * 4 + e];
+                            const int o = vb * 16 + g4 + e;
+                            cum += wi;
+                            if (wi > 0.f) {
+                                last = o;
+                                if (cum > tgt) first = min(first, o);
+                            }
+                        }
+                    }
+                    first = quad_min(first);
+                    last = quad_max(last);
+                    drawn = vseg + (first != kNone ? first : last);
+                }
+            }
+            if (live && grp == 0) stats_p[so] = SegStat{mx, ssum, drawn, C};
+        }
+    };
+
+    // One continuous stream of stages over all tiles (stage j: tile j / nk,
+    // K step j % nk), so the next tile's first stages load during an epilogue.
+    if (total > 0) {
+        issue_h(0);
+        issue_w(0);
+        if (total > 1) issue_w(1);
+    }
+    for (int j = 0; j < total; ++j) {
+        const int t = j / nk, kk = j - t * nk;
+        // h(j) was issued right before W(j + 1); the first stage of a tile also
+        // waits for the previous epilogue's stores
+        if ((kk == 0 && j > 0) || j + 1 == total) wait_vmem<0>();
+        else wait_vmem<kLoadsPerWave>();
+        bare_barrier();  // stage j landed for every wave; stage j - 1's slots are free
+        if (j + 1 < total) issue_h(j + 1);
+        if (j + 2 < total) issue_w(j + 2);
+        const bool live = rows_live && (s0 + 2 * t + wv < s1);
+        if (live) compute(j);
+        if (kk == nk - 1) {
+            if (live) epilogue(t);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+// ------------------------------------------------------------------ finalize
+struct FinArgs {
+    const SegStat* stats;
+    const u32x2* cand;
+    const uint64_t* seeds;
+    uint64_t step;
+    int nseg, gamma, k;
+    double c2;       // log2(e) / T as used by the segment sums
+    int want_exp, want_draw;
+    int32_t* idx;
+    float* val;
+    double* lse;
+    int32_t* draft;
+};
+
+__device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si) {
+    wave_best(v, i);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { sv[wave] = v; si[wave] = i; }
+    __syncthreads();
+    v = sv[0];
+    i = si[0];
+#pragma unroll
+    for (int w = 1; w < kFinThreads / 64; ++w) best_of(v, i, sv[w], si[w]);
+    __syncthreads();
+}
+
+__device__ __forceinline__ int block_min(int v, int* si) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = min(v, __shfl_xor(v, 1));
+    v = min(v, __shfl_xor(v, 2));
+    v = min(v, __shfl_xor(v, 4));
+    v = min(v, __shfl_xor(v, 8));
+    v = min(v, __shfl_xor(v, 16));
+    v = min(v, __shfl_xor(v, 32));
+    if (lane == 0) si[wave] = v;
+    __syncthreads();
+    int r = si[0];
+#pragma unroll
+    for (int w = 1; w < kFinThreads / 64; ++w) r = min(r, si[w]);
+    __syncthreads();
+    return r;
+}
+
+// segment j's mass relative to the row maximum mx
+__device__ __forceinline__ double seg_mass(const SegStat& s, float mx, double c2) {
+    return (double)s.s * exp2(((double)s.m - (double)mx) * c2);
+}
+
+__global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a) {
+    __shared__ float sv[kFinThreads / 64];
+    __shared__ int si[kFinThreads / 64];
+    __shared__ double sd[kFinThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t R = blockIdx.x;
+    const SegStat* st = a.stats + R * a.nseg;
+    const u32x2* cd = a.cand + R * a.nseg * kSlotCap;
+
+    // tau: the k-th largest segment maximum (k rounds, each taking the best
+    // segment ranked after the previous winner); -inf with fewer than k segments
+    float pv = INFINITY, tau = -INFINITY, mx = -INFINITY;
+    int pi = -1;
+    for (int r = 0; r < a.k; ++r) {
+        float bv = -INFINITY;
+        int bi = -1;
+        for (int j = tid; j < a.nseg; j += kFinThreads) {
+            const float m = st[j].m;
+            if (ranks_ahead(pv, pi, m, j) && ranks_ahead(m, j, bv, bi)) { bv = m; bi = j; }
+        }
+        block_best(bv, bi, sv, si);
+        if (bi < 0) { tau = -INFINITY; break; }
+        if (r == 0) mx = bv;
+        pv = bv;
+        pi = bi;
+        tau = bv;
+    }
+
+    // candidates of the segments that can hold a top-k entry, kept per thread
+    // as a sorted list (value desc, index asc)
+    float lv[kHeadMaxK];
+    int li[kHeadMaxK];
+#pragma unroll
+    for (int q = 0; q < kHeadMaxK; ++q) { lv[q] = -INFINITY; li[q] = -1; }
+    for (int j = tid; j < a.nseg; j += kFinThreads) {
+        const SegStat s = st[j];
+        if (!(s.m >= tau)) continue;
+        for (int c = 0; c < s.count; ++c) {
+            const u32x2 e = cd[(size_t)j * kSlotCap + c];
+            const float v = __uint_as_float(e[0]);
+            const int i = (int)e[1];
+            if (!ranks_ahead(v, i, lv[kHeadMaxK - 1], li[kHeadMaxK - 1])) continue;
+#pragma unroll
+            for (int q = kHeadMaxK - 1; q >= 0; --q) {
+                const bool above = q > 0 && ranks_ahead(v, i, lv[q - 1], li[q - 1]);
+                const bool here = ranks_ahead(v, i, lv[q], li[q]);
+                if (above) { lv[q] = lv[q - 1]; li[q] = li[q - 1]; }
+                else if (here) { lv[q] = v; li[q] = i; }
+            }
+        }
+    }
+    int top1 = -1;
+    for (int r = 0; r < a.k; ++r) {
+        float bv = lv[0];
+        int bi = li[0];
+        block_best(bv, bi, sv, si);
+        if (tid == 0) {
+            a.idx[R * a.k + r] = bi;
+            a.val[R * a.k + r] = bv;
+        }
+        if (r == 0) top1 = bi;
+        if (bi >= 0 && li[0] == bi) {
+#pragma unroll
+            for (int q = 0; q < kHeadMaxK - 1; ++q) { lv[q] = lv[q + 1]; li[q] = li[q + 1]; }
+            lv[kHeadMaxK - 1] = -INFINITY;
+            li[kHeadMaxK - 1] = -1;
+        }
+    }
+
+    if (!a.want_exp) {
+        if (tid == 0) {
+            if (a.lse) a.lse[R] = NAN;
+            if (a.draft) a.draft[R] = top1;
+        }
+        return;
+    }
+    // segment masses in vocabulary order: contiguous runs per thread, fp64
+    const int j0 = (int)((long)tid * a.nseg / kFinThreads);
+    const int j1 = (int)((long)(tid + 1) * a.nseg / kFinThreads);
+    double run = 0.0;
+    for (int j = j0; j < j1; ++j) run += seg_mass(st[j], mx, a.c2);
+    const double incl = wave_inclusive_scan(run);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    if (lane == 63) sd[wave] = incl;
+    __syncthreads();
+    double before = 0.0, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kFinThreads / 64; ++w) {
+        if (w < wave) before += sd[w];
+        total += sd[w];
+    }
+    excl += before;
+    if (tid == 0 && a.lse) a.lse[R] = (double)mx * a.c2 * kLn2 + log(total);
+    if (!a.want_draw) return;
+    const int b = (int)(R / a.gamma), g = (int)(R % a.gamma);
+    const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)g, kDraftDraw);
+    const double tgt = u * total;
+    int first = kNone, last = -1;
+    double cum = excl;
+    for (int j = j0; j < j1; ++j) {
+        const double sj = seg_mass(st[j], mx, a.c2);
+        cum += sj;
+        if (sj > 0.0) {
+            last = j;
+            if (cum > tgt && first == kNone) first = j;
+        }
+    }
+    first = block_min(first, si);
+    last = -block_min(-last, si);
+    const int J = first != kNone ? first : last;
+    if (tid == 0) a.draft[R] = st[J].draw;
+}
+
+struct HeadLayout {
+    size_t stats, cand, bytes;
+};
+
+HeadLayout head_layout(int rows, int vocab) {
+    const size_t nseg = ((size_t)vocab + kSegW - 1) / kSegW;
+    HeadLayout L{};
+    Carve c;
+    L.stats = c.take<SegStat>((size_t)rows * nseg);
+    L.cand = c.take<u32x2>((size_t)rows * nseg * kSlotCap);
+    L.bytes = c.total();
+    return L;
+}
+
+void launch_head(int tt, dim3 grid, const HeadArgs& a, hipStream_t st) {
+    const dim3 block(64 * kHWaves);
+    switch (tt) {
+        case 1: hipLaunchKernelGGL(lm_head_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(lm_head_kernel<2>, grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL(lm_head_kernel<3>, grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL(lm_head_kernel<4>, grid, block, 0, st, a); break;
+    }
+}
+
+}  // namespace
+}  // namespace dfl
+
+using namespace dfl;
+
+extern "C" size_t dflash_lm_head_topk_workspace_size(int rows, int d_model, int vocab, int k) {
+    if (rows < 1 || d_model < 1 || vocab < 1 || k < 1) return 0;
+    return head_layout(rows, vocab).bytes;
+}
+
+extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows,
+                                   int gamma, int d_model, int vocab, int k, float temperature,
+                                   const uint64_t* seeds, uint64_t step, int32_t* topk_idx,
+                                   float* topk_val, double* lse, int32_t* draft, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (rows < 0 || gamma < 1 || d_model < 1 || vocab < 1 || k < 1 || k > vocab)
+        return DFLASH_ERR_SHAPE;
+    if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
+    if (rows == 0) return DFLASH_OK;
+    if (!hidden || !w_head || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
+    const bool sample = temperature > 0.f;
+    if (sample && draft && !seeds) return DFLASH_ERR_NULL;
+    if (k > kHeadMaxK || d_model % kHBK || (reinterpret_cast<uintptr_t>(hidden) & 15) ||
+        (reinterpret_cast<uintptr_t>(w_head) & 15))
+        return DFLASH_ERR_UNSUPPORTED;
+    const HeadLayout L = head_layout(rows, vocab);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.bytes)
+        return DFLASH_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    const int nseg = (vocab + kSegW - 1) / kSegW;
+    HeadArgs ha{};
+    ha.h = hidden;
+    ha.w = w_head;
+    ha.stats = reinterpret_cast<SegStat*>(ws + L.stats);
+    ha.cand = reinterpret_cast<u32x2*>(ws + L.cand);
+    ha.seeds = seeds;
+    ha.step = step;
+    ha.d = d_model;
+    ha.V = vocab;
+    ha.nseg = nseg;
+    ha.gamma = gamma;
+    ha.groups = min(kHeadCUs, (nseg + 1) / 2);
+    ha.k = k;
+    ha.c2 = sample ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
+    ha.want_exp = sample && (lse || draft);
+    ha.want_draw = sample && draft;
+    for (int row0 = 0; row0 < rows; row0 += kHeadRows) {
+        ha.row0 = row0;
+        ha.M = min(kHeadRows, rows - row0);
+        launch_head((k + 3) / 4, dim3(ha.groups), ha, st);
+        const int rc = launch_status();
+        if (rc) return rc;
+    }
+    FinArgs fa{};
+    fa.stats = ha.stats;
+    fa.cand = ha.cand;
+    fa.seeds = seeds;
+    fa.step = step;
+    fa.nseg = nseg;
+    fa.gamma = gamma;
+    fa.k = k;
+    fa.c2 = (double)ha.c2;
+    fa.want_exp = ha.want_exp;
+    fa.want_draw = ha.want_draw;
+    fa.idx = topk_idx;
+    fa.val = topk_val;
+    fa.lse = lse;
+    fa.draft = draft;
+    hipLaunchKernelGGL(lm_head_finalize_kernel, dim3(rows), dim3(kFinThreads), 0, st, fa);
+    return launch_status();
+}

@@ -116,6 +116,16 @@ def fuse_inputs(rows, n_taps, d_tgt, d_model, n_layers, n_kv, d_head, seed, devi
     return {"x": x, "w_c": wc, "w_kv": wkv, "gain": g}
 
 
+def lm_head_inputs(rows, d_model, vocab, seed, logit_std=5 ** 0.5, device="cpu",
+                   dtype=torch.bfloat16):
+    """Drafter hidden rows h ~ N(0,1) and LM-head weights W ~ N(0, logit_std^2 / d_model)
+    (one row per vocabulary entry), so the logits h W^T are ~ N(0, logit_std^2)."""
+    h = normal((rows, d_model), seed, "head_hidden", dtype=dtype, device=device)
+    w = normal((vocab, d_model), seed, "w_head", std=logit_std / float(np.sqrt(d_model)),
+               dtype=dtype, device=device)
+    return h, w
+
+
 def philox_seeds(batch, base=0, device="cpu"):
     """Per-sequence generator seeds base, base+1, ... as int64 (reinterpreted as uint64)."""
     return torch.arange(base, base + batch, dtype=torch.int64, device=device)

@@ -13,6 +13,9 @@
  *   dflash_select_path   the candidate selector's walk through the top-k
  *                        candidates of each block position.
  *   dflash_two_tap_conv  the two-tap dynamic convolution inside a block.
+ *   dflash_lm_head_topk  the drafter's LM head with top-k, log-normaliser and
+ *                        drafted token computed in the GEMM epilogue (the
+ *                        logits never reach memory).
  *
  * Sources (web pages, cited by title and section):
  *   "DFlash vs DFlash 2" (blog): "The problem: one expensive token at a time",
@@ -280,6 +283,47 @@ int dflash_select_path(const int32_t* cand_idx, const float* cand_score, const u
  * ------------------------------------------------------------------------ */
 int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int batch, int gamma,
                         int d, int n_groups, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_lm_head_topk -- the drafter's LM head, z = hidden W_head^T, with the
+ * drafter-side outputs of dflash_topk computed from z in the GEMM's epilogue.
+ *
+ * "Beam 1.0 DFlash2" model card, "Model": the drafter reuses the target's LM
+ * head over the shared 151,936-entry vocabulary; "DFlash vs DFlash 2", "The
+ * candidate selector": top-k candidates of every block position, the
+ * full-vocabulary LM-head pass being the costly step; "The problem: one
+ * expensive token at a time": the drafter proposes y ~ softmax(z / T).
+ *
+ *   hidden   [rows, d_model] bf16 (16-byte aligned); row r is block position
+ *            r % gamma of sequence r / gamma.
+ *   w_head   [vocab, d_model] bf16 (16-byte aligned), one row per token.
+ *   topk_idx [rows, k] int32, topk_val [rows, k] float32: the k largest
+ *            logits of each row, descending; equal logits in increasing index
+ *            order.
+ *   lse      [rows] float64, log sum_v exp(z_v / T) (T > 0; NaN when T == 0);
+ *            may be NULL.
+ *   draft    [rows] int32; may be NULL.  T == 0: the row's argmax (lowest
+ *            index among equal maxima).  T > 0: an exact draw from
+ *            softmax(z / T) in two inverse-CDF steps over consecutive
+ *            128-entry vocabulary segments: the segment J by the segment
+ *            masses at the purpose-0 uniform of (seeds[b], step, b, r % gamma),
+ *            then the entry inside J by its weights at the uniform of purpose
+ *            3 + 256 J.  (A different realization than dflash_topk's
+ *            single-step draw with the same seeds; the same distribution.)
+ *   seeds    [rows / gamma rounded up] uint64 (device); may be NULL when
+ *            T == 0 or draft == NULL.
+ * Work: the weights are streamed from HBM once per 256 rows of hidden.
+ * Supported: 1 <= k <= 16, k <= vocab, d_model % 64 == 0.
+ * Accuracy: bf16 products, fp32 accumulation (the GEMM); fp32 exponentials
+ * and segment sums, fp64 across segments.
+ * Workspace: dflash_lm_head_topk_workspace_size bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t dflash_lm_head_topk_workspace_size(int rows, int d_model, int vocab, int k);
+int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows, int gamma,
+                        int d_model, int vocab, int k, float temperature,
+                        const uint64_t* seeds, uint64_t step, int32_t* topk_idx,
+                        float* topk_val, double* lse, int32_t* draft, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -181,3 +181,33 @@ def test_binding_raises_on_bad_status():
     with pytest.raises(dfl.DFlashError) as e:
         dfl._call("dflash_topk", P, 1, 1, 1024, 0, 0.0, None, 0, P, P, None, None, None, 0, None)
     assert e.value.status == -2
+
+
+def head(**kw):
+    a = dict(h=P, w=P, rows=256, G=8, d=5120, V=151936, k=8, T=0.7, seeds=P, step=0, idx=P,
+             val=P, lse=None, draft=P, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return dfl.load().dflash_lm_head_topk(a["h"], a["w"], a["rows"], a["G"], a["d"], a["V"], a["k"],
+                                          a["T"], a["seeds"], a["step"], a["idx"], a["val"],
+                                          a["lse"], a["draft"], a["ws"], a["wsb"], a["st"])
+
+
+def test_lm_head_validation():
+    assert head(rows=0) == 0                 # nothing to do, nothing launched
+    assert head(rows=-1) == -2
+    assert head(G=0) == -2
+    assert head(k=0) == -2
+    assert head(V=4, k=5) == -2              # k > vocab
+    assert head(T=-0.1) == -2
+    assert head(T=float("nan")) == -2
+    assert head(h=None) == -1
+    assert head(idx=None) == -1
+    assert head(seeds=None) == -1            # a sampled draft needs seeds
+    assert head(seeds=None, draft=None) == -4  # no draft: no seeds needed; fails on workspace only
+    assert head(seeds=None, T=0.0) == -4
+    assert head(k=17) == -3
+    assert head(d=5100) == -3
+    assert head(w=ctypes.c_void_p(0x1008)) == -3
+    assert head() == -4
+    assert dfl.dflash_lm_head_topk_workspace_size(256, 5120, 151936, 8) > 0
+    assert dfl.dflash_lm_head_topk_workspace_size(0, 5120, 151936, 8) == 0
