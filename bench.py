@@ -21,8 +21,10 @@ kernel (block attention, HBM-bound) measured with HIP events on its stream
 inside the timed region, and the CPU oracle timed on a bounded sample.  Also
 reported: the same throughput with one attention layer instead of five, the
 512-row fusion call, the candidate selector's walk and the verification of its
-deterministic drafts, one two-tap dynamic convolution, a device-copy bandwidth (context for the 8 TB/s peak) and
-the oracle on a single host thread.
+deterministic drafts, one two-tap dynamic convolution, the drafter's LM head
+with the top-k epilogue fused in (beside the unfused GEMM + top-k route), a
+device-copy bandwidth (context for the 8 TB/s peak) and the oracle on a single
+host thread.
 """
 from __future__ import annotations
 
@@ -272,6 +274,62 @@ def conv_figure(dev, warmup, steps):
             "algorithmic_bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def lm_head_figure(dev, warmup, steps):
+    """NEXT row: the drafter's LM head with the top-k / lse / draft epilogue fused
+    in (dflash_lm_head_topk) for the step's 256 rows: [256 x 5120] x [5120 x 151936]
+    bf16, top-8, T = 0.7, timed with HIP events on the launching stream.  Beside it,
+    the unfused route a caller would otherwise take: the same product as one library
+    GEMM (bf16 out), widened to fp32 logits, then dflash_topk."""
+    rows, dm = B * G, D_MODEL
+    h, w = syn.lm_head_inputs(rows, dm, V, SEED, device=dev)
+    seeds = syn.philox_seeds(B, 0, device=dev)
+    out = {"idx": torch.empty((rows, TOPK), dtype=torch.int32, device=dev),
+           "val": torch.empty((rows, TOPK), dtype=torch.float32, device=dev),
+           "lse": torch.empty(rows, dtype=torch.float64, device=dev),
+           "draft": torch.empty(rows, dtype=torch.int32, device=dev)}
+    ws = torch.empty(dfl.dflash_lm_head_topk_workspace_size(rows, dm, V, TOPK), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        dfl.dflash_lm_head_topk(h, w, G, TOPK, T, seeds=seeds, step=0, outputs=out, workspace=ws,
+                                stream=stream)
+
+    def timed(fn, n):
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    us = timed(fused, steps)
+    flops = 2.0 * rows * dm * V
+    wbytes = V * dm * 2 + rows * dm * 2
+    res = {"rows": rows, "d_model": dm, "vocab": V, "k": TOPK, "temperature": T,
+           "us": round(us, 2),
+           "weight_stream_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / 2500.0, 4)}
+    logits16 = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+    logits32 = torch.empty((rows, V), dtype=torch.float32, device=dev)
+    zd = logits32.view(B, G, V)
+    tk_ws = torch.empty(dfl.dflash_topk_workspace_size(B, G, V, TOPK), dtype=torch.uint8, device=dev)
+    res["unfused_gemm_bf16_us"] = round(timed(lambda: torch.mm(h, w.t(), out=logits16), steps), 2)
+    res["unfused_widen_fp32_us"] = round(timed(lambda: logits32.copy_(logits16), steps), 2)
+    res["unfused_topk_us"] = round(timed(lambda: dfl.dflash_topk(zd, TOPK, T, seeds=seeds,
+                                                                 workspace=tk_ws, stream=stream),
+                                         steps), 2)
+    del h, w, logits16, logits32, ws, tk_ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_probe():
     """Three copies of 2^28 fp32 (1 GiB read + 1 GiB written each): the
     calibration kernel for the HBM byte counters."""
@@ -407,6 +465,7 @@ def main():
     fuse512 = fuse_512_rows(dev, args.warmup, args.steps)
     selector = selector_figure(wl, dev, args.warmup, args.steps)
     conv = conv_figure(dev, args.warmup, args.steps)
+    head = lm_head_figure(dev, args.warmup, args.steps)
     copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
@@ -456,6 +515,7 @@ def main():
         "context_fuse_512_rows": fuse512,
         "candidate_selector": selector,
         "two_tap_conv": conv,
+        "lm_head_topk": head,
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
     }

@@ -11,9 +11,9 @@
 // a run of consecutive 128-entry vocabulary segments and streams them as
 // tiles of 256 entries x (up to) 256 hidden rows, so every weight byte is read
 // once per pass.  K advances in stages of 64 through LDS (weights in a 3-slot
-// ring, two stages ahead; hidden rows in a 2-slot ring, one stage ahead; both
-// by global_load_lds_dwordx4 with the 16-byte chunk c of row r stored at
-// chunk c ^ (r % 8)).  Eight waves each accumulate one segment (128 entries)
+// ring, two stages ahead; hidden rows in a 2-slot ring, one ahead; both
+// by buffer_load_dwordx4 ... lds with the 16-byte chunks of each row
+// XOR-swizzled).  Eight waves each accumulate one segment (128 entries)
 // x 64 rows with v_mfma_f32_16x16x32_bf16, the vocabulary as the MFMA row
 // operand: lane (g, i) of a 16 x 16 tile then holds entries 4g..4g+3 of
 // hidden row i, i.e. every lane ends with 32 logits of one row and the four
@@ -22,13 +22,15 @@
 //   * m = max z and s = sum 2^((z - m) log2(e)/T);
 //   * the entry drawn inside the segment: inverse CDF of its weights in
 //     vocabulary order at the uniform of purpose 3 + 256 * segment;
-//   * top-k candidates: theta = the smallest of the four lanes' ceil(k/4)-th
-//     largest values, so at least k distinct entries are >= theta and the
-//     segment's top k all are; up to 32 such entries go to the segment's
-//     slot, otherwise k exact selection rounds fill it.
+//   * top-k candidates: theta = the k-th largest of the four lanes' TT largest
+//     values (TT = min(4, ceil(k/2)), 4 TT >= k distinct entries), a lower
+//     bound of the segment's k-th largest entry; every quad of 4 consecutive
+//     entries (one lane's registers) holding a value >= theta is written whole
+//     to the segment's record slots, in order, with a 32-bit mask of which
+//     quads they are (ties need no special case: all of them are written).
 // A finalize kernel per row takes tau = the k-th largest segment maximum
 // (every top-k entry is >= tau, so only segments with m >= tau are read),
-// merges their slots, adds the segment masses in fp64 for the
+// merges their records, adds the segment masses in fp64 for the
 // log-normaliser, and picks the segment by the inverse CDF of the masses at
 // the row's purpose-0 uniform; the draft is that segment's drawn entry.
 // P(v) = (S_J / S) (w_v / S_J) = w_v / S: an exact draw from softmax(z / T).
@@ -43,13 +45,30 @@ namespace {
 constexpr int kSegW = 128;            // vocabulary segment: draw step and candidate slot
 constexpr int kHeadRows = 256;        // hidden rows per pass over the weights
 constexpr int kTileV = 2 * kSegW;     // vocabulary entries per workgroup tile
-constexpr int kHBK = 64;              // K stage
+#ifndef DFL_HEAD_BK
+#define DFL_HEAD_BK 64
+#endif
+#ifndef DFL_HEAD_WSLOTS
+#define DFL_HEAD_WSLOTS 3
+#endif
+#ifndef DFL_HEAD_HSLOTS
+#define DFL_HEAD_HSLOTS 2
+#endif
+constexpr int kHBK = DFL_HEAD_BK;     // K stage
 constexpr int kHRowB = kHBK * 2;      // bytes per staged row
-constexpr int kWSlots = 3;            // weight ring: two stages in flight
-constexpr int kHSlots = 2;            // hidden-row ring: one stage in flight
+constexpr int kChunks = kHRowB / 16;  // 16-byte chunks per staged row
+constexpr int kRowsPerIns = 1024 / kHRowB;  // rows per 1 KB DMA instruction
+constexpr int kWSlots = DFL_HEAD_WSLOTS;    // weight ring: kWSlots - 1 stages in flight
+constexpr int kHSlots = DFL_HEAD_HSLOTS;    // hidden-row ring: kHSlots - 1 stages in flight
+constexpr int kLeadW = kWSlots - 1, kLeadH = kHSlots - 1;
+static_assert(kLeadW >= kLeadH && kLeadH >= 1, "the weights are issued at least as far ahead");
+static_assert(kWSlots * kTileV * kHRowB + kHSlots * 256 * kHRowB <= 160 * 1024, "LDS");
 constexpr int kHWaves = 8;            // 2 segments x 4 row quarters
 constexpr int kLoadsPerWave = kTileV * kHRowB / 1024 / kHWaves;  // 1 KB DMA instructions per ring
-constexpr int kSlotCap = 32;          // candidates kept per (row, segment)
+// loads a wave may still have in flight when it needs stage j: those issued
+// after h(j), i.e. W(j - kLeadH + kLeadW) and the kLeadH - 1 later batches
+constexpr int kWaitLoads = kLoadsPerWave + (kLeadH - 1) * 2 * kLoadsPerWave;
+constexpr int kQuads = kSegW / 4;     // quads of 4 entries per segment: candidate record slots
 constexpr int kHeadMaxK = 16;
 constexpr int kHeadCUs = 256;
 constexpr int kFinThreads = 256;
@@ -57,6 +76,11 @@ constexpr int kNone = INT_MAX;
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw byte buffers on gfx9 parts
 
 static_assert(kLoadsPerWave == kHeadRows * kHRowB / 1024 / kHWaves, "both rings load alike");
+
+// 16-byte chunk c of staged row r is stored at chunk c ^ swz(r): with the
+// row's 128 (or 64) bytes, eight consecutive rows read at one logical chunk
+// hit eight distinct 16-byte bank groups
+__device__ __forceinline__ int chunk_swz(int r) { return kChunks == 8 ? (r & 7) : ((r >> 1) & 3); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -73,14 +97,14 @@ struct SegStat {
     float m;     // segment maximum
     float s;     // sum 2^((z - m) log2(e)/T) (0 when greedy)
     int draw;    // entry drawn inside the segment (-1 when no draw)
-    int count;   // candidates in the segment's slot
+    int mask;    // bit vb*4 + g: candidate quad (vb, g) was written (in bit order)
 };
 
 struct HeadArgs {
     const uint16_t* h;     // [rows, d] bf16
     const uint16_t* w;     // [V, d] bf16
     SegStat* stats;        // [rows][nseg]
-    u32x2* cand;           // [rows][nseg][kSlotCap]: (value bits, vocabulary index)
+    u32x4* cand;           // [rows][nseg][kQuads]: candidate quads (4 logits each), in mask order
     const uint64_t* seeds;
     uint64_t step;
     int M, row0, d, V, nseg, gamma, groups, k;
@@ -188,7 +212,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);  // low half of the flat address = LDS offset
 }
 
-// TT = ceil(k / 4): per-lane depth of the top-k threshold.
+// TT = min(4, ceil(k / 2)): per-lane depth of the top-k threshold (4 TT >= k).
 template <int TT>
 __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sw[kWSlots][kTileV * kHRowB];
@@ -204,7 +228,7 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wv = wave >> 2, wr = wave & 3;   // segment of the tile, row quarter
     const int i16 = lane & 15, grp = lane >> 4;
-    const int rl = lane >> 3, pc = lane & 7;   // DMA: row within an instruction, physical chunk
+    const int rl = lane / kChunks, pc = lane % kChunks;  // DMA: row within an instruction, physical chunk
 
     // DMA: a buffer resource for the tile's weight rows or the pass's hidden
     // rows, a per-lane byte offset (row, swizzled chunk) and the stage's K
@@ -213,11 +237,18 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
     uint32_t h_off[kLoadsPerWave];
 #pragma unroll
     for (int ins = 0; ins < kLoadsPerWave; ++ins) {
-        const int r = (wave * kLoadsPerWave + ins) * 8 + rl;
+        const int r = (wave * kLoadsPerWave + ins) * kRowsPerIns + rl;
         const int m = r < a.M ? r : a.M - 1;
-        h_off[ins] = (uint32_t)m * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
+        h_off[ins] = (uint32_t)m * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
     }
     const i32x4 h_rsrc = byte_buffer(a.h + (size_t)a.row0 * a.d, (uint32_t)(a.M * a.d * 2));
+    // K step kk of a tile is read at byte offset kbyte(kk): each workgroup
+    // starts its K sweep at its own step, so the CUs' concurrent loads are
+    // spread over the memory channels instead of all touching one K column of
+    // the hidden rows and of their weight rows (measured: 470 -> 446 us at
+    // 256 x 5120 x 151,936)
+    const int krot = gidx % nk;
+    auto kbyte = [&](int kk) { int x = kk + krot; x -= x >= nk ? nk : 0; return (uint32_t)(x * kHBK * 2); };
     auto issue_w = [&](int j) {
         const int t = j / nk, kk = j - t * nk;
         const int v0 = (s0 + 2 * t) * kSegW;
@@ -226,10 +257,10 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         const uint32_t lds = lds_addr(sw[j % kWSlots]) + (uint32_t)(wave * kLoadsPerWave * 1024);
 #pragma unroll
         for (int ins = 0; ins < kLoadsPerWave; ++ins) {
-            const int r = (wave * kLoadsPerWave + ins) * 8 + rl;
+            const int r = (wave * kLoadsPerWave + ins) * kRowsPerIns + rl;
             const int rr = r < nv ? r : nv - 1;
-            const uint32_t voff = (uint32_t)rr * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
-            dma16<true>(lds + ins * 1024, voff, rsrc, (uint32_t)(kk * kHBK * 2));
+            const uint32_t voff = (uint32_t)rr * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
+            dma16<true>(lds + ins * 1024, voff, rsrc, kbyte(kk));
         }
     };
     auto issue_h = [&](int j) {
@@ -237,7 +268,7 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         const uint32_t lds = lds_addr(sh[j % kHSlots]) + (uint32_t)(wave * kLoadsPerWave * 1024);
 #pragma unroll
         for (int ins = 0; ins < kLoadsPerWave; ++ins)
-            dma16<false>(lds + ins * 1024, h_off[ins], h_rsrc, (uint32_t)(kk * kHBK * 2));
+            dma16<false>(lds + ins * 1024, h_off[ins], h_rsrc, kbyte(kk));
     };
 
     f32x4 acc[8][4];
@@ -252,20 +283,20 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         const unsigned char* Ws = sw[j % kWSlots];
         const unsigned char* Hs = sh[j % kHSlots];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < kHBK / 32; ++s) {
             const int c = s * 4 + grp;
             bf16x8 fa[8], fb[4];
 #pragma unroll
             for (int vb = 0; vb < 8; ++vb) {
                 const int r = wv * kSegW + vb * 16 + i16;
                 fa[vb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                        Ws + r * kHRowB + ((c ^ (r & 7)) * 16)));
+                                                        Ws + r * kHRowB + ((c ^ chunk_swz(r)) * 16)));
             }
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 const int r = wr * 64 + rb * 16 + i16;
                 fb[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                        Hs + r * kHRowB + ((c ^ (r & 7)) * 16)));
+                                                        Hs + r * kHRowB + ((c ^ chunk_swz(r)) * 16)));
             }
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -292,8 +323,14 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         my_seed = a.seeds[my_b];
     }
     SegStat* const stats_p = a.stats + (size_t)a.row0 * a.nseg;
-    u32x2* const cand_p = a.cand + (size_t)a.row0 * a.nseg * kSlotCap;
+    u32x4* const cand_p = a.cand + (size_t)a.row0 * a.nseg * kQuads;
     const uint32_t lane_row_off = (uint32_t)(wr * 64 + i16) * (uint32_t)a.nseg;
+
+    // candidate records through a raw buffer over this pass's record slots:
+    // a record that is not a candidate is stored at an offset past the end,
+    // which the hardware drops (no branch per quad)
+    const __amdgpu_buffer_rsrc_t rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        cand_p, (short)0, (int)((size_t)a.M * a.nseg * kQuads * 16), kRsrcWord3);
 
     // acc[vb][rb][e]: entry seg*128 + vb*16 + 4*grp + e, row wr*64 + rb*16 + i16
     auto epilogue = [&](int t) {
@@ -303,148 +340,183 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         // Opaque copies: everything derived from them is computed here, per
         // tile, instead of being hoisted out of the tile loop into registers
         // that would then live through the whole K loop.
-        int g4 = grp << 2, li16 = i16, mb = my_b, mg = my_g;
+        int g4 = grp << 2, li16 = i16, mb = my_b, mg = my_g, gq = grp;
         uint32_t lro = lane_row_off;
         uint64_t seed = my_seed;
-        asm volatile("" : "+v"(g4), "+v"(li16), "+v"(mb), "+v"(mg), "+v"(lro), "+v"(seed));
+        asm volatile("" : "+v"(g4), "+v"(li16), "+v"(mb), "+v"(mg), "+v"(gq), "+v"(lro), "+v"(seed));
         double u_mine = 0.0;
         if (a.want_draw)
             u_mine = philox_uniform(seed, a.step, (uint64_t)mb, (uint64_t)mg,
                                     3 + 256 * (uint64_t)seg);
+        const float c2 = a.c2;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
+#define Z(i) acc[(i) >> 2][rb][(i) & 3]
             const bool live = wr * 64 + rb * 16 + li16 < a.M;
             const uint32_t so = lro + (uint32_t)(rb * 16) * (uint32_t)a.nseg + (uint32_t)seg;
-            float z[32];
+            if (nvalid < kSegW) {
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb)
+                for (int i = 0; i < 32; ++i)
+                    if ((i >> 2) * 16 + g4 + (i & 3) >= nvalid) Z(i) = -INFINITY;
+            }
+            float mx = fmaxf(Z(0), Z(1));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int o = vb * 16 + g4 + e;
-                    z[vb * 4 + e] = o < nvalid ? acc[vb][rb][e] : -INFINITY;
-                }
-            float mx = z[0];
-#pragma unroll
-            for (int i = 1; i < 32; ++i) mx = fmaxf(mx, z[i]);
+            for (int i = 2; i < 32; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(Z(i), Z(i + 1)));
             mx = quad_max(mx);
 
-            // top-k candidates: theta from the lanes' TT-th largest values
+            // theta: the k-th largest of the four lanes' TT largest values (4 TT
+            // distinct entries, 4 TT >= k), a nearly tight lower bound of the
+            // segment's k-th largest entry
             float top[TT];
 #pragma unroll
             for (int q = 0; q < TT; ++q) top[q] = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
 #pragma unroll
-                for (int q = TT - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], z[i]);
-                top[0] = fmaxf(top[0], z[i]);
+                for (int q = TT - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], Z(i));
+                top[0] = fmaxf(top[0], Z(i));
             }
-            const float th = quad_min(top[TT - 1]);
-            int cnt = 0;
+            float th = -INFINITY;
+            {
+                float o16[TT], o32[TT], o48[TT];  // the lists of lanes grp^1, grp^2, grp^3
 #pragma unroll
-            for (int i = 0; i < 32; ++i) cnt += (z[i] >= th && z[i] > -INFINITY) ? 1 : 0;
-            int C;
-            int at = quad_scan(cnt, grp, C);
-            u32x2* const slot = cand_p + (size_t)so * kSlotCap;
-            if (C <= kSlotCap) {
-                if (live) {
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) {
-                        if (z[i] >= th && z[i] > -INFINITY) {
-                            u32x2 c;
-                            c[0] = __float_as_uint(z[i]);
-                            c[1] = (unsigned)(vseg + (i >> 2) * 16 + g4 + (i & 3));
-                            slot[at++] = c;
-                        }
-                    }
+                for (int q = 0; q < TT; ++q) {
+                    float lo, hi;
+                    lo_hi<32>(top[q], lo, hi);
+                    o32[q] = (gq & 2) ? lo : hi;
+                    lo_hi<16>(top[q], lo, hi);
+                    o16[q] = (gq & 1) ? lo : hi;
+                    lo_hi<16>(o32[q], lo, hi);
+                    o48[q] = (gq & 1) ? lo : hi;
                 }
-            } else {
-                // more than a slot passes the threshold (many equal values):
-                // the exact top k by k rounds of (value desc, index asc) selection
-                uint32_t taken = 0;
-                for (int r = 0; r < a.k; ++r) {
-                    float bv = -INFINITY;
-                    int bi = -1;
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) {
-                        const int ti = vseg + (i >> 2) * 16 + g4 + (i & 3);
-                        if (!((taken >> i) & 1) && z[i] > -INFINITY && ranks_ahead(z[i], ti, bv, bi)) {
-                            bv = z[i];
-                            bi = ti;
-                        }
-                    }
-                    best_swap<16>(bv, bi);
-                    best_swap<32>(bv, bi);
-                    if (live && grp == 0) {
-                        u32x2 c;
-                        c[0] = __float_as_uint(bv);
-                        c[1] = (unsigned)bi;
-                        slot[r] = c;
-                    }
-                    const int o = bi - vseg - g4;  // this lane's element, if it won
-                    if (o >= 0 && (o & 15) < 4) taken |= 1u << ((o >> 4) * 4 + (o & 3));
+                for (int q = 0; q < TT; ++q) {
+                    int c = 0;
+#pragma unroll
+                    for (int r = 0; r < TT; ++r)
+                        c += (top[r] >= top[q]) + (o16[r] >= top[q]) + (o32[r] >= top[q]) + (o48[r] >= top[q]);
+                    th = c >= a.k ? fmaxf(th, top[q]) : th;
                 }
-                C = a.k;
+                th = quad_max(th);
             }
 
-            // segment mass and the draw inside the segment (z becomes the weights)
+            // candidate quads (4 consecutive entries held by one lane): those
+            // whose largest value is >= theta, stored in (vb, grp) order
+            int qb = 0;
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                const float qm = fmaxf(fmaxf(Z(vb * 4), Z(vb * 4 + 1)), fmaxf(Z(vb * 4 + 2), Z(vb * 4 + 3)));
+                qb |= (qm >= th && qm > -INFINITY) ? (1 << vb) : 0;
+            }
+            uint32_t mask = 0;
+            {
+                int lo, hi;
+                lo_hi<16>(qb, lo, hi);
+                const int b16 = (gq & 1) ? lo : hi;
+                lo_hi<32>(qb, lo, hi);
+                const int b32 = (gq & 2) ? lo : hi;
+                lo_hi<16>(b32, lo, hi);
+                const int b48 = (gq & 1) ? lo : hi;
+                // spread each lane's 8 bits to bit vb*4 + its grp
+                auto spread = [](uint32_t x) {
+                    x = (x | (x << 12)) & 0x000F000Fu;
+                    x = (x | (x << 6)) & 0x03030303u;
+                    x = (x | (x << 3)) & 0x11111111u;
+                    return x;
+                };
+                mask = (spread((uint32_t)qb) << gq) | (spread((uint32_t)b16) << (gq ^ 1)) |
+                       (spread((uint32_t)b32) << (gq ^ 2)) | (spread((uint32_t)b48) << (gq ^ 3));
+            }
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                const int bit = vb * 4 + gq;
+                const uint32_t at = so * kQuads + (uint32_t)__builtin_popcount(mask & ((1u << bit) - 1u));
+                const bool st_ok = live && ((qb >> vb) & 1);
+                u32x4 v;
+                v[0] = __float_as_uint(Z(vb * 4));
+                v[1] = __float_as_uint(Z(vb * 4 + 1));
+                v[2] = __float_as_uint(Z(vb * 4 + 2));
+                v[3] = __float_as_uint(Z(vb * 4 + 3));
+                __builtin_amdgcn_raw_buffer_store_b128(v, rec_rsrc, st_ok ? (int)(at * 16u) : (int)0x7FFFFFF0, 0, 0);
+            }
+
+            // segment mass and the draw inside the segment (Z becomes the weights)
             float ssum = 0.f;
             int drawn = -1;
             if (a.want_exp) {
+                const float mc = mx * c2;
 #pragma unroll
-                for (int i = 0; i < 32; ++i) z[i] = fast_exp2((z[i] - mx) * a.c2);
-                float pre[8];
+                for (int i = 0; i < 32; ++i) Z(i) = fast_exp2(__builtin_fmaf(Z(i), c2, -mc));
+                float pre[8], qs[8];
                 float base = 0.f;
 #pragma unroll
                 for (int vb = 0; vb < 8; ++vb) {
-                    const float q = ((z[vb * 4] + z[vb * 4 + 1]) + z[vb * 4 + 2]) + z[vb * 4 + 3];
+                    qs[vb] = ((Z(vb * 4) + Z(vb * 4 + 1)) + Z(vb * 4 + 2)) + Z(vb * 4 + 3);
                     float tot;
-                    pre[vb] = base + quad_scan(q, grp, tot);
+                    pre[vb] = base + quad_scan(qs[vb], gq, tot);
                     base += tot;
                 }
                 ssum = base;
                 if (a.want_draw) {
                     const double u = __shfl(u_mine, li16 + 16 * rb);
                     const float tgt = (float)(u * (double)ssum);
-                    int first = kNone, last = -1;
+                    // the lane's first quad whose running sum passes the target, and
+                    // its last quad with positive mass (the fallback when rounding
+                    // leaves no crossing)
+                    int fq = -1, lq = -1;
+#pragma unroll
+                    for (int vb = 7; vb >= 0; --vb) {
+                        fq = (qs[vb] > 0.f && pre[vb] + qs[vb] > tgt) ? vb : fq;
+                        lq = (lq < 0 && qs[vb] > 0.f) ? vb : lq;
+                    }
+                    const int sq = fq >= 0 ? fq : lq;
+                    float w4[4] = {0.f, 0.f, 0.f, 0.f}, p0 = 0.f;
 #pragma unroll
                     for (int vb = 0; vb < 8; ++vb) {
-                        float cum = pre[vb];
+                        const bool on = vb == sq;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float wi = z[vb * 4 + e];
-                            const int o = vb * 16 + g4 + e;
-                            cum += wi;
-                            if (wi > 0.f) {
-                                last = o;
-                                if (cum > tgt) first = min(first, o);
-                            }
-                        }
+                        for (int e = 0; e < 4; ++e) w4[e] = on ? Z(vb * 4 + e) : w4[e];
+                        p0 = on ? pre[vb] : p0;
                     }
+                    int first = kNone, last = -1;
+                    float part = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        part = e == 0 ? w4[0] : part + w4[e];
+                        const int o = sq * 16 + g4 + e;
+                        const bool pos = w4[e] > 0.f;
+                        last = pos ? o : last;
+                        first = (fq >= 0 && pos && first == kNone && p0 + part > tgt) ? o : first;
+                    }
+                    if (sq < 0) last = -1;
                     first = quad_min(first);
                     last = quad_max(last);
                     drawn = vseg + (first != kNone ? first : last);
                 }
             }
-            if (live && grp == 0) stats_p[so] = SegStat{mx, ssum, drawn, C};
+            if (live && gq == 0) stats_p[so] = SegStat{mx, ssum, drawn, (int)mask};
+#undef Z
         }
     };
 
     // One continuous stream of stages over all tiles (stage j: tile j / nk,
     // K step j % nk), so the next tile's first stages load during an epilogue.
-    if (total > 0) {
-        issue_h(0);
-        issue_w(0);
-        if (total > 1) issue_w(1);
+    // Issue order: W(0 .. kLeadW - kLeadH - 1), then batches [h(i), W(i + kLeadW
+    // - kLeadH)]; stage j issues the batch [h(j + kLeadH), W(j + kLeadW)] into
+    // the slots that stage j - 1 used.
+    for (int i = 0; i < kLeadW - kLeadH && i < total; ++i) issue_w(i);
+    for (int i = 0; i < kLeadH; ++i) {
+        if (i < total) issue_h(i);
+        if (i + kLeadW - kLeadH < total) issue_w(i + kLeadW - kLeadH);
     }
     for (int j = 0; j < total; ++j) {
         const int t = j / nk, kk = j - t * nk;
-        // h(j) was issued right before W(j + 1); the first stage of a tile also
-        // waits for the previous epilogue's stores
-        if ((kk == 0 && j > 0) || j + 1 == total) wait_vmem<0>();
-        else wait_vmem<kLoadsPerWave>();
+        // the first stage of a tile also waits for the previous epilogue's stores
+        if ((kk == 0 && j > 0) || j + kLeadW - 1 >= total) wait_vmem<0>();
+        else wait_vmem<kWaitLoads>();
         bare_barrier();  // stage j landed for every wave; stage j - 1's slots are free
-        if (j + 1 < total) issue_h(j + 1);
-        if (j + 2 < total) issue_w(j + 2);
+        if (j + kLeadH < total) issue_h(j + kLeadH);
+        if (j + kLeadW < total) issue_w(j + kLeadW);
         const bool live = rows_live && (s0 + 2 * t + wv < s1);
         if (live) compute(j);
         if (kk == nk - 1) {
@@ -458,12 +530,14 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
 }
 
 // ------------------------------------------------------------------ finalize
+constexpr int kFinMaxSeg = 8192;  // segments per row the finalize stages in LDS
+
 struct FinArgs {
     const SegStat* stats;
-    const u32x2* cand;
+    const u32x4* cand;
     const uint64_t* seeds;
     uint64_t step;
-    int nseg, gamma, k;
+    int nseg, gamma, k, V;
     double c2;       // log2(e) / T as used by the segment sums
     int want_exp, want_draw;
     int32_t* idx;
@@ -502,18 +576,44 @@ __device__ __forceinline__ int block_min(int v, int* si) {
 }
 
 // segment j's mass relative to the row maximum mx
-__device__ __forceinline__ double seg_mass(const SegStat& s, float mx, double c2) {
-    return (double)s.s * exp2(((double)s.m - (double)mx) * c2);
+__device__ __forceinline__ double seg_mass(float s, float m, float mx, double c2) {
+    return (double)s * exp2(((double)m - (double)mx) * c2);
 }
 
+// position of the r-th (0-based) set bit of m (r < popcount(m))
+__device__ __forceinline__ int nth_set_bit(uint32_t m, int r) {
+    int pos = 0;
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1) {
+        const int c = __builtin_popcount(m & ((1u << w) - 1u));
+        if (r >= c) { r -= c; m >>= w; pos += w; }
+    }
+    return pos;
+}
+
+constexpr int kFinChunk = 8;                         // candidate segments per selection chunk
+constexpr int kFinCand = kFinChunk * kQuads * 4;     // candidate entries per chunk
+
+// One workgroup per row.
 __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a) {
+    __shared__ float s_m[kFinMaxSeg];
+    __shared__ float c_v[kFinCand + kHeadMaxK];
+    __shared__ int c_i[kFinCand + kHeadMaxK];
+    __shared__ int q_seg[kFinMaxSeg];
+    __shared__ float w_v[kHeadMaxK];
+    __shared__ int w_i[kHeadMaxK];
+    __shared__ int n_q;
     __shared__ float sv[kFinThreads / 64];
     __shared__ int si[kFinThreads / 64];
     __shared__ double sd[kFinThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t R = blockIdx.x;
     const SegStat* st = a.stats + R * a.nseg;
-    const u32x2* cd = a.cand + R * a.nseg * kSlotCap;
+    const u32x4* cd = a.cand + R * a.nseg * kQuads;
+
+    if (tid == 0) n_q = 0;
+    for (int j = tid; j < a.nseg; j += kFinThreads) s_m[j] = st[j].m;
+    __syncthreads();
 
     // tau: the k-th largest segment maximum (k rounds, each taking the best
     // segment ranked after the previous winner); -inf with fewer than k segments
@@ -523,7 +623,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
         float bv = -INFINITY;
         int bi = -1;
         for (int j = tid; j < a.nseg; j += kFinThreads) {
-            const float m = st[j].m;
+            const float m = s_m[j];
             if (ranks_ahead(pv, pi, m, j) && ranks_ahead(m, j, bv, bi)) { bv = m; bi = j; }
         }
         block_best(bv, bi, sv, si);
@@ -534,46 +634,66 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
         tau = bv;
     }
 
-    // candidates of the segments that can hold a top-k entry, kept per thread
-    // as a sorted list (value desc, index asc)
-    float lv[kHeadMaxK];
-    int li[kHeadMaxK];
+    // the segments that can hold a top-k entry (m >= tau), in any order
+    for (int j = tid; j < a.nseg; j += kFinThreads)
+        if (s_m[j] >= tau) q_seg[atomicAdd(&n_q, 1)] = j;
+    __syncthreads();
+    const int nq = n_q;
+
+    // Chunks of kFinChunk segments: every record (quad) of the chunk's
+    // segments is unpacked into LDS, then k rounds of a block-wide (value desc,
+    // index asc) selection over the chunk and the running top k (kept in the
+    // last kHeadMaxK entries) take the new top k.
+    const int k = a.k;
+    if (tid < kHeadMaxK) { c_v[kFinCand + tid] = -INFINITY; c_i[kFinCand + tid] = -1; }
+    for (int c0 = 0; c0 < nq; c0 += kFinChunk) {
+        for (int slot = tid; slot < kFinChunk * kQuads; slot += kFinThreads) {
+            const int qi = c0 + slot / kQuads, r = slot % kQuads;
+            float v4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            int i0 = -1;
+            if (qi < nq) {
+                const int j = q_seg[qi];
+                const uint32_t mask = (uint32_t)st[j].mask;
+                if (r < __builtin_popcount(mask)) {
+                    const u32x4 q = cd[(size_t)j * kQuads + r];
+                    const int bit = nth_set_bit(mask, r);
+                    i0 = j * kSegW + (bit >> 2) * 16 + (bit & 3) * 4;
 #pragma unroll
-    for (int q = 0; q < kHeadMaxK; ++q) { lv[q] = -INFINITY; li[q] = -1; }
-    for (int j = tid; j < a.nseg; j += kFinThreads) {
-        const SegStat s = st[j];
-        if (!(s.m >= tau)) continue;
-        for (int c = 0; c < s.count; ++c) {
-            const u32x2 e = cd[(size_t)j * kSlotCap + c];
-            const float v = __uint_as_float(e[0]);
-            const int i = (int)e[1];
-            if (!ranks_ahead(v, i, lv[kHeadMaxK - 1], li[kHeadMaxK - 1])) continue;
+                    for (int e = 0; e < 4; ++e)
+                        v4[e] = i0 + e < a.V ? __uint_as_float(q[e]) : -INFINITY;
+                }
+            }
 #pragma unroll
-            for (int q = kHeadMaxK - 1; q >= 0; --q) {
-                const bool above = q > 0 && ranks_ahead(v, i, lv[q - 1], li[q - 1]);
-                const bool here = ranks_ahead(v, i, lv[q], li[q]);
-                if (above) { lv[q] = lv[q - 1]; li[q] = li[q - 1]; }
-                else if (here) { lv[q] = v; li[q] = i; }
+            for (int e = 0; e < 4; ++e) {
+                c_v[slot * 4 + e] = v4[e];
+                c_i[slot * 4 + e] = v4[e] > -INFINITY ? i0 + e : -1;
             }
         }
-    }
-    int top1 = -1;
-    for (int r = 0; r < a.k; ++r) {
-        float bv = lv[0];
-        int bi = li[0];
-        block_best(bv, bi, sv, si);
-        if (tid == 0) {
-            a.idx[R * a.k + r] = bi;
-            a.val[R * a.k + r] = bv;
+        __syncthreads();
+        float qv = INFINITY;
+        int qi_ = -1;
+        for (int r = 0; r < k; ++r) {
+            float bv = -INFINITY;
+            int bi = -1;
+            for (int e = tid; e < kFinCand + k; e += kFinThreads) {  // chunk, then running top k
+                const float v = c_v[e];
+                const int i = c_i[e];
+                if (i >= 0 && ranks_ahead(qv, qi_, v, i) && ranks_ahead(v, i, bv, bi)) { bv = v; bi = i; }
+            }
+            block_best(bv, bi, sv, si);
+            if (tid == 0) { w_v[r] = bv; w_i[r] = bi; }
+            qv = bv;
+            qi_ = bi;
         }
-        if (r == 0) top1 = bi;
-        if (bi >= 0 && li[0] == bi) {
-#pragma unroll
-            for (int q = 0; q < kHeadMaxK - 1; ++q) { lv[q] = lv[q + 1]; li[q] = li[q + 1]; }
-            lv[kHeadMaxK - 1] = -INFINITY;
-            li[kHeadMaxK - 1] = -1;
-        }
+        __syncthreads();
+        if (tid < k) { c_v[kFinCand + tid] = w_v[tid]; c_i[kFinCand + tid] = w_i[tid]; }
+        __syncthreads();
     }
+    if (tid < k) {
+        a.idx[R * k + tid] = c_i[kFinCand + tid];
+        a.val[R * k + tid] = c_v[kFinCand + tid];
+    }
+    const int top1 = c_i[kFinCand];
 
     if (!a.want_exp) {
         if (tid == 0) {
@@ -586,7 +706,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     const int j0 = (int)((long)tid * a.nseg / kFinThreads);
     const int j1 = (int)((long)(tid + 1) * a.nseg / kFinThreads);
     double run = 0.0;
-    for (int j = j0; j < j1; ++j) run += seg_mass(st[j], mx, a.c2);
+    for (int j = j0; j < j1; ++j) run += seg_mass(st[j].s, s_m[j], mx, a.c2);
     const double incl = wave_inclusive_scan(run);
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = 0.0;
@@ -607,7 +727,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     int first = kNone, last = -1;
     double cum = excl;
     for (int j = j0; j < j1; ++j) {
-        const double sj = seg_mass(st[j], mx, a.c2);
+        const double sj = seg_mass(st[j].s, s_m[j], mx, a.c2);
         cum += sj;
         if (sj > 0.0) {
             last = j;
@@ -616,7 +736,8 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     }
     first = block_min(first, si);
     last = -block_min(-last, si);
-    const int J = first != kNone ? first : last;
+    int J = first != kNone ? first : last;
+    if (J < 0) J = 0;  // no positive mass (non-finite logits): any segment, never out of range
     if (tid == 0) a.draft[R] = st[J].draw;
 }
 
@@ -629,7 +750,7 @@ HeadLayout head_layout(int rows, int vocab) {
     HeadLayout L{};
     Carve c;
     L.stats = c.take<SegStat>((size_t)rows * nseg);
-    L.cand = c.take<u32x2>((size_t)rows * nseg * kSlotCap);
+    L.cand = c.take<u32x4>((size_t)rows * nseg * kQuads);
     L.bytes = c.total();
     return L;
 }
@@ -666,7 +787,8 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     if (!hidden || !w_head || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     const bool sample = temperature > 0.f;
     if (sample && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > kHeadMaxK || d_model % kHBK || (reinterpret_cast<uintptr_t>(hidden) & 15) ||
+    if (k > kHeadMaxK || d_model % kHBK || vocab > kFinMaxSeg * kSegW ||
+        (reinterpret_cast<uintptr_t>(hidden) & 15) ||
         (reinterpret_cast<uintptr_t>(w_head) & 15))
         return DFLASH_ERR_UNSUPPORTED;
     const HeadLayout L = head_layout(rows, vocab);
@@ -680,7 +802,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     ha.h = hidden;
     ha.w = w_head;
     ha.stats = reinterpret_cast<SegStat*>(ws + L.stats);
-    ha.cand = reinterpret_cast<u32x2*>(ws + L.cand);
+    ha.cand = reinterpret_cast<u32x4*>(ws + L.cand);
     ha.seeds = seeds;
     ha.step = step;
     ha.d = d_model;
@@ -695,7 +817,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     for (int row0 = 0; row0 < rows; row0 += kHeadRows) {
         ha.row0 = row0;
         ha.M = min(kHeadRows, rows - row0);
-        launch_head((k + 3) / 4, dim3(ha.groups), ha, st);
+        launch_head(min(4, (k + 1) / 2), dim3(ha.groups), ha, st);
         const int rc = launch_status();
         if (rc) return rc;
     }
@@ -707,6 +829,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     fa.nseg = nseg;
     fa.gamma = gamma;
     fa.k = k;
+    fa.V = vocab;
     fa.c2 = (double)ha.c2;
     fa.want_exp = ha.want_exp;
     fa.want_draw = ha.want_draw;

@@ -211,3 +211,7 @@ def test_lm_head_validation():
     assert head() == -4
     assert dfl.dflash_lm_head_topk_workspace_size(256, 5120, 151936, 8) > 0
     assert dfl.dflash_lm_head_topk_workspace_size(0, 5120, 151936, 8) == 0
+
+
+def test_lm_head_vocab_limit():
+    assert head(V=1048577) == -3
