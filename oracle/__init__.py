@@ -26,6 +26,9 @@ What each function follows (pages cited by title and section):
   model" (H_t equation and the context half of K_i, V_i).
 * ``position_weights`` -- "DFlash vs DFlash 2", "Training with anchors"
   (w_k equation).
+* ``top_p_mask`` -- "Beam 1.0 DFlash2" model card, "Evaluation" (sampled
+  runs use temperature 0.7 and top-p 0.99): the nucleus of softmax(z/T)
+  kept, everything else masked to -inf.
 * ``lm_head_topk`` -- "Beam 1.0 DFlash2" model card, "Model" (the drafter
   reuses the target's LM head) and "DFlash vs DFlash 2", "The candidate
   selector" (top-k per position); the draft draw is exact softmax sampling
@@ -96,6 +99,7 @@ def _load():
         "orc_two_tap_conv": (c_int, [_D, _D, c_int, c_int, c_int, c_int, _D]),
         "orc_lm_head_topk": (c_int, [_U16, _U16, _I64, c_int, c_int, c_i64, c_int, c_int, c_dbl,
                                      _U64, c_u64, _I64, _D, _D, _I64, _D]),
+        "orc_top_p_mask": (c_int, [_D, c_i64, c_i64, c_dbl, c_dbl, _D, _I64]),
         "orc_num_threads": (c_int, []),
         "orc_set_num_threads": (None, [c_int]),
     }
@@ -238,6 +242,20 @@ def lm_head_topk(h_bits, w_bits, gamma, k, temperature, seeds=None, step=0, row_
                               _ptr(z, _D))
     _check(rc, "lm_head_topk")
     return {"idx": idx, "val": val, "lse": lse, "draft": draft, "z": z}
+
+
+def top_p_mask(z, temperature, top_p):
+    """z [..., V] -> (z with the entries outside each row's top-p nucleus set to -inf,
+    nucleus sizes [...])."""
+    lib = _load()
+    z = _f64(z)
+    V = z.shape[-1]
+    rows = int(np.prod(z.shape[:-1])) if z.ndim > 1 else 1
+    out = np.empty_like(z)
+    kept = np.zeros(z.shape[:-1] if z.ndim > 1 else (1,), dtype=np.int64)
+    _check(lib.orc_top_p_mask(_ptr(z, _D), rows, V, float(temperature), float(top_p),
+                              _ptr(out, _D), _ptr(kept, _I64)), "top_p_mask")
+    return out, kept
 
 
 # ------------------------------------------------------------------------ verify

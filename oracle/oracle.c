@@ -351,6 +351,56 @@ int orc_lm_head_topk(const uint16_t* h, const uint16_t* w, const int64_t* row_id
 }
 
 /* ------------------------------------------------------------------------ */
+/* Top-p (nucleus) truncation of a logits row.                               */
+/* [P2] "Evaluation": sampled runs use temperature 0.7 and top-p 0.99.       */
+/* [P3] "The problem: one expensive token at a time": verification keeps    */
+/* the output distribution equal to the target's, so with top-p the target  */
+/* distribution is the truncated one, and so is the drafter's proposal.     */
+/* Reading: the nucleus of softmax(z/T) is the shortest prefix, in the order */
+/* (logit descending, index ascending), whose probability reaches top_p;   */
+/* the truncated distribution renormalises it.  Masking the logits outside  */
+/* the nucleus to -inf gives exactly that distribution under softmax(z/T),  */
+/* so the unchanged draws and verification run on the masked rows.          */
+/* top_p >= 1 keeps every entry.                                              */
+/* z [rows, V] -> z_out [rows, V] (may equal z); kept [rows] (may be NULL):  */
+/* the nucleus size.                                                          */
+/* ------------------------------------------------------------------------ */
+int orc_top_p_mask(const double* z, int64_t rows, int64_t V, double T, double top_p,
+                   double* z_out, int64_t* kept)
+{
+    if (rows < 0 || V < 1 || !(T > 0.0) || !(top_p > 0.0)) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* zr = z + r * V;
+        double* out = z_out + r * V;
+        zi_t* t = (zi_t*)malloc(sizeof(zi_t) * (size_t)V);
+        if (!t) { bad = 1; continue; }
+        double m = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) if (zr[v] / T > m) m = zr[v] / T;
+        /* probabilities by definition: exponentials, then the total */
+        double S = 0.0;
+        for (int64_t v = 0; v < V; ++v) S += exp(zr[v] / T - m);
+        for (int64_t v = 0; v < V; ++v) { t[v].z = zr[v]; t[v].i = v; }
+        qsort(t, (size_t)V, sizeof(zi_t), cmp_desc_then_index);
+        int64_t K = V;
+        if (top_p < 1.0) {
+            double c = 0.0;
+            for (int64_t j = 0; j < V; ++j) {
+                c += exp(t[j].z / T - m) / S;
+                if (c >= top_p) { K = j + 1; break; }
+            }
+        }
+        if (kept) kept[r] = K;
+        /* copy first (z_out may alias z), then mask the entries ranked after K */
+        for (int64_t v = 0; v < V; ++v) out[v] = zr[v];
+        for (int64_t j = K; j < V; ++j) out[t[j].i] = -INFINITY;
+        free(t);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Verification.                                                              */
 /* [P3] "The problem: one expensive token at a time": the target scores the  */
 /* whole block in one pass, keeps the longest valid prefix and corrects the  */
