@@ -22,7 +22,9 @@ inside the timed region, and the CPU oracle timed on a bounded sample.  Also
 reported: the same throughput with one attention layer instead of five, the
 512-row fusion call, the candidate selector's walk and the verification of its
 deterministic drafts, one two-tap dynamic convolution, the drafter's LM head
-with the top-k epilogue fused in (beside the unfused GEMM + top-k route), a
+with the top-k epilogue fused in (beside the unfused GEMM + top-k route),
+sampled decoding with top-p 0.99 (nucleus masking, then the draws and the
+verification on the masked rows), a
 device-copy bandwidth (context for the 8 TB/s peak) and the oracle on a single
 host thread.
 """
@@ -330,6 +332,55 @@ def lm_head_figure(dev, warmup, steps):
     return res
 
 
+def top_p_figure(wl, dev, warmup, steps, top_p=0.99):
+    """NEXT row: sampled decoding with top-p 0.99 (the pages' sampled setting) at the
+    step's batch and block: both logits tensors masked to their nuclei
+    (dflash_top_p_mask, 256 + 256 rows), then the draws and verification on the
+    masked rows.  Timed with HIP events on the launching stream."""
+    stream = torch.cuda.current_stream()
+    mt = torch.empty_like(wl["zt"])
+    md = torch.empty_like(wl["zd"])
+
+    def mask():
+        dfl.dflash_top_p_mask(wl["zt"], T, top_p, out=mt, stream=stream)
+        dfl.dflash_top_p_mask(wl["zd"], T, top_p, out=md, stream=stream)
+
+    def draw():
+        dfl.dflash_topk(md, TOPK, T, seeds=wl["seeds"], step=0, outputs=wl["topk_out"],
+                        workspace=wl["ws_topk"], stream=stream)
+
+    def verify():
+        dfl.spec_verify(mt, md, wl["topk_out"]["draft"], T, seeds=wl["seeds"], step=0,
+                        draft_lse=wl["topk_out"]["lse"], outputs=wl["verify_out"],
+                        workspace=wl["ws_verify"], stream=stream)
+
+    def timed(fn, n):
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    mask()
+    draw()
+    res = {"top_p": top_p, "temperature": T, "mask_512_rows_us": round(timed(mask, steps), 2),
+           "topk_masked_us": round(timed(draw, steps), 2),
+           "verify_masked_us": round(timed(verify, steps), 2)}
+    _, kept = dfl.dflash_top_p_mask(wl["zt"], T, top_p, want_kept=True, stream=stream)
+    torch.cuda.synchronize()
+    res["mean_nucleus_target"] = round(float(kept.float().mean()), 1)
+    res["mean_tau"] = round(wl["verify_out"]["accept_len"].float().mean().item() + 1.0, 3)
+    row_bytes = 2 * B * G * V * 4
+    res["mask_read_passes_equiv"] = round(res["mask_512_rows_us"] * 1e-6 * HBM_PEAK_GBS * 1e9 / row_bytes, 2)
+    del mt, md
+    return res
+
+
 def copy_probe():
     """Three copies of 2^28 fp32 (1 GiB read + 1 GiB written each): the
     calibration kernel for the HBM byte counters."""
@@ -412,12 +463,23 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=B,
                     help="sequences of the workload the CPU oracle baseline runs on "
                          "(default: all of them, i.e. the whole step)")
+    ap.add_argument("--lm-head-probe", action="store_true",
+                    help="only run dflash_lm_head_topk three times at the step's 256 rows "
+                         "(the LM head's counter passes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.lm_head_probe:
+        dev = torch.device("cuda:0")
+        h, w = syn.lm_head_inputs(B * G, D_MODEL, V, SEED, device=dev)
+        seeds = syn.philox_seeds(B, 0, device=dev)
+        for _ in range(3):
+            dfl.dflash_lm_head_topk(h, w, G, TOPK, T, seeds=seeds)
+        torch.cuda.synchronize()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -466,6 +528,7 @@ def main():
     selector = selector_figure(wl, dev, args.warmup, args.steps)
     conv = conv_figure(dev, args.warmup, args.steps)
     head = lm_head_figure(dev, args.warmup, args.steps)
+    topp = top_p_figure(wl, dev, args.warmup, args.steps)
     copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
@@ -516,6 +579,7 @@ def main():
         "candidate_selector": selector,
         "two_tap_conv": conv,
         "lm_head_topk": head,
+        "top_p_sampled": topp,
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
     }

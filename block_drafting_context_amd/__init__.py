@@ -22,6 +22,7 @@ __all__ = [
     "dflash_context_fuse", "dflash_context_fuse_workspace_size",
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk", "dflash_lm_head_topk_workspace_size",
+    "dflash_top_p_mask",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "dflash_context_fuse_workspace_size", "dflash_context_fuse",
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk_workspace_size", "dflash_lm_head_topk",
+    "dflash_top_p_mask",
 )
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
@@ -76,6 +78,7 @@ def load():
         "dflash_select_path": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
         "dflash_two_tap_conv": (_i, [_vp] * 3 + [_i] * 4 + [_vp]),
         "dflash_lm_head_topk_workspace_size": (_sz, [_i] * 4),
+        "dflash_top_p_mask": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
         "dflash_lm_head_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp]),
     }
@@ -272,6 +275,22 @@ def dflash_two_tap_conv(x, kern, y=None, stream=None):
     _need(y, "y", torch.bfloat16, (B, G, D), dev)
     _call("dflash_two_tap_conv", _ptr(x), _ptr(kern), _ptr(y), B, G, D, n_groups, _stream(stream))
     return y
+
+
+# ---------------------------------------------------------------------- top-p
+def dflash_top_p_mask(logits, temperature, top_p, out=None, want_kept=False, stream=None):
+    """logits [..., V] fp32 -> (rows with the entries outside each row's top-p nucleus
+    set to -inf, nucleus sizes [...] int32 or None).  out=logits masks in place."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    dev = logits.device
+    _need(logits, "logits", torch.float32, None, dev)
+    out = out if out is not None else torch.empty_like(logits)
+    _need(out, "out", torch.float32, tuple(logits.shape), dev)
+    kept = torch.empty(logits.shape[:-1], dtype=torch.int32, device=dev) if want_kept else None
+    _call("dflash_top_p_mask", _ptr(logits), _ptr(out), _ptr(kept), rows, V, float(temperature),
+          float(top_p), _stream(stream))
+    return out, kept
 
 
 # -------------------------------------------------------------------- LM head

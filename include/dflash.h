@@ -13,6 +13,8 @@
  *   dflash_select_path   the candidate selector's walk through the top-k
  *                        candidates of each block position.
  *   dflash_two_tap_conv  the two-tap dynamic convolution inside a block.
+ *   dflash_top_p_mask    top-p (nucleus) truncation of logits rows, for
+ *                        sampling and verifying with top-p.
  *   dflash_lm_head_topk  the drafter's LM head with top-k, log-normaliser and
  *                        drafted token computed in the GEMM epilogue (the
  *                        logits never reach memory).
@@ -324,6 +326,31 @@ int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows
                         const uint64_t* seeds, uint64_t step, int32_t* topk_idx,
                         float* topk_val, double* lse, int32_t* draft, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dflash_top_p_mask -- top-p (nucleus) truncation of logits rows.
+ *
+ * "Beam 1.0 DFlash2" model card, "Evaluation": sampled runs use temperature
+ * 0.7 and top-p 0.99.  The nucleus of softmax(z / T) is the shortest prefix of
+ * the row, in the order (logit descending, index ascending), whose
+ * probability reaches top_p; every entry outside it is set to -inf.  Then
+ * softmax(z / T) of the masked row is the renormalised truncation, and
+ * dflash_topk (drafter rows) and spec_verify (target and drafter rows) run on
+ * masked rows sample and verify top-p decoding losslessly ("DFlash vs DFlash
+ * 2", "The problem: one expensive token at a time").
+ *
+ *   logits [rows, vocab] float32 (finite or -inf)
+ *   out    [rows, vocab] float32; may equal logits (in place: only the masked
+ *          entries are written)
+ *   kept   [rows] int32 or NULL: the nucleus size of each row
+ *   temperature > 0; 0 < top_p <= 1 (top_p == 1 keeps every entry)
+ * Accuracy: weights 2^((z - max) log2(e)/T) in fp32, summed exactly in fixed
+ * point (2^-40 of the maximum's weight); the nucleus boundary is exact up to
+ * that rounding of the cumulative mass.
+ * No workspace; one workgroup per row.
+ * ------------------------------------------------------------------------ */
+int dflash_top_p_mask(const float* logits, float* out, int32_t* kept, int rows, int vocab,
+                      float temperature, float top_p, void* stream);
 
 #ifdef __cplusplus
 }

@@ -215,3 +215,23 @@ def test_lm_head_validation():
 
 def test_lm_head_vocab_limit():
     assert head(V=1048577) == -3
+
+
+def topp(**kw):
+    a = dict(z=P, out=P, kept=None, rows=4, V=151936, T=0.7, p=0.99, st=None)
+    a.update(kw)
+    return dfl.load().dflash_top_p_mask(a["z"], a["out"], a["kept"], a["rows"], a["V"], a["T"],
+                                        a["p"], a["st"])
+
+
+def test_top_p_validation():
+    assert topp(rows=0) == 0
+    assert topp(rows=-1) == -2
+    assert topp(V=0) == -2
+    assert topp(T=0.0) == -2
+    assert topp(T=float("inf")) == -2
+    assert topp(p=0.0) == -2
+    assert topp(p=1.5) == -2
+    assert topp(p=float("nan")) == -2
+    assert topp(z=None) == -1
+    assert topp(out=None) == -1
