@@ -9,7 +9,7 @@
 // ("DFlash vs DFlash 2", "The problem: one expensive token at a time": the
 // committed tokens follow the target's distribution, here the truncated one).
 //
-// One 1,024-thread workgroup per row; the row is streamed a few times:
+// One 512-thread workgroup per row (two per CU); the row is streamed a few times:
 //   A  row maximum m;
 //   B  a histogram of the entries' masses over 4,096 bins of
 //      x = (m - z) log2(e)/T (64 bins per unit of log2 weight; the last bin
@@ -17,11 +17,11 @@
 //      so the bin where the cumulative mass (from the top) reaches top_p of the
 //      total holds the nucleus boundary.  Masses are fixed point (2^-40 of the
 //      maximum's weight) added with integer atomics: exact and order free;
-//   C  the entries of that bin (at most 2,048; more are narrowed down first by
-//      histograms over successive 12-bit digits of the 64-bit rank key
-//      (ordered logit, inverted index), one pass each) are gathered into LDS
-//      and the boundary entry is found by counting, for every gathered entry,
-//      the mass of the gathered entries ranked at or ahead of it;
+//   C  the entries of that bin are gathered into LDS (if there are more than
+//      2,048, histograms over successive 12-bit digits of the 64-bit rank key
+//      (ordered logit, inverted index), one pass each, narrow the set and it is
+//      gathered again) and the boundary entry is found by counting, for every
+//      gathered entry, the mass of the gathered entries ranked at or ahead of it;
 //   D  every entry ranked after the boundary is written as -inf.
 #include <cmath>
 
@@ -30,7 +30,7 @@
 namespace dfl {
 namespace {
 
-constexpr int kPThreads = 1024;
+constexpr int kPThreads = 512;
 constexpr int kPBins = 4096;
 constexpr float kPBinsPerUnit = 64.f;   // bins per unit of log2 weight below the maximum
 constexpr int kPCap = 2048;             // entries gathered for the final count
@@ -78,50 +78,54 @@ __device__ __forceinline__ T block_reduce(T v, T* red, Op op) {
 
 __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     __shared__ unsigned long long h_mass[kPBins];
-    __shared__ unsigned int h_cnt[kPBins];
     __shared__ unsigned long long g_key[kPCap];
-    __shared__ unsigned long long g_w[kPCap];
+    __shared__ unsigned long long g_w[kPCap];  // also the digit counts while narrowing
     __shared__ float red_f[kPThreads / 64];
     __shared__ unsigned long long red_u[kPThreads / 64];
     __shared__ unsigned long long s_before, s_prefix;
     __shared__ int s_bin, s_n;
+    static_assert(sizeof(g_w) >= kPBins * sizeof(unsigned int), "digit counts fit");
+    unsigned int* const h_cnt = reinterpret_cast<unsigned int*>(g_w);
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t R = blockIdx.x;
     const float* z = a.z + R * a.V;
     float* out = a.out + R * a.V;
     const int V = a.V;
     const float c2 = a.c2;
-
-    // A: the row maximum
-    float m = -INFINITY;
-    for (int v = tid; v < V; v += kPThreads) m = fmaxf(m, z[v]);
-    m = block_reduce(m, red_f, [](float x, float y) { return fmaxf(x, y); });
-
-    unsigned long long cut = 0;  // rank key of the last kept entry (0: keep everything)
-    if (a.top_p < 1.0 && m != -INFINITY) {
-        // B: bin masses and counts
-        for (int b = tid; b < kPBins; b += kPThreads) { h_mass[b] = 0; h_cnt[b] = 0; }
-        __syncthreads();
-        for (int v = tid; v < V; v += kPThreads) {
-            const float x = z[v];
-            const int b = bin_of(x, m, c2);
-            atomicAdd(&h_mass[b], (unsigned long long)weight_fx(x, m, c2));
-            atomicAdd(&h_cnt[b], 1u);
-        }
-        __syncthreads();
-        // the bin where the cumulative mass from the top reaches top_p of the total
-        constexpr int kPer = kPBins / kPThreads;
-        unsigned long long mine = 0;
+    const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    // fn(logit, index) for every entry of the row (16-byte loads when aligned)
+    auto each = [&](auto&& fn) {
+        if (vec) {
+            // four 16-byte loads in flight per thread before any is used
+            const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
+            const int V4 = V >> 2;
+            int i = tid;
+            for (; i + 3 * kPThreads < V4; i += 4 * kPThreads) {
+                f32x4 q[4];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) mine += h_mass[tid * kPer + i];
-        const unsigned long long total =
-            block_reduce(mine, red_u, [](unsigned long long x, unsigned long long y) { return x + y; });
-        const unsigned long long target = (unsigned long long)ceil(a.top_p * (double)total);
-        if (tid == 0) { s_bin = kPBins - 1; s_before = 0; }
-        // exclusive prefix of `mine` over threads (wave scan, then waves)
+                for (int u = 0; u < 4; ++u) q[u] = z4[i + u * kPThreads];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int b = 4 * (i + u * kPThreads);
+                    fn(q[u][0], b); fn(q[u][1], b + 1); fn(q[u][2], b + 2); fn(q[u][3], b + 3);
+                }
+            }
+            for (; i < V4; i += kPThreads) {
+                const f32x4 q = z4[i];
+                fn(q[0], 4 * i); fn(q[1], 4 * i + 1); fn(q[2], 4 * i + 2); fn(q[3], 4 * i + 3);
+            }
+        } else {
+            for (int v = tid; v < V; v += kPThreads) fn(z[v], v);
+        }
+    };
+    auto block_sum_u = [&](unsigned long long v) {
+        return block_reduce(v, red_u, [](unsigned long long x, unsigned long long y) { return x + y; });
+    };
+    // exclusive prefix over threads of `mine` (ascending thread order)
+    auto thread_prefix = [&](unsigned long long mine) {
         unsigned long long incl = mine;
-        const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const unsigned long long t = __shfl_up(incl, o);
@@ -132,6 +136,32 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
         __syncthreads();
         unsigned long long before = incl - mine;
         for (int w = 0; w < wave; ++w) before += red_u[w];
+        return before;
+    };
+
+    // A: the row maximum
+    float m = -INFINITY;
+    each([&](float x, int) { m = fmaxf(m, x); });
+    m = block_reduce(m, red_f, [](float x, float y) { return fmaxf(x, y); });
+
+    unsigned long long cut = 0;  // rank key of the last kept entry (0: keep everything)
+    if (a.top_p < 1.0 && m != -INFINITY) {
+        // B: bin masses
+        for (int b = tid; b < kPBins; b += kPThreads) h_mass[b] = 0;
+        __syncthreads();
+        each([&](float x, int) {
+            atomicAdd(&h_mass[bin_of(x, m, c2)], (unsigned long long)weight_fx(x, m, c2));
+        });
+        __syncthreads();
+        // the bin where the cumulative mass from the top reaches top_p of the total
+        constexpr int kPer = kPBins / kPThreads;
+        unsigned long long mine = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) mine += h_mass[tid * kPer + i];
+        const unsigned long long total = block_sum_u(mine);
+        const unsigned long long target = (unsigned long long)ceil(a.top_p * (double)total);
+        if (tid == 0) { s_bin = kPBins - 1; s_before = 0; s_prefix = 0; }
+        const unsigned long long before = thread_prefix(mine);
         if (before < target && before + mine >= target) {
             unsigned long long c = before;
             for (int i = 0; i < kPer; ++i) {
@@ -140,7 +170,6 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
                 c += h_mass[b];
             }
         }
-        if (tid == 0) s_prefix = 0;
         __syncthreads();
         const int bstar = s_bin;
         // the candidate set: bin bstar and, after `level` narrowing steps, the
@@ -153,38 +182,45 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
         };
         int level = 0;
         unsigned long long prefix = 0;
-        unsigned int count = h_cnt[bstar];
-        // narrow the set to at most kPCap entries, 12 bits of the rank key at a time
-        while (count > (unsigned)kPCap && level < 6) {  // 6 digits cover the 64-bit key
+        // C: gather the set (every pass counts it; entries beyond kPCap are dropped)
+        auto gather = [&]() {
+            __syncthreads();
+            if (tid == 0) s_n = 0;
+            __syncthreads();
+            each([&](float x, int v) {
+                const uint64_t key = rank_key(x, v);
+                if (in_set(key, bin_of(x, m, c2), level, prefix)) {
+                    const int at = atomicAdd(&s_n, 1);
+                    if (at < kPCap) {
+                        g_key[at] = key;
+                        g_w[at] = weight_fx(x, m, c2);
+                    }
+                }
+            });
+            __syncthreads();
+            return s_n;
+        };
+        int count = gather();
+        // more than kPCap: narrow the set, 12 bits of the rank key at a time, then gather again
+        while (count > kPCap && level < 6) {  // 6 digits cover the 64-bit key
             const int sh = 64 - 12 * (level + 1);  // digit = bits [sh, sh + 12)
             __syncthreads();
             for (int b = tid; b < kPBins; b += kPThreads) { h_mass[b] = 0; h_cnt[b] = 0; }
             __syncthreads();
-            for (int v = tid; v < V; v += kPThreads) {
-                const float x = z[v];
+            each([&](float x, int v) {
                 const uint64_t key = rank_key(x, v);
-                if (!in_set(key, bin_of(x, m, c2), level, prefix)) continue;
+                if (!in_set(key, bin_of(x, m, c2), level, prefix)) return;
                 const int d = sh >= 0 ? (int)((key >> sh) & 0xFFF) : (int)((key << -sh) & 0xFFF);
                 atomicAdd(&h_mass[kPBins - 1 - d], (unsigned long long)weight_fx(x, m, c2));
                 atomicAdd(&h_cnt[kPBins - 1 - d], 1u);
-            }
+            });
             __syncthreads();
             const unsigned long long sb = s_before;  // read by every thread before the winner rewrites it
             // digits in descending order = bins in ascending order
             unsigned long long mine2 = 0;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) mine2 += h_mass[tid * kPer + i];
-            unsigned long long inc2 = mine2;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const unsigned long long t = __shfl_up(inc2, o);
-                if (lane >= o) inc2 += t;
-            }
-            __syncthreads();
-            if (lane == 63) red_u[wave] = inc2;
-            __syncthreads();
-            unsigned long long bef2 = sb + inc2 - mine2;
-            for (int w = 0; w < wave; ++w) bef2 += red_u[w];
+            const unsigned long long bef2 = sb + thread_prefix(mine2);
             if (bef2 < target && bef2 + mine2 >= target) {
                 unsigned long long c = bef2;
                 for (int i = 0; i < kPer; ++i) {
@@ -193,7 +229,6 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
                         const uint64_t d = (uint64_t)(kPBins - 1 - b);
                         s_prefix = sh >= 0 ? (prefix | (d << sh)) : (prefix | (d >> -sh));
                         s_before = c;
-                        s_n = (int)h_cnt[b];
                         break;
                     }
                     c += h_mass[b];
@@ -201,30 +236,17 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
             }
             __syncthreads();
             prefix = s_prefix;
-            count = (unsigned)s_n;
             ++level;
+            count = gather();
         }
-        // C: gather the set and find the entry where the mass reaches the target
-        if (tid == 0) s_n = 0;
-        __syncthreads();
-        for (int v = tid; v < V; v += kPThreads) {
-            const float x = z[v];
-            const uint64_t key = rank_key(x, v);
-            if (in_set(key, bin_of(x, m, c2), level, prefix)) {
-                const int at = atomicAdd(&s_n, 1);
-                if (at < kPCap) {
-                    g_key[at] = key;
-                    g_w[at] = weight_fx(x, m, c2);
-                }
-            }
-        }
-        __syncthreads();
-        const int n = min(s_n, kPCap);
+        // the entry where the mass reaches the target: for every gathered entry,
+        // the mass of the gathered entries ranked at or ahead of it
+        const int n = min(count, kPCap);
         const unsigned long long need = target - s_before;  // > 0
         unsigned long long best = 0;
         for (int i = tid; i < n; i += kPThreads) {
             const uint64_t ki = g_key[i];
-            unsigned long long ge = 0;  // mass of the gathered entries ranked at or ahead of i
+            unsigned long long ge = 0;
             for (int j = 0; j < n; ++j) ge += g_key[j] >= ki ? g_w[j] : 0ull;
             if (ge >= need && ki > best) best = ki;
         }
@@ -232,12 +254,30 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     }
     // D: mask everything ranked after the cut
     unsigned int kept = 0;
-    for (int v = tid; v < V; v += kPThreads) {
-        const float x = z[v];
-        const bool keep = cut == 0 || rank_key(x, v) >= cut;
-        kept += keep ? 1u : 0u;
-        if (!keep) out[v] = -INFINITY;
-        else if (out != z) out[v] = x;
+    const bool inplace = out == z;
+    if (vec) {
+        const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
+        f32x4* o4 = reinterpret_cast<f32x4*>(out);
+        for (int i = tid; i < (V >> 2); i += kPThreads) {
+            f32x4 q = z4[i];
+            bool any_masked = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool keep = cut == 0 || rank_key(q[e], 4 * i + e) >= cut;
+                kept += keep ? 1u : 0u;
+                any_masked |= !keep;
+                q[e] = keep ? q[e] : -INFINITY;
+            }
+            if (!inplace || any_masked) o4[i] = q;
+        }
+    } else {
+        for (int v = tid; v < V; v += kPThreads) {
+            const float x = z[v];
+            const bool keep = cut == 0 || rank_key(x, v) >= cut;
+            kept += keep ? 1u : 0u;
+            if (!keep) out[v] = -INFINITY;
+            else if (!inplace) out[v] = x;
+        }
     }
     if (a.kept) {
         kept = block_reduce(kept, (unsigned int*)red_f, [](unsigned int x, unsigned int y) { return x + y; });
