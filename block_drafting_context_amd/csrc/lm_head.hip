@@ -70,6 +70,7 @@ constexpr int kLoadsPerWave = kTileV * kHRowB / 1024 / kHWaves;  // 1 KB DMA ins
 constexpr int kWaitLoads = kLoadsPerWave + (kLeadH - 1) * 2 * kLoadsPerWave;
 constexpr int kQuads = kSegW / 4;     // quads of 4 entries per segment: candidate record slots
 constexpr int kHeadMaxK = 16;
+constexpr int kHeadMaxD = 65536;     // keeps a tile's byte offsets (256 rows x d x 2 B) in 32 bits
 constexpr int kHeadCUs = 256;
 constexpr int kFinThreads = 256;
 constexpr int kNone = INT_MAX;
@@ -230,16 +231,18 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
     const int i16 = lane & 15, grp = lane >> 4;
     const int rl = lane / kChunks, pc = lane % kChunks;  // DMA: row within an instruction, physical chunk
 
-    // DMA: a buffer resource for the tile's weight rows or the pass's hidden
-    // rows, a per-lane byte offset (row, swizzled chunk) and the stage's K
-    // offset as the scalar offset.  Rows beyond the tile or the pass read a
-    // valid row (never used).
+    // DMA: a buffer resource over exactly the tile's weight rows or the pass's
+    // hidden rows, a per-lane byte offset (row, swizzled chunk) and the stage's
+    // K offset as the scalar offset.  Rows beyond the tile or the pass fall
+    // outside the resource, so the hardware skips their reads (they still
+    // count as issued loads, which keeps every wave's wait counts the same);
+    // what their LDS rows hold only reaches outputs that are never stored
+    // (rows >= M) or entries the epilogue replaces by -inf (>= V).
     uint32_t h_off[kLoadsPerWave];
 #pragma unroll
     for (int ins = 0; ins < kLoadsPerWave; ++ins) {
         const int r = (wave * kLoadsPerWave + ins) * kRowsPerIns + rl;
-        const int m = r < a.M ? r : a.M - 1;
-        h_off[ins] = (uint32_t)m * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
+        h_off[ins] = (uint32_t)r * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
     }
     const i32x4 h_rsrc = byte_buffer(a.h + (size_t)a.row0 * a.d, (uint32_t)(a.M * a.d * 2));
     // K step kk of a tile is read at byte offset kbyte(kk): each workgroup
@@ -258,8 +261,7 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
 #pragma unroll
         for (int ins = 0; ins < kLoadsPerWave; ++ins) {
             const int r = (wave * kLoadsPerWave + ins) * kRowsPerIns + rl;
-            const int rr = r < nv ? r : nv - 1;
-            const uint32_t voff = (uint32_t)rr * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
+            const uint32_t voff = (uint32_t)r * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
             dma16<true>(lds + ins * 1024, voff, rsrc, kbyte(kk));
         }
     };
@@ -787,7 +789,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     if (!hidden || !w_head || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     const bool sample = temperature > 0.f;
     if (sample && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > kHeadMaxK || d_model % kHBK || vocab > kFinMaxSeg * kSegW ||
+    if (k > kHeadMaxK || d_model % kHBK || d_model > kHeadMaxD || vocab > kFinMaxSeg * kSegW ||
         (reinterpret_cast<uintptr_t>(hidden) & 15) ||
         (reinterpret_cast<uintptr_t>(w_head) & 15))
         return DFLASH_ERR_UNSUPPORTED;

@@ -315,7 +315,8 @@ int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int b
  *   seeds    [rows / gamma rounded up] uint64 (device); may be NULL when
  *            T == 0 or draft == NULL.
  * Work: the weights are streamed from HBM once per 256 rows of hidden.
- * Supported: 1 <= k <= 16, k <= vocab <= 1,048,576, d_model % 64 == 0.
+ * Supported: 1 <= k <= 16, k <= vocab <= 1,048,576, d_model % 64 == 0,
+ * d_model <= 65,536 (DFLASH_ERR_UNSUPPORTED otherwise).
  * Accuracy: bf16 products, fp32 accumulation (the GEMM); fp32 exponentials
  * and segment sums, fp64 across segments.
  * Workspace: dflash_lm_head_topk_workspace_size bytes, 256-byte aligned.

@@ -217,6 +217,10 @@ def test_lm_head_vocab_limit():
     assert head(V=1048577) == -3
 
 
+def test_lm_head_d_model_limit():
+    assert head(d=65536 + 64) == -3
+
+
 def topp(**kw):
     a = dict(z=P, out=P, kept=None, rows=4, V=151936, T=0.7, p=0.99, st=None)
     a.update(kw)

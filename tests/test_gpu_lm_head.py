@@ -157,6 +157,33 @@ def test_more_rows_than_one_pass():
     run_case(h, w, 6, 8, 1.0, seeds=syn.philox_seeds(50, 9), step=2, what="300 rows")
 
 
+def test_uneven_segment_runs():
+    """547 segments over 256 workgroups: runs of 2 and 3 segments (a 3-segment
+    run ends in a half tile), the last segment ragged.  Planted maxima in the
+    upper vocabulary and in the ragged segment put top-k entries there."""
+    h, w = syn.lm_head_inputs(40, 256, 70000, seed=8)
+    w = w.clone()
+    w[66000:66006] = w[66000:66006] * 3
+    w[69950:69953] = w[69950:69953] * 3        # inside the ragged last segment
+    run_case(h, w, 8, 8, 0.7, seeds=syn.philox_seeds(5, 3), step=4,
+             check_rows=[0, 7, 20, 39], what="uneven runs")
+    run_case(h, w, 8, 16, 0.0, check_rows=[1, 38], what="uneven runs greedy")
+
+
+def test_long_segment_runs():
+    """911 segments over 256 workgroups: runs of 3 and 4 segments."""
+    h, w = syn.lm_head_inputs(16, 128, 116600, seed=9)
+    run_case(h, w, 8, 8, 0.9, seeds=syn.philox_seeds(2, 4), check_rows=[0, 9, 15],
+             what="long runs")
+
+
+def test_uneven_runs_over_two_passes():
+    """300 rows (two passes over the weights) with uneven segment runs."""
+    h, w = syn.lm_head_inputs(300, 128, 70000, seed=10)
+    run_case(h, w, 6, 8, 1.0, seeds=syn.philox_seeds(50, 1), step=1,
+             check_rows=[0, 1, 255, 256, 299], what="uneven runs, 300 rows")
+
+
 def test_few_rows():
     h, w = syn.lm_head_inputs(8, 512, 4096, seed=5)
     run_case(h, w, 8, 8, 0.7, seeds=syn.philox_seeds(1, 0), what="8 rows")
