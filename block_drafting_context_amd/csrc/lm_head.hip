@@ -22,12 +22,13 @@
 //   * m = max z and s = sum 2^((z - m) log2(e)/T);
 //   * the entry drawn inside the segment: inverse CDF of its weights in
 //     vocabulary order at the uniform of purpose 3 + 256 * segment;
-//   * top-k candidates: theta = the k-th largest of the four lanes' TT largest
-//     values (TT = min(4, ceil(k/2)), 4 TT >= k distinct entries), a lower
-//     bound of the segment's k-th largest entry; every quad of 4 consecutive
-//     entries (one lane's registers) holding a value >= theta is written whole
-//     to the segment's record slots, in order, with a 32-bit mask of which
-//     quads they are (ties need no special case: all of them are written).
+//   * top-k candidates: theta = a lower bound of the k-th largest of the
+//     segment's 32 quad maxima (quad: 4 consecutive entries in one lane's
+//     registers), taken from the four lanes' TT largest quad maxima (TT =
+//     min(4, ceil(k/2)), 4 TT >= k), hence of the segment's k-th largest
+//     entry; every quad whose maximum is >= theta is written whole to the
+//     segment's record slots, in order, with a 32-bit mask of which quads they
+//     are (ties need no special case: all of them are written).
 // A finalize kernel per row takes tau = the k-th largest segment maximum
 // (every top-k entry is >= tau, so only segments with m >= tau are read),
 // merges their records, adds the segment masses in fp64 for the
@@ -361,22 +362,29 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
                 for (int i = 0; i < 32; ++i)
                     if ((i >> 2) * 16 + g4 + (i & 3) >= nvalid) Z(i) = -INFINITY;
             }
-            float mx = fmaxf(Z(0), Z(1));
+            // quad maxima: the largest of the 4 consecutive entries a lane holds
+            float qm[8];
 #pragma unroll
-            for (int i = 2; i < 32; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(Z(i), Z(i + 1)));
+            for (int vb = 0; vb < 8; ++vb)
+                qm[vb] = fmaxf(fmaxf(Z(vb * 4), Z(vb * 4 + 1)), fmaxf(Z(vb * 4 + 2), Z(vb * 4 + 3)));
+            float mx = fmaxf(fmaxf(fmaxf(qm[0], qm[1]), fmaxf(qm[2], qm[3])),
+                             fmaxf(fmaxf(qm[4], qm[5]), fmaxf(qm[6], qm[7])));
             mx = quad_max(mx);
 
-            // theta: the k-th largest of the four lanes' TT largest values (4 TT
-            // distinct entries, 4 TT >= k), a nearly tight lower bound of the
-            // segment's k-th largest entry
+            // theta: a lower bound of the k-th largest of the segment's 32 quad
+            // maxima, hence of its k-th largest entry.  Each lane keeps its TT
+            // largest quad maxima (sorted); a value x of that list has at least
+            // (its rank + 1) entries >= x in its own list, and the three other
+            // lanes' lists are counted exactly; theta is the largest list value
+            // with at least k counted (4 TT >= k, so the smallest qualifies).
             float top[TT];
 #pragma unroll
             for (int q = 0; q < TT; ++q) top[q] = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int vb = 0; vb < 8; ++vb) {
 #pragma unroll
-                for (int q = TT - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], Z(i));
-                top[0] = fmaxf(top[0], Z(i));
+                for (int q = TT - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], qm[vb]);
+                top[0] = fmaxf(top[0], qm[vb]);
             }
             float th = -INFINITY;
             {
@@ -393,23 +401,20 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
                 }
 #pragma unroll
                 for (int q = 0; q < TT; ++q) {
-                    int c = 0;
+                    int c = q + 1;
 #pragma unroll
                     for (int r = 0; r < TT; ++r)
-                        c += (top[r] >= top[q]) + (o16[r] >= top[q]) + (o32[r] >= top[q]) + (o48[r] >= top[q]);
+                        c += (o16[r] >= top[q]) + (o32[r] >= top[q]) + (o48[r] >= top[q]);
                     th = c >= a.k ? fmaxf(th, top[q]) : th;
                 }
-                th = quad_max(th);
+                th = quad_max(th);  // the lanes' bounds may differ: all take the largest
             }
 
             // candidate quads (4 consecutive entries held by one lane): those
-            // whose largest value is >= theta, stored in (vb, grp) order
+            // whose maximum is >= theta, stored in (vb, grp) order
             int qb = 0;
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb) {
-                const float qm = fmaxf(fmaxf(Z(vb * 4), Z(vb * 4 + 1)), fmaxf(Z(vb * 4 + 2), Z(vb * 4 + 3)));
-                qb |= (qm >= th && qm > -INFINITY) ? (1 << vb) : 0;
-            }
+            for (int vb = 0; vb < 8; ++vb) qb |= (qm[vb] >= th && qm[vb] > -INFINITY) ? (1 << vb) : 0;
             uint32_t mask = 0;
             {
                 int lo, hi;
