@@ -28,6 +28,8 @@
 namespace dfl {
 namespace {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kSeg = 2048;             // elements per segment (8 x 64 lanes x 4)
 constexpr int kIters = kSeg / 256;     // float4 loads per lane per segment
 constexpr int kCap = 256;              // top-k candidate buffer fill that triggers a rebuild
@@ -133,8 +135,8 @@ template <int MODE>
 __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
     __shared__ float s_lv[kScanWaves][64];
     __shared__ int s_li[kScanWaves][64];
-    __shared__ float s_bv[kScanWaves][kBuf];
-    __shared__ int s_bi[kScanWaves][kBuf];
+    __shared__ __attribute__((aligned(16))) float s_bv[kScanWaves][kBuf];
+    __shared__ __attribute__((aligned(16))) int s_bi[kScanWaves][kBuf];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kScanWaves + wave;
@@ -207,23 +209,25 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
             if (ballot(lane_m >= tk.tv)) {
 #pragma unroll
                 for (int it = 0; it < kIters; ++it) {
-                    // skip a load group in which no lane holds a candidate
-                    if (!ballot(gmax[it] >= tk.tv)) continue;
+                    // a lane whose 4 elements of this load group include one that
+                    // can pass the filter appends all 4 (16-byte LDS writes, one
+                    // ballot per group); the rebuild ranks them exactly, and
+                    // elements past the row's end go in as empties (-inf, -1)
+                    const bool pass = gmax[it] >= tk.tv;
+                    const uint64_t mask = ballot(pass);
+                    if (mask) {
+                        if (pass) {
+                            const int pos = tk.cnt + 4 * lanes_below(mask);
+                            const int idx = base + it * 256;
+                            i32x4 ii;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int idx = base + it * 256 + c;
-                        const bool pass = idx < a.V && ranks_ahead(v[it][c], idx, tk.tv, tk.ti);
-                        const uint64_t mask = ballot(pass);
-                        if (mask) {
-                            if (pass) {
-                                const int pos = tk.cnt + lanes_below(mask);
-                                s_bv[wave][pos] = v[it][c];
-                                s_bi[wave][pos] = idx;
-                            }
-                            tk.cnt += __popcll(mask);
+                            for (int c = 0; c < 4; ++c) ii[c] = idx + c < a.V ? idx + c : -1;
+                            *reinterpret_cast<f32x4*>(&s_bv[wave][pos]) = v[it];
+                            *reinterpret_cast<i32x4*>(&s_bi[wave][pos]) = ii;
                         }
+                        tk.cnt += 4 * __popcll(mask);
+                        if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
                     }
-                    if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
                 }
             }
         }
