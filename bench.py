@@ -16,9 +16,11 @@ resident in HBM before timing: context lengths uniform in [512, 131072]
 (attention reads min(len, 4096) ring rows + 8 block rows), bf16 Q/K/V ~
 N(0,1)/sqrt(128), target logits ~ N(0, 2^2), drafter = target + N(0, 1).
 
-Prints one JSON line: drafted tokens/s (value), the roofline of the dominant
-kernel (block attention, HBM-bound) measured with HIP events on its stream
-inside the timed region, and the CPU oracle timed on a bounded sample.  Also
+Prints one JSON line: drafted tokens/s (value: K steps back to back between
+two HIP events), the roofline of the dominant kernel (block attention,
+HBM-bound) from HIP events on its stream around each of its launches in a
+second pass of K steps (the per-operation breakdown comes from the same pass),
+and the CPU oracle timed on a bounded sample.  Also
 reported: the same throughput with one attention layer instead of five, the
 512-row fusion call, the candidate selector's walk and the verification of its
 deterministic drafts, one two-tap dynamic convolution, the drafter's LM head
@@ -103,32 +105,35 @@ def build_workload(dev):
 OPS = ["context_fuse"] + [f"block_attn_l{i}" for i in range(LAYERS)] + ["topk", "spec_verify"]
 
 
-def run_step(wl, step, stream, events=None):
+def run_step(wl, step, stream, events=None, attn_events=None):
     """One pass of the path; if `events` is a list, a HIP event is recorded on
-    `stream` before every operation and after the last one."""
-    def mark():
-        if events is not None:
+    `stream` before every operation and after the last one; if `attn_events`
+    is a list, one before the first attention layer and one after the last."""
+    def mark(lst):
+        if lst is not None:
             e = torch.cuda.Event(enable_timing=True)
             e.record(stream)
-            events.append(e)
+            lst.append(e)
     fz = wl["fuse"]
-    mark()
+    mark(events)
     dfl.dflash_context_fuse(fz["x"], fz["w_c"], fz["gain"], 1e-6, fz["w_kv"], wl["row_seq"],
                             wl["row_pos"], wl["ring"], N_TAPS, workspace=wl["ws_fuse"],
                             stream=stream)
+    mark(attn_events)
     for i, L in enumerate(wl["layers"]):
-        mark()
+        mark(events)
         dfl.dflash_block_attn(L["q"], L["k_blk"], L["v_blk"], wl["ring"][i, 0], wl["ring"][i, 1],
                               wl["ctx_len"], 1 / np.sqrt(D), out=L["out"], workspace=wl["ws_attn"],
                               stream=stream)
-    mark()
+    mark(attn_events)
+    mark(events)
     tk = dfl.dflash_topk(wl["zd"], TOPK, T, seeds=wl["seeds"], step=step, outputs=wl["topk_out"],
                          workspace=wl["ws_topk"], stream=stream)
-    mark()
+    mark(events)
     dfl.spec_verify(wl["zt"], wl["zd"], tk["draft"], T, seeds=wl["seeds"], step=step,
                     draft_lse=tk["lse"], outputs=wl["verify_out"], workspace=wl["ws_verify"],
                     stream=stream)
-    mark()
+    mark(events)
 
 
 def algorithmic_bytes(ctx_len):
@@ -505,23 +510,42 @@ def main():
         run_step(wl, s, stream)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
+    # the timed region: K steps back to back, one HIP event before and one after
+    # (an event recorded between two kernels delays the second by a few us)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(args.steps):
+        run_step(wl, args.warmup + s, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    # per-operation durations (breakdown, roofline): K more steps with an event
+    # on the stream around every operation
+    log(f"[bench] per-operation timing {args.steps} steps")
     events = []
     for s in range(args.steps):
-        run_step(wl, args.warmup + s, stream, events)
+        run_step(wl, args.warmup + args.steps + s, stream, events)
     torch.cuda.synchronize()
     nops = len(OPS)
     per = np.zeros((args.steps, nops))
     for s in range(args.steps):
         for o in range(nops):
             per[s, o] = events[s * (nops + 1) + o].elapsed_time(events[s * (nops + 1) + o + 1])
-    total_ms = events[0].elapsed_time(events[-1])
-    ms_step = total_ms / args.steps
+    ms_step_events = events[0].elapsed_time(events[-1]) / args.steps
+    # the attention launches' average duration (roofline): K more steps with an
+    # event only before the first and after the last of the back-to-back layers
+    aev = []
+    for s in range(args.steps):
+        run_step(wl, args.warmup + 2 * args.steps + s, stream, attn_events=aev)
+    torch.cuda.synchronize()
+    attn_us = float(np.mean([aev[2 * s].elapsed_time(aev[2 * s + 1]) for s in range(args.steps)])
+                    * 1e3 / LAYERS)
     drafted = B * (G - 1)
     value = drafted * args.steps / (total_ms / 1e3)
 
     ab = algorithmic_bytes(wl["ctx_len"].cpu().numpy())
     op_us = {name: float(per[:, o].mean() * 1e3) for o, name in enumerate(OPS)}
-    attn_us = float(per[:, 1:1 + LAYERS].mean() * 1e3)
     achieved = ab["block_attn"] / (attn_us * 1e-6) / 1e9
     step_bytes = ab["context_fuse"] + LAYERS * ab["block_attn"] + ab["topk"] + ab["spec_verify"]
     kernel_src = os.path.join(HERE, "block_drafting_context_amd", "csrc", "block_attn.hip")
@@ -572,6 +596,8 @@ def main():
             "avg_launch_us": round(attn_us, 2),
         },
         "breakdown_us": {k: round(v, 2) for k, v in op_us.items()},
+        "breakdown_timing": "a second pass of the same K steps with a HIP event around every "
+                            f"operation ({ms_step_events:.4f} ms per step with the events)",
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "attn_topk_verify_tok_s": round(drafted / ((LAYERS * attn_us + op_us["topk"] +
                                                     op_us["spec_verify"]) * 1e-6), 1),
