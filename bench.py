@@ -26,9 +26,9 @@ reported: the same throughput with one attention layer instead of five, the
 deterministic drafts, one two-tap dynamic convolution, the drafter's LM head
 with the top-k epilogue fused in (beside the unfused GEMM + top-k route),
 sampled decoding with top-p 0.99 (nucleus masking, then the draws and the
-verification on the masked rows), a
-device-copy bandwidth (context for the 8 TB/s peak) and the oracle on a single
-host thread.
+verification on the masked rows), the step's logits taken literally from the
+tiny workload (vocabulary 1,024, top-4), a device-copy bandwidth (context for
+the 8 TB/s peak) and the oracle on a single host thread.
 """
 from __future__ import annotations
 
@@ -337,6 +337,43 @@ def lm_head_figure(dev, warmup, steps):
     return res
 
 
+def literal_vocab_figure(wl, dev, warmup, steps, attn_us, vocab=1024, k=4):
+    """The step's logits taken literally from the tiny workload (vocabulary 1,024,
+    top-4; target N(0, 2^2), drafter + N(0, 1), T = 0.7 sampled) with the same
+    five attention layers: top-k and verification timed with HIP events."""
+    stream = torch.cuda.current_stream()
+    zt, zd = syn.logits_pair(B, G, vocab, 2.0, 1.0, SEED + 100, device=dev)
+    ws_t = torch.empty(dfl.dflash_topk_workspace_size(B, G, vocab, k), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(dfl.spec_verify_workspace_size(B, G, vocab), dtype=torch.uint8, device=dev)
+    out_t = {"idx": torch.empty((B, G, k), dtype=torch.int32, device=dev),
+             "val": torch.empty((B, G, k), dtype=torch.float32, device=dev),
+             "lse": torch.empty((B, G), dtype=torch.float64, device=dev),
+             "draft": torch.empty((B, G), dtype=torch.int32, device=dev)}
+    out_v = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+             "out_tokens": torch.empty((B, G), dtype=torch.int32, device=dev),
+             "accepted": torch.empty((B, G - 1), dtype=torch.uint8, device=dev)}
+
+    def run():
+        dfl.dflash_topk(zd, k, T, seeds=wl["seeds"], step=0, outputs=out_t, workspace=ws_t,
+                        stream=stream)
+        dfl.spec_verify(zt, zd, out_t["draft"], T, seeds=wl["seeds"], step=0,
+                        draft_lse=out_t["lse"], outputs=out_v, workspace=ws_v, stream=stream)
+
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tv_us = e0.elapsed_time(e1) / steps * 1e3
+    return {"vocab": vocab, "top_k": k, "topk_plus_verify_us": round(tv_us, 2),
+            "attn_topk_verify_tok_s": round(B * (G - 1) / ((LAYERS * attn_us + tv_us) * 1e-6), 1),
+            "mean_tau": round(out_v["accept_len"].float().mean().item() + 1.0, 3)}
+
+
 def top_p_figure(wl, dev, warmup, steps, top_p=0.99):
     """NEXT row: sampled decoding with top-p 0.99 (the pages' sampled setting) at the
     step's batch and block: both logits tensors masked to their nuclei
@@ -398,6 +435,17 @@ def copy_probe():
     log("[bench] copy probe: 3 x 1 GiB copied")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, n_seq, min_seconds=0.0):
     """The fp64 oracle, as it stands, on `n_seq` sequences of the same workload:
     their 8 fused rows, 5 attention layers, top-k/draws and sampled verify
@@ -427,7 +475,7 @@ def cpu_baseline(wl, n_seq, min_seconds=0.0):
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(done * n_seq * (G - 1) / dt, 3), "unit": "drafted tokens/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{done} pass(es) over {n_seq} of {B} sequences of the step (each: fuse its "
                       f"8 rows, 5 attention layers, top-8 + draws, sampled verify), {dt:.1f} s"}
 
@@ -557,6 +605,7 @@ def main():
     conv = conv_figure(dev, args.warmup, args.steps)
     head = lm_head_figure(dev, args.warmup, args.steps)
     topp = top_p_figure(wl, dev, args.warmup, args.steps)
+    lit = literal_vocab_figure(wl, dev, args.warmup, args.steps, attn_us)
     copy_gbs = copy_bandwidth(dev)
 
     log("[bench] cpu baseline")
@@ -610,6 +659,7 @@ def main():
         "two_tap_conv": conv,
         "lm_head_topk": head,
         "top_p_sampled": topp,
+        "literal_vocab_1024_top4": lit,
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
     }
