@@ -13,14 +13,19 @@
 // segment, holds all 32 of each lane's elements in registers (8 float4
 // loads issued together), so it can take an exact wave-uniform segment
 // maximum m_s before exponentiating.  Per segment it can produce
-//   * s_s = sum 2^((z - m_s) * log2(e)/T)   (fp32 pairwise sums, fp64 across)
-//   * the wave's argmax, or
-//   * top-k candidates: elements beating the wave's running k-th best are
-//     compacted into an LDS buffer; the list is rebuilt by k rounds of a
-//     wave-wide (value desc, index asc) reduction when the buffer fills.
-// An inverse-CDF draw then needs only the segment sums plus one re-read of
-// the single 2,048-element segment holding the crossing, recomputing the
-// element weights with exactly the arithmetic that produced the sums.
+//   * m_s, and s_s = sum 2^((z - m_s) * log2(e)/T)   (fp32 pairwise sums,
+//     fp64 across), or
+//   * the wave's argmax.
+// Top-k needs only the segment maxima from the streaming pass: tau = the k-th
+// largest m_s of the row (counting repeats) is a lower bound of the row's k-th
+// largest entry, since those k maxima are k distinct entries, so every top-k
+// entry lies in a segment with m_s >= tau.  The finalize re-reads just those
+// segments (about k of them) with tau as the first filter: entries that can
+// still rank are compacted into an LDS buffer, whose list is rebuilt by k
+// rounds of a wave-wide (value desc, index asc) reduction when it fills.
+// An inverse-CDF draw needs only the segment sums plus one re-read of the
+// single 2,048-element segment holding the crossing, recomputing the element
+// weights with exactly the arithmetic that produced the sums.
 #include <cmath>
 
 #include "common.hpp"
@@ -34,19 +39,21 @@ constexpr int kSeg = 2048;             // elements per segment (8 x 64 lanes x 4
 constexpr int kIters = kSeg / 256;     // float4 loads per lane per segment
 constexpr int kCap = 256;              // top-k candidate buffer fill that triggers a rebuild
 constexpr int kBuf = kCap + 256;       // buffer size: one load group (4 x 64) of slack
-constexpr int kMaxCand = 4096;         // candidates merged per row by the finalize
 constexpr int kScanWaves = 4;          // waves per workgroup
+constexpr int kFinWaves = 4;           // waves per top-k finalize workgroup (one row)
 constexpr int kTargetWaves = 3072;     // waves per row-scan launch (~12 per CU)
+constexpr int kRsrcWord3 = 0x00020000; // buffer resource word 3 for raw byte buffers on gfx9 parts
+constexpr int kMaxVocab = 1 << 29;     // a row's bytes, and a segment past it, fit 32-bit offsets
 
-enum : int { kArgmax = 1, kSumExp = 2, kTopK = 4 };
+enum : int { kArgmax = 1, kSumExp = 2, kSegMax = 4 };
 
 struct ScanArgs {
     const float* z;  // [rows, V]
-    int rows, V, nseg, spw, wpr, k;
+    int rows, V, nseg, spw, wpr;
     float c2;        // log2(e) / T
     float* seg_m;    // [rows][nseg]
     double* seg_s;   // [rows][nseg]
-    float* cand_v;   // [rows][wpr][k]
+    float* cand_v;   // [rows][wpr]: each wave's argmax
     int* cand_i;
 };
 
@@ -72,15 +79,15 @@ constexpr int kNPL = (64 + kBuf + 63) / 64;  // candidates per lane in a rebuild
 struct TopKRegs {
     int cnt;     // buffer fill (wave-uniform)
     int lcount;  // list length (wave-uniform)
-    float tv;    // filter: an element passes if it ranks ahead of (tv, ti)
-    int ti;
+    float tv;    // filter: a quad is appended when its maximum is >= tv
 };
 
 // Rebuild the sorted list of `wave` from list + buffer: k rounds of a
 // wave-wide (value desc, index asc) reduction.
+// Entries below `floor` are known not to rank, so the filter never drops under it.
 __device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (*li)[64],
                                              float (*bv)[kBuf], int (*bi)[kBuf], int wave, int k,
-                                             int lane) {
+                                             int lane, float floor) {
     wave_lds_sync();
     const int N = s.lcount + s.cnt;
     float cv[kNPL];
@@ -95,7 +102,6 @@ __device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (
     wave_lds_sync();
     const int newcount = N < k ? N : k;
     float lastv = -INFINITY;
-    int lasti = -1;
     for (int r = 0; r < newcount; ++r) {
         float b_v = cv[0];
         int b_i = ci[0];
@@ -108,36 +114,15 @@ __device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (
             if (ci[e] == b_i && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
         if (lane == 0) { lv[wave][r] = b_v; li[wave][r] = b_i; }
         lastv = b_v;
-        lasti = b_i;
     }
     wave_lds_sync();
     s.lcount = newcount;
     s.cnt = 0;
-    if (newcount == k) { s.tv = lastv; s.ti = lasti; }
-    else { s.tv = -INFINITY; s.ti = -1; }
-}
-
-// k-th largest of the 64 lane values (k <= 64): a safe first filter, since
-// k distinct elements are at least that large.
-__device__ __forceinline__ float kth_of_lanes(float v, int k, int lane) {
-    float kth = -INFINITY;
-    for (int r = 0; r < k; ++r) {
-        float b_v = v;
-        int b_i = lane;
-        wave_best(b_v, b_i);
-        if (lane == b_i) v = -INFINITY;
-        kth = b_v;
-    }
-    return kth;
+    s.tv = newcount == k ? fmaxf(lastv, floor) : floor;
 }
 
 template <int MODE>
 __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
-    __shared__ float s_lv[kScanWaves][64];
-    __shared__ int s_li[kScanWaves][64];
-    __shared__ __attribute__((aligned(16))) float s_bv[kScanWaves][kBuf];
-    __shared__ __attribute__((aligned(16))) int s_bi[kScanWaves][kBuf];
-
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kScanWaves + wave;
     const int row = gw / a.wpr, wr = gw % a.wpr;
@@ -148,21 +133,32 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
 
     float best_v = -INFINITY;
     int best_i = -1;
-    TopKRegs tk{0, 0, -INFINITY, -1};
 
-    // the 32 elements of this lane in segment `seg`: base + it*256 + c
+    // The 32 elements of this lane in segment `seg`: base + it*256 + c.  The
+    // row is read through a raw buffer of V*4 bytes, so every load is issued
+    // unconditionally: a quad past the row's end (V % 4 == 0, so quads are
+    // whole) or of a segment past this wave's run reads as zeros without
+    // touching memory, and the compiler counts the loads in flight exactly
+    // (with the loads in branches it waited for all of them, the next
+    // segment's prefetch included, before processing the current one).
+    const __amdgpu_buffer_rsrc_t zr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(zr), (short)0, a.V * 4, kRsrcWord3);
     auto load = [&](f32x4 (&vv)[kIters], int seg) {
-        const int base = seg * kSeg + 4 * lane;
+        const uint32_t base = (uint32_t)(seg * kSeg + 4 * lane) * 4u;  // < 2^32: V <= 2^29
 #pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int e = base + it * 256;
-            const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int it = 0; it < kIters; ++it)
             // logits rows are streamed once: non-temporal loads
-            vv[it] = e < a.V ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zr + e)) : ninf;
-        }
+            vv[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  zr_rsrc, (int)(base + it * 1024u), 0, kLoadStream));
     };
-    auto process = [&](const f32x4 (&v)[kIters], int seg) {
+    auto process = [&](f32x4 (&v)[kIters], int seg) {
         const int base = seg * kSeg + 4 * lane;
+        if (seg * kSeg + kSeg > a.V) {
+            // quads past the row's end read as zeros: they take no part
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+                if (base + it * 256 >= a.V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
         if (MODE & kArgmax) {
 #pragma unroll
             for (int it = 0; it < kIters; ++it)
@@ -170,14 +166,15 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                 for (int c = 0; c < 4; ++c)
                     if (v[it][c] > best_v) { best_v = v[it][c]; best_i = base + it * 256 + c; }
         }
-        float gmax[kIters];
         float lane_m = -INFINITY;
-        if (MODE & (kSumExp | kTopK)) {
+        if (MODE & (kSumExp | kSegMax)) {
 #pragma unroll
-            for (int it = 0; it < kIters; ++it) {
-                gmax[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3]));
-                lane_m = fmaxf(lane_m, gmax[it]);
-            }
+            for (int it = 0; it < kIters; ++it)
+                lane_m = fmaxf(lane_m, fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3])));
+        }
+        if (MODE & kSegMax) {
+            const float m = wave_max(lane_m);
+            if (lane == 0) a.seg_m[(size_t)row * a.nseg + seg] = m;
         }
         if (MODE & kSumExp) {
             const float m = wave_max(lane_m);
@@ -201,61 +198,26 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                 a.seg_s[(size_t)row * a.nseg + seg] = sacc;
             }
         }
-        if (MODE & kTopK) {
-            if (tk.lcount == 0 && tk.cnt == 0) {
-                tk.tv = kth_of_lanes(lane_m, a.k, lane);
-                tk.ti = -1;  // ties with the filter value pass
-            }
-            if (ballot(lane_m >= tk.tv)) {
-#pragma unroll
-                for (int it = 0; it < kIters; ++it) {
-                    // a lane whose 4 elements of this load group include one that
-                    // can pass the filter appends all 4 (16-byte LDS writes, one
-                    // ballot per group); the rebuild ranks them exactly, and
-                    // elements past the row's end go in as empties (-inf, -1)
-                    const bool pass = gmax[it] >= tk.tv;
-                    const uint64_t mask = ballot(pass);
-                    if (mask) {
-                        if (pass) {
-                            const int pos = tk.cnt + 4 * lanes_below(mask);
-                            const int idx = base + it * 256;
-                            i32x4 ii;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) ii[c] = idx + c < a.V ? idx + c : -1;
-                            *reinterpret_cast<f32x4*>(&s_bv[wave][pos]) = v[it];
-                            *reinterpret_cast<i32x4*>(&s_bi[wave][pos]) = ii;
-                        }
-                        tk.cnt += 4 * __popcll(mask);
-                        if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
-                    }
-                }
-            }
-        }
     };
 
-    // two segments per trip, each one's loads issued before the other is processed
+    // two segments per trip, each one's loads issued before the other is
+    // processed; a segment past the run is loaded from past the row's end
+    const int dead = a.nseg;
     f32x4 va[kIters], vb[kIters];
-    if (seg0 < seg1) load(va, seg0);
+    load(va, seg0 < seg1 ? seg0 : dead);
     for (int seg = seg0; seg < seg1; seg += 2) {
         const bool has_b = seg + 1 < seg1;
-        if (has_b) load(vb, seg + 1);
+        load(vb, has_b ? seg + 1 : dead);
         process(va, seg);
-        if (has_b) {
-            if (seg + 2 < seg1) load(va, seg + 2);
-            process(vb, seg + 1);
-        }
+        load(va, seg + 2 < seg1 ? seg + 2 : dead);
+        if (has_b) process(vb, seg + 1);
     }
 
-    const size_t cbase = ((size_t)row * a.wpr + wr) * a.k;
     if (MODE & kArgmax) {
         wave_best(best_v, best_i);
-        if (lane == 0) { a.cand_v[cbase] = best_v; a.cand_i[cbase] = best_i; }
-    }
-    if (MODE & kTopK) {
-        if (tk.cnt > 0 || tk.lcount < a.k) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane);
-        if (lane < a.k) {
-            a.cand_v[cbase + lane] = lane < tk.lcount ? s_lv[wave][lane] : -INFINITY;
-            a.cand_i[cbase + lane] = lane < tk.lcount ? s_li[wave][lane] : -1;
+        if (lane == 0) {
+            a.cand_v[(size_t)row * a.wpr + wr] = best_v;
+            a.cand_i[(size_t)row * a.wpr + wr] = best_i;
         }
     }
 }
@@ -391,68 +353,275 @@ __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const fl
 // ------------------------------------------------------- top-k finalize
 struct TopKFin {
     const float* z;
-    int B, G, V, nseg, wpr, k;
+    int B, G, V, nseg, k;
     float T, c2;
     const uint64_t* seeds;
     uint64_t step;
     const float* seg_m;
     const double* seg_s;
-    const float* cand_v;
-    const int* cand_i;
     int32_t* topk_idx;
     float* topk_val;
     double* lse;
     int32_t* draft;
 };
 
-// One row per workgroup of two waves: wave 0 merges the waves' candidate
-// lists into the row's top-k (k rounds of a wave-wide reduction over LDS);
-// wave 1 merges the segment statistics into the log-normaliser and draws the
-// drafted token (T > 0).
-__global__ void __launch_bounds__(128) topk_finalize_kernel(TopKFin a) {
-    __shared__ float cv[kMaxCand];
-    __shared__ int ci[kMaxCand];
-    const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int b = row / a.G, r = row % a.G;
-    if (wave == 1) {
-        if (a.T == 0.f) return;
-        float M;
-        double S;
-        const float* sm = a.seg_m + (size_t)row * a.nseg;
-        const double* ss = a.seg_s + (size_t)row * a.nseg;
-        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
-        if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
-        if (a.draft) {
-            const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
-            const int tok = draw_softmax_row(a.z + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M,
-                                             S, u, lane);
-            if (lane == 0) a.draft[row] = tok;
+constexpr int kSegCache = 4;  // segment maxima per lane held in registers by the finalize
+
+// The k-th largest of a row's segment maxima, counting repeats; -inf when
+// fewer than k of them are above -inf.  Each round takes the largest maximum
+// below the previous one and counts its copies, so at most k rounds.  The
+// first 64 * kSegCache maxima come from registers (c), the rest from memory.
+__device__ __forceinline__ float kth_segment_max(const float (&c)[kSegCache], const float* sm, int nseg,
+                                                 int k, int lane) {
+    float t = INFINITY;
+    int counted = 0;
+    for (;;) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kSegCache; ++j)
+            if (c[j] < t) m = fmaxf(m, c[j]);
+        for (int s = 64 * kSegCache + lane; s < nseg; s += 64) {
+            const float x = sm[s];
+            if (x < t) m = fmaxf(m, x);
         }
-        return;
+        m = wave_max(m);
+        if (m == -INFINITY) return -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kSegCache; ++j) counted += __popcll(ballot(c[j] == m));
+        for (int s0 = 64 * kSegCache; s0 < nseg; s0 += 64)
+            counted += __popcll(ballot(s0 + lane < nseg && sm[s0 + lane] == m));
+        if (counted >= k) return m;
+        t = m;
     }
-    const int N = a.wpr * a.k;
-    const float* src_v = a.cand_v + (size_t)row * N;
-    const int* src_i = a.cand_i + (size_t)row * N;
-    for (int e = lane; e < N; e += 64) { cv[e] = src_v[e]; ci[e] = src_i[e]; }
-    wave_lds_sync();
-    for (int rr = 0; rr < a.k; ++rr) {
-        float bv = -INFINITY;
-        int bi = -1, bpos = -1;
-        for (int e = lane; e < N; e += 64)
-            if (ranks_ahead(cv[e], ci[e], bv, bi)) { bv = cv[e]; bi = ci[e]; bpos = e; }
-        float wv = bv;
-        int wi = bi;
-        wave_best(wv, wi);
-        if (bi == wi && bpos >= 0 && wi != -1) { cv[bpos] = -INFINITY; ci[bpos] = -1; }
-        wave_lds_sync();
-        if (lane == 0) {
-            a.topk_idx[(size_t)row * a.k + rr] = wi;
-            a.topk_val[(size_t)row * a.k + rr] = wv;
-            if (rr == 0 && a.T == 0.f) {
-                if (a.lse) a.lse[row] = NAN;
-                if (a.draft) a.draft[row] = wi;
+}
+
+// One row per workgroup of five waves.  Waves 0-3 find tau; the segments with
+// m_s >= tau are dealt to them in index order (the i-th such segment to wave
+// i mod 4), and each re-reads its segments (two in flight) and keeps a top-k
+// list over the quads whose maximum passes its filter (tau, raised to the
+// wave's own k-th best once it holds k entries).  Meanwhile, at T > 0, wave 4
+// merges the segment statistics into the log-normaliser and draws the drafted
+// token.  Wave 0 then merges the four lists into the row's top-k.
+__global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(TopKFin a) {
+    __shared__ float s_lv[kFinWaves][64];
+    __shared__ int s_li[kFinWaves][64];
+    __shared__ __attribute__((aligned(16))) float s_bv[kFinWaves][kBuf];
+    __shared__ __attribute__((aligned(16))) int s_bi[kFinWaves][kBuf];
+    __shared__ int s_len[kFinWaves], s_lc[kFinWaves];
+    const int row = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b = row / a.G, r = row % a.G;
+    const float* sm = a.seg_m + (size_t)row * a.nseg;
+    const float* zr = a.z + (size_t)row * a.V;
+
+    TopKRegs tk{0, 0, -INFINITY};
+    float tau = -INFINITY;
+    if (wave == kFinWaves) {
+        if (a.T > 0.f) {
+            float M;
+            double S;
+            const double* ss = a.seg_s + (size_t)row * a.nseg;
+            merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+            if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
+            if (a.draft) {
+                const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
+                const int tok = draw_softmax_row(zr, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+                if (lane == 0) a.draft[row] = tok;
             }
         }
+    } else {
+        float cache[kSegCache];
+#pragma unroll
+        for (int j = 0; j < kSegCache; ++j) {
+            const int sj = 64 * j + lane;
+            cache[j] = sj < a.nseg ? sm[sj] : -INFINITY;
+        }
+        tau = kth_segment_max(cache, sm, a.nseg, a.k, lane);
+
+        const __amdgpu_buffer_rsrc_t zr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(zr), (short)0, a.V * 4, kRsrcWord3);
+        auto load = [&](f32x4 (&v)[kIters], int seg) {
+            const uint32_t base = (uint32_t)(seg * kSeg + 4 * lane) * 4u;  // < 2^32: V <= 2^29
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+                v[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     zr_rsrc, (int)(base + it * 1024u), 0, kLoadStream));
+        };
+        tk.tv = tau;
+        // a lane whose 4 elements of load group `it` include one that can pass
+        // the filter appends all 4 (16-byte LDS writes); the rebuild ranks
+        // them exactly, and elements past the row's end go in as empties
+        auto append = [&](const f32x4& q, bool pass, uint64_t mask, int idx) {
+            if (pass) {
+                const int pos = tk.cnt + 4 * lanes_below(mask);
+                i32x4 ii;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ii[c] = idx + c < a.V ? idx + c : -1;
+                *reinterpret_cast<f32x4*>(&s_bv[wave][pos]) = q;
+                *reinterpret_cast<i32x4*>(&s_bi[wave][pos]) = ii;
+            }
+            tk.cnt += 4 * __popcll(mask);
+        };
+        auto process = [&](f32x4 (&v)[kIters], int seg) {
+            const int base = seg * kSeg + 4 * lane;
+            bool pass[kIters];
+            uint64_t mask[kIters];
+            int total = 0;
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) {
+                // quads past the row's end read as zeros: they take no part
+                if (base + it * 256 >= a.V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                pass[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3])) >= tk.tv;
+                mask[it] = ballot(pass[it]);
+                total += __popcll(mask[it]);
+            }
+            if (!total) return;
+            if (tk.cnt + 4 * total <= kBuf) {
+                // the whole segment's quads fit: append, then rebuild once
+#pragma unroll
+                for (int it = 0; it < kIters; ++it)
+                    if (mask[it]) append(v[it], pass[it], mask[it], base + it * 256);
+                if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane, tau);
+                return;
+            }
+            // many passing quads (e.g. long runs of equal logits): one load
+            // group at a time, rebuilding whenever the buffer fills
+#pragma unroll 1
+            for (int it = 0; it < kIters; ++it) {
+                f32x4 q = v[0];
+#pragma unroll
+                for (int j = 1; j < kIters; ++j)
+                    if (j == it) q = v[j];
+                const bool p = fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])) >= tk.tv;
+                const uint64_t m = ballot(p);
+                if (m) {
+                    append(q, p, m, base + it * 256);
+                    if (tk.cnt > kCap) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane, tau);
+                }
+            }
+        };
+
+        // Collect up to 64 of this wave's segments (lane i holds the i-th),
+        // then stream them two at a time; repeat while segments remain.
+        const int dead = a.nseg;  // a segment past the row's end: loads read zeros
+        int s0 = 0, group = 0, dealt = 0;
+        uint64_t pick = 0;
+        for (;;) {
+            int n_own = 0, my_seg = dead;
+            while (n_own < 64) {
+                if (!pick) {
+                    if (s0 >= a.nseg) break;
+                    group = s0;
+                    const int sl = s0 + lane;
+                    float m = sl < a.nseg && s0 >= 64 * kSegCache ? sm[sl] : -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < kSegCache; ++j)
+                        if (s0 == 64 * j) m = cache[j];
+                    pick = ballot(sl < a.nseg && m >= tau);
+                    s0 += 64;
+                    continue;
+                }
+                const int p = __builtin_ctzll(pick);
+                pick &= pick - 1;
+                if ((dealt++ % kFinWaves) == wave) {
+                    if (lane == n_own) my_seg = group + p;
+                    ++n_own;
+                }
+            }
+            if (n_own == 0) break;
+            f32x4 va[kIters], vb[kIters];
+            load(va, lane_value(my_seg, 0));
+            for (int i = 0; i < n_own; i += 2) {
+                const int sa = lane_value(my_seg, i);
+                const int sb = i + 1 < 64 ? lane_value(my_seg, i + 1) : dead;  // dead past n_own
+                load(vb, sb);
+                process(va, sa);
+                load(va, i + 2 < 64 ? lane_value(my_seg, i + 2) : dead);
+                if (i + 1 < n_own) process(vb, sb);
+            }
+            if (n_own < 64) break;
+        }
+        if (lane == 0) { s_len[wave] = tk.lcount + tk.cnt; s_lc[wave] = tk.lcount; }
+    }
+    __syncthreads();
+    // A wave's entries are its list (s_lc of them) followed by its buffer.
+    // Usually the four waves hold a few dozen in all; otherwise each wave
+    // first reduces its own to at most k.
+    int n_tot = 0;
+#pragma unroll
+    for (int w = 0; w < kFinWaves; ++w) n_tot += s_len[w];
+    if (n_tot > 64) {
+        if (wave < kFinWaves) {
+            if (tk.cnt > 0) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane, -INFINITY);
+            if (lane == 0) { s_len[wave] = tk.lcount; s_lc[wave] = tk.lcount; }
+        }
+        __syncthreads();
+        n_tot = 0;
+#pragma unroll
+        for (int w = 0; w < kFinWaves; ++w) n_tot += s_len[w];
+    }
+    if (wave != 0) return;
+
+    // entry e of the waves' concatenated entries
+    auto entry = [&](int e, float& v, int& i) {
+        v = -INFINITY;
+        i = -1;
+        int off = 0;
+#pragma unroll
+        for (int w = 0; w < kFinWaves; ++w) {
+            const int loc = e - off;
+            if (loc >= 0 && loc < s_len[w]) {
+                v = loc < s_lc[w] ? s_lv[w][loc] : s_bv[w][loc - s_lc[w]];
+                i = loc < s_lc[w] ? s_li[w][loc] : s_bi[w][loc - s_lc[w]];
+            }
+            off += s_len[w];
+        }
+    };
+    auto emit = [&](int rank, float v, int i) {
+        a.topk_idx[(size_t)row * a.k + rank] = i;
+        a.topk_val[(size_t)row * a.k + rank] = v;
+        if (rank == 0 && a.T == 0.f) {
+            if (a.lse) a.lse[row] = NAN;
+            if (a.draft) a.draft[row] = i;
+        }
+    };
+    if (n_tot <= 64) {
+        // One entry per lane.  Only entries >= tau can rank, and the row's
+        // top k are among them (k <= V entries of the row exist, so no empty
+        // ranks); each of those counts the others ranking ahead of it, so the
+        // ranks are 0, 1, ... without repeats (every index appears once).
+        float v;
+        int i;
+        entry(lane, v, i);
+        const bool keep = lane < n_tot && v >= tau && i != -1;
+        uint64_t kept = ballot(keep);
+        int rank = 0;
+        while (kept) {
+            const int j = __builtin_ctzll(kept);
+            kept &= kept - 1;
+            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+            const int ij = __builtin_amdgcn_readlane(i, j);
+            rank += ranks_ahead(vj, ij, v, i) ? 1 : 0;
+        }
+        if (keep && rank < a.k) emit(rank, v, i);
+        return;
+    }
+    // more than 64 entries (k > 16): k rounds of a wave-wide reduction
+    float cv[kFinWaves];
+    int ci[kFinWaves];
+#pragma unroll
+    for (int q = 0; q < kFinWaves; ++q) entry(q * 64 + lane, cv[q], ci[q]);
+    for (int rr = 0; rr < a.k; ++rr) {
+        float bv = cv[0];
+        int bi = ci[0];
+#pragma unroll
+        for (int q = 1; q < kFinWaves; ++q)
+            if (ranks_ahead(cv[q], ci[q], bv, bi)) { bv = cv[q]; bi = ci[q]; }
+        wave_best(bv, bi);
+#pragma unroll
+        for (int q = 0; q < kFinWaves; ++q)
+            if (ci[q] == bi && ci[q] != -1) { cv[q] = -INFINITY; ci[q] = -1; }
+        if (lane == 0) emit(rr, bv, bi);
     }
 }
 
@@ -699,14 +868,12 @@ struct ScanPlan {
     int nseg, spw, wpr;
 };
 
-ScanPlan plan_scan(long rows, int V, int k) {
+ScanPlan plan_scan(long rows, int V) {
     ScanPlan p;
     p.nseg = (V + kSeg - 1) / kSeg;
     long spw = (rows * p.nseg + kTargetWaves - 1) / kTargetWaves;
     if (spw < 1) spw = 1;
     if (spw > p.nseg) spw = p.nseg;
-    // the finalize merges wpr * k candidates in a kMaxCand-entry LDS array
-    while (spw < p.nseg && ((p.nseg + spw - 1) / spw) * (long)k > kMaxCand) ++spw;
     p.spw = (int)spw;
     p.wpr = (p.nseg + p.spw - 1) / p.spw;
     return p;
@@ -714,18 +881,16 @@ ScanPlan plan_scan(long rows, int V, int k) {
 
 struct TopKLayout {
     ScanPlan sp;
-    size_t seg_m, seg_s, cand_v, cand_i, bytes;
+    size_t seg_m, seg_s, bytes;
 };
 
-TopKLayout topk_layout(int batch, int gamma, int vocab, int k) {
+TopKLayout topk_layout(int batch, int gamma, int vocab) {
     TopKLayout L{};
     const long rows = (long)batch * gamma;
-    L.sp = plan_scan(rows, vocab, k);
+    L.sp = plan_scan(rows, vocab);
     Carve c;
     L.seg_m = c.take<float>((size_t)rows * L.sp.nseg);
     L.seg_s = c.take<double>((size_t)rows * L.sp.nseg);
-    L.cand_v = c.take<float>((size_t)rows * L.sp.wpr * k);
-    L.cand_i = c.take<int>((size_t)rows * L.sp.wpr * k);
     L.bytes = c.total();
     return L;
 }
@@ -738,7 +903,7 @@ struct VerifyLayout {
 VerifyLayout verify_layout(int batch, int gamma, int vocab) {
     VerifyLayout L{};
     const long rows = (long)batch * gamma;
-    L.sp = plan_scan(rows, vocab, 1);
+    L.sp = plan_scan(rows, vocab);
     const size_t rs = (size_t)rows * L.sp.nseg;
     Carve c;
     L.p_m = c.take<float>(rs);
@@ -772,7 +937,7 @@ using namespace dfl;
 
 extern "C" size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k) {
     if (batch < 0 || gamma < 1 || vocab < 1 || k < 1) return 0;
-    return topk_layout(batch, gamma, vocab, k).bytes;
+    return topk_layout(batch, gamma, vocab).bytes;
 }
 
 extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
@@ -784,22 +949,22 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
     if (batch == 0) return DFLASH_OK;
     if (!logits || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     if (temperature > 0.f && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > 64 || gamma > 32 || vocab % 4 != 0) return DFLASH_ERR_UNSUPPORTED;
-    const TopKLayout L = topk_layout(batch, gamma, vocab, k);
+    if (k > 64 || gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab) return DFLASH_ERR_UNSUPPORTED;
+    const TopKLayout L = topk_layout(batch, gamma, vocab);
     if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
-    ScanArgs s{logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, k, c2,
+    ScanArgs s{logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, c2,
                reinterpret_cast<float*>(ws + L.seg_m), reinterpret_cast<double*>(ws + L.seg_s),
-               reinterpret_cast<float*>(ws + L.cand_v), reinterpret_cast<int*>(ws + L.cand_i)};
-    if (temperature > 0.f) launch_scan<kTopK | kSumExp>(s, st);
-    else launch_scan<kTopK>(s, st);
+               nullptr, nullptr};
+    if (temperature > 0.f) launch_scan<kSumExp>(s, st);
+    else launch_scan<kSegMax>(s, st);
     int rc = launch_status();
     if (rc) return rc;
-    TopKFin f{logits, batch, gamma, vocab, L.sp.nseg, L.sp.wpr, k, temperature, c2, seeds, step,
-              s.seg_m, s.seg_s, s.cand_v, s.cand_i, topk_idx, topk_val, lse, draft};
-    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(128), 0, st, f);
+    TopKFin f{logits, batch, gamma, vocab, L.sp.nseg, k, temperature, c2, seeds, step,
+              s.seg_m, s.seg_s, topk_idx, topk_val, lse, draft};
+    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(64 * (kFinWaves + 1)), 0, st, f);
     return launch_status();
 }
 
@@ -819,7 +984,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     if (batch == 0) return DFLASH_OK;
     if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_ERR_NULL;
     if (temperature > 0.f && !seeds) return DFLASH_ERR_NULL;
-    if (gamma > 32 || vocab % 4 != 0) return DFLASH_ERR_UNSUPPORTED;
+    if (gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab) return DFLASH_ERR_UNSUPPORTED;
     const VerifyLayout L = verify_layout(batch, gamma, vocab);
     if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
@@ -839,7 +1004,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     v.seq_w = reinterpret_cast<f32x4*>(ws + L.seq_w);
     v.resid_s = reinterpret_cast<double*>(ws + L.resid);
     v.accept_len = accept_len; v.out_tokens = out_tokens; v.accepted = accepted;
-    ScanArgs s{target_logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, 1, c2,
+    ScanArgs s{target_logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, c2,
                const_cast<float*>(v.p_seg_m), const_cast<double*>(v.p_seg_s),
                const_cast<float*>(v.cand_v), const_cast<int*>(v.cand_i)};
     if (temperature == 0.f) {

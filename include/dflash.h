@@ -139,7 +139,7 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
  *            softmax(logits / T) by inverse CDF in increasing vocabulary order
  *            with the purpose-0 uniform of (seeds[b], step, b, r).
  *   seeds    [batch] uint64 (device); may be NULL when T == 0.
- * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, 1 <= gamma <= 32.
+ * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, vocab <= 2^29, 1 <= gamma <= 32.
  * ------------------------------------------------------------------------ */
 size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k);
 int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
@@ -184,7 +184,7 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
  *                 or bonus token, then -1.
  *   accepted      [batch, gamma-1] uint8 or NULL: the accept test of every
  *                 draft row (also rows after the first rejection).
- * Supported: 1 <= gamma <= 32, vocab % 4 == 0.
+ * Supported: 1 <= gamma <= 32, vocab % 4 == 0, vocab <= 2^29.
  * ------------------------------------------------------------------------ */
 size_t spec_verify_workspace_size(int batch, int gamma, int vocab);
 int spec_verify(const float* target_logits, const float* draft_logits,

@@ -89,6 +89,7 @@ def test_topk_validation():
     assert topk(T=float("inf")) == -2
     assert topk(k=65) == -3
     assert topk(V=151935) == -3
+    assert topk(V=(1 << 29) + 4) == -3     # row bytes past 32-bit buffer offsets
     assert topk(G=40) == -3
     assert topk() == -4
     assert topk(seeds=None, T=0.0) == -4   # greedy needs no seeds; fails on workspace only
@@ -112,6 +113,7 @@ def test_verify_validation():
     assert verify(T=-0.5) == -2
     assert verify(G=33) == -3
     assert verify(V=1001) == -3
+    assert verify(V=(1 << 29) + 4) == -3
     assert verify() == -4
     assert verify(zq=None, seeds=None, T=0.0) == -4
 

@@ -85,6 +85,27 @@ def test_topk_all_equal_row():
     _topk_case(zd, 64, 1.0, syn.philox_seeds(1, 3), what="all equal sampled")
 
 
+def test_topk_long_rows_many_candidate_segments():
+    """600,000 entries = 293 segments: the finalize reads segment maxima past the
+    ones it holds in registers, and a row of equal logits with a few planted
+    larger ones puts every segment among the candidates (over 64 per wave)."""
+    g = torch.Generator().manual_seed(11)
+    zd = torch.zeros((1, 3, 600000), dtype=torch.float32)
+    zd[0, 0, [599999, 412345, 7, 300000]] = torch.tensor([2.0, 2.0, 1.0, 0.5])
+    zd[0, 1] = torch.randn(600000, generator=g)
+    zd[0, 2] = torch.round(torch.randn(600000, generator=g) * 2) / 2  # many exact ties
+    for k in (8, 64):
+        _topk_case(zd, k, 0.0, None, what=f"V=600000 k={k} greedy")
+    _topk_case(zd, 8, 0.8, syn.philox_seeds(1, 2), what="V=600000 k=8 sampled")
+
+
+def test_topk_rows_with_fewer_finite_entries_than_k():
+    zd = torch.full((1, 2, 8192), float("-inf"), dtype=torch.float32)
+    zd[0, 0, [5000, 17, 8191]] = torch.tensor([1.0, 3.0, 1.0])
+    zd[0, 1, 4096:] = 0.0
+    _topk_case(zd, 8, 0.0, None, what="mostly -inf greedy")
+
+
 def test_topk_trained_block_size_rows():
     """Batch 16, gamma 16, drafter noise growing from 0.5 to 3.0 along the block."""
     zt, zd = syn.logits_pair(16, 16, 151936, 3.0, syn.linear_noise_std(16, 0.5, 3.0), seed=6)
