@@ -196,6 +196,26 @@ def fuse_512_rows(dev, warmup, steps):
             "mfma_frac_of_2500": round(flops / (us * 1e-6) / 2.5e15, 4)}
 
 
+def fuse_probe():
+    """dflash_context_fuse three times at 256 rows (32 sequences x 8 new tokens) and
+    three times at 512 rows (64 x 8), nothing else: the MFMA counter passes."""
+    dev = torch.device("cuda:0")
+    for Bf in (B, 64):
+        rows = Bf * G
+        fz = syn.fuse_inputs(rows, N_TAPS, D_TGT, D_MODEL, LAYERS, HKV, D, SEED + 1, device=dev)
+        ring = torch.zeros((LAYERS, 2, Bf, HKV, W, D), dtype=torch.bfloat16, device=dev)
+        row_seq = torch.arange(Bf, device=dev, dtype=torch.int32).repeat_interleave(G)
+        row_pos = (W + torch.arange(G, device=dev)).repeat(Bf).to(torch.int64)
+        ws = torch.empty(dfl.dflash_context_fuse_workspace_size(rows, N_TAPS, D_TGT, D_MODEL, LAYERS,
+                                                                HKV, D), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dfl.dflash_context_fuse(fz["x"], fz["w_c"], fz["gain"], 1e-6, fz["w_kv"], row_seq,
+                                    row_pos, ring, N_TAPS, workspace=ws)
+        torch.cuda.synchronize()
+        del fz, ring, ws
+        torch.cuda.empty_cache()
+
+
 def selector_figure(wl, dev, warmup, steps):
     """NEXT row: the candidate selector's walk over top-16 candidates (r = 64 token
     embeddings, synthetic) and verification of its deterministic drafts, at the
@@ -523,12 +543,18 @@ def main():
     ap.add_argument("--lm-head-probe", action="store_true",
                     help="only run dflash_lm_head_topk three times at the step's 256 rows "
                          "(the LM head's counter passes)")
+    ap.add_argument("--fuse-probe", action="store_true",
+                    help="only run dflash_context_fuse three times at the step's 256 rows and "
+                         "three times at 512 rows (the fusion GEMMs' MFMA counter passes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.fuse_probe:
+        fuse_probe()
         return
     if args.lm_head_probe:
         dev = torch.device("cuda:0")
