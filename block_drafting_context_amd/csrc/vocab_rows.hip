@@ -223,14 +223,33 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
 }
 
 // ----------------------------------------------------------- draws
-// Merge a row's segment statistics: M = max m_s, S = sum s_s 2^((m_s - M) c2).
+// Merge a row's segment statistics: M = max m_s, S = sum s_s 2^((m_s - M) c2)
+// (each lane sums its segments lane, lane + 64, ... in that order).  The
+// first 64 * kStatRegs segments are loaded at once into registers (addresses
+// clamped into the row, so no load sits behind a branch), the rest in a loop.
+constexpr int kStatRegs = 4;
 __device__ __forceinline__ void merge_row_stats(const float* sm, const double* ss, int nseg, float c2, int lane,
                                 float& M, double& S) {
+    float mv[kStatRegs];
+    double sv[kStatRegs];
+#pragma unroll
+    for (int j = 0; j < kStatRegs; ++j) {
+        const int sj = lane + 64 * j;
+        const int sc = sj < nseg ? sj : nseg - 1;
+        const float x = sm[sc];
+        sv[j] = ss[sc];
+        mv[j] = sj < nseg ? x : -INFINITY;
+    }
     float m = -INFINITY;
-    for (int s = lane; s < nseg; s += 64) m = fmaxf(m, sm[s]);
+#pragma unroll
+    for (int j = 0; j < kStatRegs; ++j) m = fmaxf(m, mv[j]);
+    for (int s = lane + 64 * kStatRegs; s < nseg; s += 64) m = fmaxf(m, sm[s]);
     M = wave_max(m);
     double acc = 0.0;
-    for (int s = lane; s < nseg; s += 64)
+#pragma unroll
+    for (int j = 0; j < kStatRegs; ++j)
+        if (mv[j] != -INFINITY) acc += sv[j] * (double)fast_exp2((mv[j] - M) * c2);
+    for (int s = lane + 64 * kStatRegs; s < nseg; s += 64)
         if (sm[s] != -INFINITY) acc += ss[s] * (double)fast_exp2((sm[s] - M) * c2);
     S = wave_sum(acc);
 }
@@ -246,9 +265,12 @@ __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const
     float w[32];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
-        if (lo + 4 * q < V) w4 = wfn.w4(lo + 4 * q);
-        w[4 * q + 0] = w4[0]; w[4 * q + 1] = w4[1]; w[4 * q + 2] = w4[2]; w[4 * q + 3] = w4[3];
+        // a quad past the row's end reads the last quad (V % 4 == 0) and weighs
+        // nothing, so the eight loads are issued together
+        const int v = lo + 4 * q;
+        const f32x4 w4 = wfn.w4(v < V ? v : V - 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[4 * q + c] = v < V ? w4[c] : 0.f;
     }
     double mine = 0.0;
 #pragma unroll
@@ -662,7 +684,8 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
     __shared__ int s_acc[32], s_tok[32];
     __shared__ float s_M[32];
     __shared__ double s_S[32], s_lsep[32], s_lseq[32];
-    const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = a.G;
     const double Td = (double)a.T;
     for (int r = wave; r < G; r += kCommitWaves) {
@@ -809,7 +832,7 @@ __device__ __forceinline__ ResidualW make_residual(const VerifyArgs& a, int b, i
 
 // Residual mass per segment of row j, for sequences that rejected a draft.
 __global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kScanWaves + wave;
     const int b = gw / a.nseg, seg = gw % a.nseg;
     if (b >= a.B) return;
@@ -820,8 +843,10 @@ __global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
     f32x4 t4[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
+        // a quad past the row's end reads the last quad and weighs nothing
         const int e = base + it * 256;
-        t4[it] = e < a.V ? w.w4(e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 x = w.w4(e < a.V ? e : a.V - 4);
+        t4[it] = e < a.V ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     double s = 0.0;
 #pragma unroll
