@@ -80,3 +80,19 @@ def test_fuse_full_drafter_step_sampled_rows():
     sample = np.random.default_rng(3).choice(rows, 16, replace=False)
     _case(rows, 5, 5120, 5120, 5, 8, 128, W, B, seqs, pos, seed=3, sample=sample,
           gain_random=False)
+
+
+def test_fuse_serving_step_sampled_rows():
+    """The throughput workload's fusion: 32 sequences x 8 newly verified tokens
+    (256 rows, the launch configuration the bench times), positions ctx_len - 8
+    .. ctx_len - 1 of context lengths uniform in [512, 131072], so the rows land
+    at wrapped slots of the 4,096-slot rings (16 sampled rows against the oracle,
+    all untouched slots bit-exact)."""
+    B, W, per = 32, 4096, 8
+    rows = B * per
+    cl = syn.ctx_lengths(B, 512, 131072, 3).numpy().astype(np.int64)
+    seqs = np.repeat(np.arange(B), per)
+    pos = np.repeat(cl, per) - per + np.tile(np.arange(per), B)
+    sample = np.random.default_rng(4).choice(rows, 16, replace=False)
+    _case(rows, 5, 5120, 5120, 5, 8, 128, W, B, seqs, pos, seed=4, sample=sample,
+          gain_random=False)
