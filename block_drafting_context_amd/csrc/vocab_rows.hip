@@ -675,7 +675,7 @@ __device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >
 
 constexpr int kCommitWaves = 8;  // one wave per block row (gamma <= 8 in one round)
 
-// Verification of one sequence.  The block's rows are spread over the four
+// Verification of one sequence.  The block's rows are spread over the eight
 // waves: each merges its rows' statistics with all 64 lanes (target argmax for
 // greedy; max and fp64 exp-sum for sampled), gathers p and q at the draft and
 // takes the fp64 accept decision.  Wave 0 then forms the accepted prefix and,
