@@ -106,6 +106,15 @@ def test_topk_rows_with_fewer_finite_entries_than_k():
     _topk_case(zd, 8, 0.0, None, what="mostly -inf greedy")
 
 
+def test_topk_largest_k_full_vocab_and_longest_block():
+    """The supported extremes: k = 64 over 151,936-entry rows, and gamma = 32."""
+    zt, zd = syn.logits_pair(1, 2, 151936, 2.0, 1.0, seed=18)
+    _topk_case(zd, 64, 0.7, syn.philox_seeds(1, 4), what="k=64 V=151936 sampled")
+    _topk_case(zd, 64, 0.0, None, what="k=64 V=151936 greedy")
+    zt, zd = syn.logits_pair(2, 32, 5000, 2.0, 1.0, seed=19)
+    _topk_case(zd, 8, 0.9, syn.philox_seeds(2, 5), what="gamma=32")
+
+
 def test_topk_trained_block_size_rows():
     """Batch 16, gamma 16, drafter noise growing from 0.5 to 3.0 along the block."""
     zt, zd = syn.logits_pair(16, 16, 151936, 3.0, syn.linear_noise_std(16, 0.5, 3.0), seed=6)
@@ -229,3 +238,27 @@ def test_verify_sampled_disjoint_point_masses():
     s = syn.philox_seeds(B, 0)
     j = _verify_case(zt, zd, drafts, 1.0, s, what="point masses")
     assert (j == 0).all()
+
+
+def test_verify_longest_block_greedy_planted_prefixes():
+    """gamma = 32 (the supported maximum): drafts equal to the target argmax for
+    0, 1, ..., 31 leading rows, so every prefix length including all-accepted
+    (bonus from the last row) occurs."""
+    B, G, V = 32, 32, 4096
+    zt, zd = syn.logits_pair(B, G, V, 3.0, 1.5, seed=20)
+    am = torch.argmax(zt, dim=-1)
+    drafts = (am[:, :G - 1] + 1) % V
+    for b in range(B):
+        drafts[b, :b] = am[b, :b]
+    j = _verify_case(zt, zd, drafts, 0.0, None, what="gamma=32 greedy planted")
+    assert j.tolist() == [min(b, G - 1) for b in range(B)]
+
+
+def test_verify_longest_block_sampled_long_prefixes():
+    """gamma = 32, drafter rows close to the target rows (acceptance near 1), so
+    the accepted prefixes are long and some sequences take the bonus token."""
+    B, G, V = 6, 32, 4096
+    zt, zd = syn.logits_pair(B, G, V, 2.0, 0.02, seed=21)
+    s = syn.philox_seeds(B, 6)
+    j = _verify_case(zt, zd, _drafts_from(zd, 0.8, s), 0.8, s, what="gamma=32 sampled")
+    assert j.max() >= 20
