@@ -598,6 +598,7 @@ __device__ __forceinline__ int nth_set_bit(uint32_t m, int r) {
     return pos;
 }
 
+constexpr int kFinBatch = 8;                         // segment records per thread per preload batch
 constexpr int kFinChunk = 8;                         // candidate segments per selection chunk
 constexpr int kFinCand = kFinChunk * kQuads * 4;     // candidate entries per chunk
 
@@ -609,7 +610,9 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     __shared__ int q_seg[kFinMaxSeg];
     __shared__ float w_v[kHeadMaxK];
     __shared__ int w_i[kHeadMaxK];
-    __shared__ int n_q;
+    __shared__ int n_q, n_s;
+    __shared__ float s_s[kFinMaxSeg];
+    __shared__ float s_tm[kFinThreads];
     __shared__ float sv[kFinThreads / 64];
     __shared__ int si[kFinThreads / 64];
     __shared__ double sd[kFinThreads / 64];
@@ -619,26 +622,61 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     const u32x4* cd = a.cand + R * a.nseg * kQuads;
 
     if (tid == 0) n_q = 0;
-    for (int j = tid; j < a.nseg; j += kFinThreads) s_m[j] = st[j].m;
+    // segment statistics into LDS, kFinBatch records per thread in flight
+    // (addresses clamped into the row, so no load waits behind a branch); each
+    // thread also keeps the largest maximum of the segments it loaded
+    float tmax = -INFINITY;
+    for (int j0 = 0; j0 < a.nseg; j0 += kFinBatch * kFinThreads) {
+        SegStat t[kFinBatch];
+#pragma unroll
+        for (int q = 0; q < kFinBatch; ++q) {
+            const int j = j0 + q * kFinThreads + tid;
+            t[q] = st[j < a.nseg ? j : a.nseg - 1];
+        }
+#pragma unroll
+        for (int q = 0; q < kFinBatch; ++q) {
+            const int j = j0 + q * kFinThreads + tid;
+            if (j < a.nseg) {
+                s_m[j] = t[q].m;
+                s_s[j] = t[q].s;
+                tmax = fmaxf(tmax, t[q].m);
+            }
+        }
+    }
+    s_tm[tid] = tmax;
     __syncthreads();
 
-    // tau: the k-th largest segment maximum (k rounds, each taking the best
-    // segment ranked after the previous winner); -inf with fewer than k segments
-    float pv = INFINITY, tau = -INFINITY, mx = -INFINITY;
-    int pi = -1;
-    for (int r = 0; r < a.k; ++r) {
-        float bv = -INFINITY;
-        int bi = -1;
-        for (int j = tid; j < a.nseg; j += kFinThreads) {
-            const float m = s_m[j];
-            if (ranks_ahead(pv, pi, m, j) && ranks_ahead(m, j, bv, bi)) { bv = m; bi = j; }
+    // tau: the k-th largest of the threads' maxima, counting repeats (-inf
+    // when fewer than k are above -inf).  Those k maxima are k distinct
+    // entries of the row, so tau bounds the row's k-th largest entry from
+    // below and every top-k entry lies in a segment whose maximum is >= tau.
+    // Every wave computes it (and the row maximum mx) from the same 256
+    // values, with wave-level reductions only: no barrier per round.
+    constexpr int kTm = kFinThreads / 64;
+    float cm[kTm];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kTm; ++q) {
+        cm[q] = s_tm[q * 64 + lane];
+        lm = fmaxf(lm, cm[q]);
+    }
+    const float mx = wave_max(lm);
+    float tau = -INFINITY;
+    {
+        float t = INFINITY;
+        int counted = 0;
+        for (;;) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < kTm; ++q)
+                if (cm[q] < t) m = fmaxf(m, cm[q]);
+            m = wave_max(m);
+            if (m == -INFINITY) break;
+#pragma unroll
+            for (int q = 0; q < kTm; ++q) counted += __popcll(__ballot(cm[q] == m));
+            if (counted >= a.k) { tau = m; break; }
+            t = m;
         }
-        block_best(bv, bi, sv, si);
-        if (bi < 0) { tau = -INFINITY; break; }
-        if (r == 0) mx = bv;
-        pv = bv;
-        pi = bi;
-        tau = bv;
     }
 
     // the segments that can hold a top-k entry (m >= tau), in any order
@@ -647,60 +685,105 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     __syncthreads();
     const int nq = n_q;
 
-    // Chunks of kFinChunk segments: every record (quad) of the chunk's
-    // segments is unpacked into LDS, then k rounds of a block-wide (value desc,
-    // index asc) selection over the chunk and the running top k (kept in the
-    // last kHeadMaxK entries) take the new top k.
+    // Only entries >= tau can rank (tau is at most the row's k-th largest
+    // value), and every top-k entry's quad was recorded by its segment.  The
+    // records of the candidate segments are unpacked keeping just those
+    // entries; when at most kFinThreads survive (the usual case), each thread
+    // ranks one by counting the survivors ranked ahead of it (every index
+    // appears once, so the ranks are 0, 1, ... without repeats).
     const int k = a.k;
-    if (tid < kHeadMaxK) { c_v[kFinCand + tid] = -INFINITY; c_i[kFinCand + tid] = -1; }
-    for (int c0 = 0; c0 < nq; c0 += kFinChunk) {
-        for (int slot = tid; slot < kFinChunk * kQuads; slot += kFinThreads) {
-            const int qi = c0 + slot / kQuads, r = slot % kQuads;
-            float v4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            int i0 = -1;
-            if (qi < nq) {
-                const int j = q_seg[qi];
-                const uint32_t mask = (uint32_t)st[j].mask;
-                if (r < __builtin_popcount(mask)) {
-                    const u32x4 q = cd[(size_t)j * kQuads + r];
-                    const int bit = nth_set_bit(mask, r);
-                    i0 = j * kSegW + (bit >> 2) * 16 + (bit & 3) * 4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v4[e] = i0 + e < a.V ? __uint_as_float(q[e]) : -INFINITY;
-                }
-            }
+    if (tid == 0) n_s = 0;
+    __syncthreads();
+    for (int slot = tid; slot < nq * kQuads; slot += kFinThreads) {
+        const int j = q_seg[slot / kQuads], r = slot % kQuads;
+        // the record slot is read with the mask (slots past the mask's count
+        // hold stale data and are ignored)
+        const uint32_t mask = (uint32_t)st[j].mask;
+        const u32x4 q = cd[(size_t)j * kQuads + r];
+        if (r < __builtin_popcount(mask)) {
+            const int bit = nth_set_bit(mask, r);
+            const int i0 = j * kSegW + (bit >> 2) * 16 + (bit & 3) * 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                c_v[slot * 4 + e] = v4[e];
-                c_i[slot * 4 + e] = v4[e] > -INFINITY ? i0 + e : -1;
+                const float v = __uint_as_float(q[e]);
+                if (i0 + e < a.V && v >= tau) {
+                    const int at = atomicAdd(&n_s, 1);
+                    if (at < kFinCand) { c_v[at] = v; c_i[at] = i0 + e; }
+                }
             }
         }
-        __syncthreads();
-        float qv = INFINITY;
-        int qi_ = -1;
-        for (int r = 0; r < k; ++r) {
-            float bv = -INFINITY;
-            int bi = -1;
-            for (int e = tid; e < kFinCand + k; e += kFinThreads) {  // chunk, then running top k
-                const float v = c_v[e];
-                const int i = c_i[e];
-                if (i >= 0 && ranks_ahead(qv, qi_, v, i) && ranks_ahead(v, i, bv, bi)) { bv = v; bi = i; }
-            }
-            block_best(bv, bi, sv, si);
-            if (tid == 0) { w_v[r] = bv; w_i[r] = bi; }
-            qv = bv;
-            qi_ = bi;
+    }
+    __syncthreads();
+    const int ns = n_s;
+    int top1;
+    if (ns <= kFinThreads) {
+        const bool mine = tid < ns;
+        const float v = mine ? c_v[tid] : -INFINITY;
+        const int i = mine ? c_i[tid] : -1;
+        int rank = 0;
+        for (int e = 0; e < ns; ++e) rank += ranks_ahead(c_v[e], c_i[e], v, i) ? 1 : 0;
+        if (mine && rank < k) {
+            a.idx[R * k + rank] = i;
+            a.val[R * k + rank] = v;
+            if (rank == 0) w_i[0] = i;
         }
         __syncthreads();
-        if (tid < k) { c_v[kFinCand + tid] = w_v[tid]; c_i[kFinCand + tid] = w_i[tid]; }
-        __syncthreads();
+        top1 = w_i[0];
+    } else {
+        // many entries >= tau (long runs of equal logits): chunks of kFinChunk
+        // segments, every record unpacked into LDS, then k rounds of a
+        // block-wide (value desc, index asc) selection over the chunk and the
+        // running top k (kept in the last kHeadMaxK entries)
+        if (tid < kHeadMaxK) { c_v[kFinCand + tid] = -INFINITY; c_i[kFinCand + tid] = -1; }
+        for (int c0 = 0; c0 < nq; c0 += kFinChunk) {
+            for (int slot = tid; slot < kFinChunk * kQuads; slot += kFinThreads) {
+                const int qi = c0 + slot / kQuads, r = slot % kQuads;
+                float v4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                int i0 = -1;
+                if (qi < nq) {
+                    const int j = q_seg[qi];
+                    const uint32_t mask = (uint32_t)st[j].mask;
+                    if (r < __builtin_popcount(mask)) {
+                        const u32x4 q = cd[(size_t)j * kQuads + r];
+                        const int bit = nth_set_bit(mask, r);
+                        i0 = j * kSegW + (bit >> 2) * 16 + (bit & 3) * 4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v4[e] = i0 + e < a.V ? __uint_as_float(q[e]) : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    c_v[slot * 4 + e] = v4[e];
+                    c_i[slot * 4 + e] = v4[e] > -INFINITY ? i0 + e : -1;
+                }
+            }
+            __syncthreads();
+            float qv = INFINITY;
+            int qi_ = -1;
+            for (int r = 0; r < k; ++r) {
+                float bv = -INFINITY;
+                int bi = -1;
+                for (int e = tid; e < kFinCand + k; e += kFinThreads) {  // chunk, then running top k
+                    const float v = c_v[e];
+                    const int i = c_i[e];
+                    if (i >= 0 && ranks_ahead(qv, qi_, v, i) && ranks_ahead(v, i, bv, bi)) { bv = v; bi = i; }
+                }
+                block_best(bv, bi, sv, si);
+                if (tid == 0) { w_v[r] = bv; w_i[r] = bi; }
+                qv = bv;
+                qi_ = bi;
+            }
+            __syncthreads();
+            if (tid < k) { c_v[kFinCand + tid] = w_v[tid]; c_i[kFinCand + tid] = w_i[tid]; }
+            __syncthreads();
+        }
+        if (tid < k) {
+            a.idx[R * k + tid] = c_i[kFinCand + tid];
+            a.val[R * k + tid] = c_v[kFinCand + tid];
+        }
+        top1 = c_i[kFinCand];
     }
-    if (tid < k) {
-        a.idx[R * k + tid] = c_i[kFinCand + tid];
-        a.val[R * k + tid] = c_v[kFinCand + tid];
-    }
-    const int top1 = c_i[kFinCand];
 
     if (!a.want_exp) {
         if (tid == 0) {
@@ -713,7 +796,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     const int j0 = (int)((long)tid * a.nseg / kFinThreads);
     const int j1 = (int)((long)(tid + 1) * a.nseg / kFinThreads);
     double run = 0.0;
-    for (int j = j0; j < j1; ++j) run += seg_mass(st[j].s, s_m[j], mx, a.c2);
+    for (int j = j0; j < j1; ++j) run += seg_mass(s_s[j], s_m[j], mx, a.c2);
     const double incl = wave_inclusive_scan(run);
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = 0.0;
@@ -734,7 +817,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     int first = kNone, last = -1;
     double cum = excl;
     for (int j = j0; j < j1; ++j) {
-        const double sj = seg_mass(st[j].s, s_m[j], mx, a.c2);
+        const double sj = seg_mass(s_s[j], s_m[j], mx, a.c2);
         cum += sj;
         if (sj > 0.0) {
             last = j;
