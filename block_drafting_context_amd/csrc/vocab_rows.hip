@@ -690,7 +690,10 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
     const double Td = (double)a.T;
     for (int r = wave; r < G; r += kCommitWaves) {
         const bool is_draft = r < G - 1;
+        // the row's inputs that do not depend on each other are loaded together
         const int d = is_draft ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : 0;
+        const double lseq_in =
+            is_draft && a.zq && a.draft_lse && a.T > 0.f ? a.draft_lse[(size_t)b * G + r] : 0.0;
         if (a.T == 0.f) {
             const size_t cb = ((size_t)b * G + r) * a.wpr;
             float bv = -INFINITY;
@@ -722,7 +725,7 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
         double lseq = 0.0;
         if (is_draft && a.zq) {
             if (a.draft_lse) {
-                lseq = a.draft_lse[(size_t)b * G + r];
+                lseq = lseq_in;
             } else {
                 float Mq;
                 double Sq;
