@@ -34,6 +34,7 @@ constexpr int kPThreads = 512;
 constexpr int kPBins = 4096;
 constexpr float kPBinsPerUnit = 64.f;   // bins per unit of log2 weight below the maximum
 constexpr int kPCap = 2048;             // entries gathered for the final count
+constexpr int kPInFlight = 8;           // 16-byte loads per thread in flight in a pass over the row
 constexpr float kFix = 1099511627776.f; // 2^40: fixed-point scale of a weight
 
 struct TopPArgs {
@@ -98,16 +99,18 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     // fn(logit, index) for every entry of the row (16-byte loads when aligned)
     auto each = [&](auto&& fn) {
         if (vec) {
-            // four 16-byte loads in flight per thread before any is used
+            // kPInFlight 16-byte loads in flight per thread before any is used
+            // (one workgroup streams a whole row: its passes are bound by the
+            // loads it keeps in flight)
             const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
             const int V4 = V >> 2;
             int i = tid;
-            for (; i + 3 * kPThreads < V4; i += 4 * kPThreads) {
-                f32x4 q[4];
+            for (; i + (kPInFlight - 1) * kPThreads < V4; i += kPInFlight * kPThreads) {
+                f32x4 q[kPInFlight];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) q[u] = z4[i + u * kPThreads];
+                for (int u = 0; u < kPInFlight; ++u) q[u] = z4[i + u * kPThreads];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kPInFlight; ++u) {
                     const int b = 4 * (i + u * kPThreads);
                     fn(q[u][0], b); fn(q[u][1], b + 1); fn(q[u][2], b + 2); fn(q[u][3], b + 3);
                 }
@@ -247,6 +250,7 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
         for (int i = tid; i < n; i += kPThreads) {
             const uint64_t ki = g_key[i];
             unsigned long long ge = 0;
+#pragma unroll 8
             for (int j = 0; j < n; ++j) ge += g_key[j] >= ki ? g_w[j] : 0ull;
             if (ge >= need && ki > best) best = ki;
         }
@@ -258,8 +262,8 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     if (vec) {
         const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
         f32x4* o4 = reinterpret_cast<f32x4*>(out);
-        for (int i = tid; i < (V >> 2); i += kPThreads) {
-            f32x4 q = z4[i];
+        const int V4 = V >> 2;
+        auto mask4 = [&](f32x4 q, int i) {
             bool any_masked = false;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -269,7 +273,16 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
                 q[e] = keep ? q[e] : -INFINITY;
             }
             if (!inplace || any_masked) o4[i] = q;
+        };
+        int i = tid;
+        for (; i + (kPInFlight - 1) * kPThreads < V4; i += kPInFlight * kPThreads) {
+            f32x4 q[kPInFlight];
+#pragma unroll
+            for (int u = 0; u < kPInFlight; ++u) q[u] = z4[i + u * kPThreads];
+#pragma unroll
+            for (int u = 0; u < kPInFlight; ++u) mask4(q[u], i + u * kPThreads);
         }
+        for (; i < V4; i += kPThreads) mask4(z4[i], i);
     } else {
         for (int v = tid; v < V; v += kPThreads) {
             const float x = z[v];
