@@ -96,10 +96,14 @@ __global__ void __launch_bounds__(kSelThreads) select_path_kernel(SelArgs a) {
                 u32x4 va[4], vg[4], vb[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    // a block past the row's end reads its last block and adds nothing
+                    // (addresses clamped, so the 12 loads are never behind a branch)
                     const bool in = i0 + q < r / 8;
-                    va[q] = in ? ea[i0 + q] : u32x4{0u, 0u, 0u, 0u};
-                    vg[q] = in ? gt[i0 + q] : u32x4{0u, 0u, 0u, 0u};
-                    vb[q] = in ? eb[i0 + q] : u32x4{0u, 0u, 0u, 0u};
+                    const int qc = in ? i0 + q : r / 8 - 1;
+                    const u32x4 xa = ea[qc], xg = gt[qc], xb = eb[qc];
+                    va[q] = in ? xa : u32x4{0u, 0u, 0u, 0u};
+                    vg[q] = in ? xg : u32x4{0u, 0u, 0u, 0u};
+                    vb[q] = in ? xb : u32x4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
