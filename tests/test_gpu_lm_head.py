@@ -152,6 +152,25 @@ def test_equal_logits_take_lower_index_and_overflow_a_slot():
     run_case(h, w, 8, 16, 0.5, seeds=syn.philox_seeds(1, 2), what="ties sampled")
 
 
+def test_more_equal_maxima_than_the_finalize_ranks_at_once():
+    """Four hundred identical weight rows (entries 0..399, four segments) give
+    more entries at or above the finalize's threshold than it ranks in one
+    step (256), so it selects through its block-wide rounds."""
+    h, w = syn.lm_head_inputs(8, 128, 1200, seed=5)
+    w = w.clone()
+    w[0:400] = (h[0].float() * 0.2).to(w.dtype)  # far above every other logit of row 0
+    res = run_case(h, w, 8, 16, 0.0, what="400 ties greedy")
+    idx = to64(res["idx"])
+    z = f64(h) @ f64(w).T
+    hit = 0
+    for r in range(8):
+        if np.argmax(z[r]) == 0:
+            np.testing.assert_array_equal(idx[r], np.arange(16))
+            hit += 1
+    assert hit > 0
+    run_case(h, w, 8, 16, 0.5, seeds=syn.philox_seeds(1, 3), what="400 ties sampled")
+
+
 def test_more_rows_than_one_pass():
     h, w = syn.lm_head_inputs(300, 64, 513, seed=4)      # two passes over the weights
     run_case(h, w, 6, 8, 1.0, seeds=syn.philox_seeds(50, 9), step=2, what="300 rows")
