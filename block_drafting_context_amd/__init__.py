@@ -124,6 +124,7 @@ def _workspace(nbytes, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", torch.uint8, None, device)
     if workspace.numel() < nbytes:
         raise ValueError(f"workspace too small: {workspace.numel()} < {nbytes}")
     return workspace, workspace.numel()
@@ -232,6 +233,9 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=No
     acc_len = o.get("accept_len") if o.get("accept_len") is not None else torch.empty(B, dtype=torch.int32, device=dev)
     out_tok = o.get("out_tokens") if o.get("out_tokens") is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
     accepted = o.get("accepted") if o.get("accepted") is not None else torch.empty((B, max(G - 1, 1)), dtype=torch.uint8, device=dev)
+    _need(acc_len, "accept_len", torch.int32, (B,), dev)
+    _need(out_tok, "out_tokens", torch.int32, (B, G), dev)
+    _need(accepted, "accepted", torch.uint8, (B, max(G - 1, 1)), dev)
     ws, wsb = _workspace(spec_verify_workspace_size(B, G, V), dev, workspace)
     _call("spec_verify", _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
           _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),

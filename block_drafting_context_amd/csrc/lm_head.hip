@@ -187,16 +187,17 @@ __device__ __forceinline__ int quad_max(int v) {
 // (buffer_load_dwordx4 ... lds).  Written as inline assembly so that the
 // compiler, which cannot see which ring slot a DMA targets, does not guard the
 // operand fetches from the other slots with waits for every load in flight;
-// the kernel waits for its own loads explicitly.  NT: non-temporal.
+// the kernel waits for its own loads explicitly.  NT: non-temporal.  m0 (the
+// LDS destination) is declared clobbered, so the compiler keeps nothing there.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <bool NT>
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
     if (NT)
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
-                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
     else
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
 // raw byte buffer over [base, base + bytes)

@@ -36,6 +36,7 @@ constexpr float kPBinsPerUnit = 64.f;   // bins per unit of log2 weight below th
 constexpr int kPCap = 2048;             // entries gathered for the final count
 constexpr int kPInFlight = 8;           // 16-byte loads per thread in flight in a pass over the row
 constexpr float kFix = 1099511627776.f; // 2^40: fixed-point scale of a weight
+constexpr int kMaxTopPVocab = 1 << 24;   // rows shorter than this cannot overflow the 64-bit sums
 
 struct TopPArgs {
     const float* z;
@@ -310,6 +311,9 @@ extern "C" int dflash_top_p_mask(const float* logits, float* out, int32_t* kept,
     if (!(top_p > 0.f) || !(top_p <= 1.f)) return DFLASH_ERR_SHAPE;
     if (rows == 0) return DFLASH_OK;
     if (!logits || !out) return DFLASH_ERR_NULL;
+    // every weight is at most 2^40 in fixed point, so a row's 64-bit total
+    // cannot overflow below 2^24 entries
+    if (vocab >= kMaxTopPVocab) return DFLASH_ERR_UNSUPPORTED;
     TopPArgs a{logits, out, kept, vocab, (float)(1.4426950408889634 / (double)temperature), (double)top_p};
     hipLaunchKernelGGL(top_p_kernel, dim3(rows), dim3(kPThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), a);

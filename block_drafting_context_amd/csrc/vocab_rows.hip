@@ -741,7 +741,9 @@ __global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(Verify
                                           : exp((double)zpd / Td - lsep);
                 const double u =
                     philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
-                acc = u < (ratio < 1.0 ? ratio : 1.0);
+                // u < min(1, ratio); a ratio that is NaN (p and q both zero at the
+                // draft, e.g. a draft outside a truncated target row) rejects
+                acc = ratio >= 1.0 || u < ratio;
             }
             s_acc[r] = acc;
             s_M[r] = M;

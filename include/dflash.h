@@ -173,7 +173,8 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
  *            and the correction is drawn from p_j with the rejected draft
  *            removed (still lossless).  Unused when T == 0.
  *   draft_tokens  [batch, gamma] int32 (as written by dflash_topk); entries
- *            0..gamma-2 are the drafts, in [0, vocab) (precondition).
+ *            0..gamma-2 are the drafts, in [0, vocab) (precondition); entry
+ *            gamma-1 is ignored (so dflash_topk's output passes unchanged).
  *   draft_lse     [batch, gamma] float64 from dflash_topk at the same T;
  *            may be NULL (then recomputed from draft_logits; unused with
  *            deterministic drafts).
@@ -209,9 +210,12 @@ int spec_verify(const float* target_logits, const float* draft_logits,
  *   kv_ring[i, t, row_seq[r], h, row_pos[r] % window, d] = bf16(kv[r,c])
  *
  *   taps     [rows, n_taps*d_tgt] bf16, the tapped states of each new token
- *   w_c      [d_model, n_taps*d_tgt] bf16 (one row per output feature)
+ *   w_c      [d_model, n_taps*d_tgt] bf16, one row per output feature (the
+ *            H_t equation's W_c applied to the concatenated column; both
+ *            GEMM operands then have the reduction dimension contiguous)
  *   rms_gain [d_model] float32
- *   w_kv     [n_layers*2*n_kv*d_head, d_model] bf16
+ *   w_kv     [n_layers*2*n_kv*d_head, d_model] bf16, one row per output
+ *            feature (W_i^K, W_i^V of every layer stacked)
  *   row_seq  [rows] int32 in [0, batch), row_pos [rows] int64 >= 0
  *            (preconditions; no two rows may address the same slot)
  *   kv_ring  [n_layers, 2, batch, n_kv, window, d_head] bf16, in/out
@@ -279,8 +283,9 @@ int dflash_select_path(const int32_t* cand_idx, const float* cand_score, const u
  *         the caller's projection)
  *   y     [batch, gamma, d] bf16 out (16-byte aligned; must not overlap x)
  * Supported: d % n_groups == 0, (d / n_groups) % 8 == 0.
- * Accuracy: fp32 arithmetic (one fused multiply-add per channel), output
- * rounded to bf16, nearest even.
+ * Accuracy: fp32 arithmetic, per channel one multiply (the predecessor term)
+ * and one fused multiply-add (the own term added to it): two fp32
+ * roundings, then the output is rounded to bf16, nearest even.
  * All pointers are device memory owned by the caller; no workspace.
  * ------------------------------------------------------------------------ */
 int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int batch, int gamma,
@@ -345,6 +350,8 @@ int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows
  *          entries are written)
  *   kept   [rows] int32 or NULL: the nucleus size of each row
  *   temperature > 0; 0 < top_p <= 1 (top_p == 1 keeps every entry)
+ * Supported: vocab < 2^24 (the fixed-point row sums below stay within 64
+ * bits); DFLASH_ERR_UNSUPPORTED otherwise.
  * Accuracy: weights 2^((z - max) log2(e)/T) in fp32, summed exactly in fixed
  * point (2^-40 of the maximum's weight); the nucleus boundary is exact up to
  * that rounding of the cumulative mass.

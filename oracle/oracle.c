@@ -467,8 +467,10 @@ int orc_sampled_verify_seq_u(const double* zp, const double* zq, const int64_t* 
             rk = exp(zp[(int64_t)r * V + d] / T - Lp);  /* p(d) / 1 */
         }
         if (ratio) ratio[r] = rk;
-        const double a = rk < 1.0 ? rk : 1.0;
-        const int ok = u_acc[r] < a;
+        /* accept iff u < min(1, r).  When p(d) and q(d) are both zero, r is
+         * 0/0 (NaN): the target gives d no probability, so it is rejected
+         * (committing it would leave the target's distribution). */
+        const int ok = rk >= 1.0 || u_acc[r] < rk;
         if (accepted) accepted[r] = (uint8_t)ok;
         if (leading && ok) ++j; else leading = 0;
     }

@@ -241,3 +241,49 @@ def test_top_p_validation():
     assert topp(p=float("nan")) == -2
     assert topp(z=None) == -1
     assert topp(out=None) == -1
+
+
+def test_top_p_vocab_limit():
+    """Fixed-point row sums (2^40 per maximal weight) stay within 64 bits only
+    below 2^24 entries."""
+    assert topp(V=(1 << 24)) == -3
+    assert topp(V=(1 << 24) + 4) == -3
+
+
+def _verify_inputs(B=2, G=4, V=64):
+    import torch
+    return (torch.zeros((B, G, V), dtype=torch.float32), torch.zeros((B, G, V), dtype=torch.float32),
+            torch.zeros((B, G), dtype=torch.int32), torch.zeros(B, dtype=torch.int64))
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("accept_len", ("int64", (2,))),        # wrong dtype: the kernel writes int32
+    ("accept_len", ("int32", (3,))),
+    ("out_tokens", ("int32", (2, 3))),      # [B, G-1] instead of [B, G]: writes past the end
+    ("out_tokens", ("int64", (2, 4))),
+    ("accepted", ("uint8", (2, 2))),        # [B, G-2]
+    ("accepted", ("int32", (2, 3))),
+])
+def test_spec_verify_binding_checks_caller_outputs(name, bad):
+    """Caller-supplied outputs are checked (dtype, shape, device) before the
+    library is called: a wrong one would let the kernels write past it."""
+    import torch
+    zp, zq, d, seeds = _verify_inputs()
+    dtype, shape = bad
+    out = {name: torch.zeros(shape, dtype=getattr(torch, dtype))}
+    with pytest.raises((TypeError, ValueError)):
+        dfl.spec_verify(zp, zq, d, 0.7, seeds=seeds, outputs=out)
+
+
+def test_binding_checks_workspace_dtype_and_device():
+    import torch
+    zp, zq, d, seeds = _verify_inputs()
+    with pytest.raises(TypeError):
+        dfl.spec_verify(zp, zq, d, 0.7, seeds=seeds,
+                        workspace=torch.zeros(1 << 20, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        dfl.spec_verify(zp, zq, d, 0.7, seeds=seeds,
+                        workspace=torch.empty(1 << 20, dtype=torch.uint8, device="meta"))
+    with pytest.raises(TypeError):
+        dfl.dflash_topk(zq, 4, 0.7, seeds=seeds,
+                        workspace=torch.zeros(1 << 20, dtype=torch.int32))

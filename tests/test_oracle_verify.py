@@ -360,3 +360,24 @@ def test_verify_uses_documented_counters():
         one = oracle.sampled_verify_seq_u(zt[b], zd[b], drafts[b], T, ua, ud)
         assert one["accept_len"] == res["accept_len"][b]
         assert one["out_tokens"].tolist() == res["out_tokens"][b].tolist()
+
+
+def test_draft_with_zero_target_and_draft_probability_is_rejected():
+    """A draft that neither p nor q can produce (both logits -inf there, as for
+    a draft outside a truncated row) makes p/q = 0/0.  The target gives it no
+    probability, so committing it would leave the target's distribution: it is
+    rejected for every uniform, and the correction is drawn from [p - q]_+."""
+    V, G, T = 5, 3, 1.0
+    zp = np.log(np.array([[0.5, 0.5, 0.0, 0.0, 0.0]] * G))
+    zq = np.log(np.array([[0.25, 0.25, 0.0, 0.5, 0.0]] * G))
+    drafts = np.array([[2, 2]])
+    for step in range(200):
+        res = oracle.spec_verify(zp[None], zq[None], drafts, T, seeds=np.array([6], np.uint64),
+                                 step=step)
+        assert res["accept_len"][0] == 0
+        assert res["accepted"][0].tolist() == [0, 0]
+        assert res["out_tokens"][0, 0] in (0, 1)   # the residual's support
+    assert np.isnan(res["ratio"][0, 0])
+    # with u fixed at 0 (the most permissive uniform) the draft is still rejected
+    one = oracle.sampled_verify_seq_u(zp, zq, drafts[0], T, [0.0, 0.0], [0.3, 0.3, 0.3])
+    assert one["accept_len"] == 0 and one["accepted"].tolist() == [0, 0]
