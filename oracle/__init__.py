@@ -31,8 +31,9 @@ What each function follows (pages cited by title and section):
   kept, everything else masked to -inf.
 * ``lm_head_topk`` -- "Beam 1.0 DFlash2" model card, "Model" (the drafter
   reuses the target's LM head) and "DFlash vs DFlash 2", "The candidate
-  selector" (top-k per position); the draft draw is exact softmax sampling
-  done in two inverse-CDF steps over 128-entry vocabulary segments.
+  selector" (top-k per position); top-k, log-normaliser and draft are
+  ``draft_rows``' definitions applied to the LM head's logits (one inverse-CDF
+  draw over the whole row).
 * ``philox4x64_10`` / ``uniform`` -- Salmon et al., SC'11.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against values

@@ -65,8 +65,7 @@ void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t ou
 /* One uniform in [0,1) per (sequence seed, step, sequence, block row,
  * purpose): key = (seed, 0), counter = (step, b, row, purpose); the top 53
  * bits of the first output word, times 2^-53.  Purposes: 0 = draft draw,
- * 1 = accept test, 2 = correction or bonus draw, 3 + 256 j = the draw inside
- * vocabulary segment j of the LM-head sampler.  (Reading: the pages name no
+ * 1 = accept test, 2 = correction or bonus draw.  (Reading: the pages name no
  * generator; this layout is this project's choice.) */
 double orc_uniform(uint64_t seed, uint64_t step, uint64_t b, uint64_t row, uint64_t purpose)
 {
@@ -266,23 +265,18 @@ int orc_draft_rows(const double* z, int B, int G, int64_t V, int k, double T,
 /* the costly part.  [P3] "The problem: one expensive token at a time": the  */
 /* drafter proposes y ~ q = softmax(z / T).                                  */
 /*                                                                            */
-/* z = h W^T, W stored one row per vocabulary entry.  Top-k, the            */
-/* log-normaliser and T == 0 (argmax draft) are as in orc_draft_rows.       */
-/* Reading (sampler): the T > 0 draw is an exact softmax draw made in two   */
-/* inverse-CDF steps over consecutive 128-entry vocabulary segments (the    */
-/* last one may be shorter): the segment J from the segment masses          */
-/* S_j = sum_{v in j} w_v with the row's draft-draw uniform (purpose 0),    */
-/* then the entry inside J from its own weights with the uniform of purpose */
-/* 3 + 256 J.  P(v) = (S_J / S) (w_v / S_J) = w_v / S; each step needs only */
-/* the segment sums or one segment's weights, never a second full row.      */
+/* z = h W^T, W stored one row per vocabulary entry.  Everything computed    */
+/* from z is orc_draft_rows' definition, unchanged: top-k, the              */
+/* log-normaliser, and the draft (T == 0 the argmax; T > 0 one inverse-CDF   */
+/* draw from softmax(z / T) over the whole row, in increasing vocabulary    */
+/* order, with the row's purpose-0 uniform).  The same seeds give the same  */
+/* draft as orc_draft_rows on the same logits.                               */
 /*                                                                            */
 /* h [n, d] and w [V, d] are bf16 bit patterns (converted exactly to double  */
 /* here); row_id [n] is each row's global index r (sequence b = r / G,       */
 /* block row g = r % G; NULL = 0..n-1).  -> idx, val [n, k]; lse [n] (NaN at */
 /* T == 0; may be NULL); draft [n] (may be NULL); z_out [n, V] (may be NULL).*/
 /* ------------------------------------------------------------------------ */
-#define ORC_HEAD_SEGMENT 128
-
 static double bf16_bits_to_double(uint16_t bits)
 {
     const uint32_t u = (uint32_t)bits << 16;
@@ -297,7 +291,6 @@ int orc_lm_head_topk(const uint16_t* h, const uint16_t* w, const int64_t* row_id
 {
     if (n < 0 || G < 1 || V < 1 || d < 1 || k < 1 || k > V || T < 0.0) return -2;
     if (T > 0.0 && draft && !seeds) return -2;
-    const int64_t nseg = (V + ORC_HEAD_SEGMENT - 1) / ORC_HEAD_SEGMENT;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int i = 0; i < n; ++i) {
@@ -306,8 +299,7 @@ int orc_lm_head_topk(const uint16_t* h, const uint16_t* w, const int64_t* row_id
         double* hr = (double*)malloc(sizeof(double) * (size_t)d);
         double* z = (double*)malloc(sizeof(double) * (size_t)V);
         double* wv = (double*)malloc(sizeof(double) * (size_t)V);
-        double* S = (double*)malloc(sizeof(double) * (size_t)nseg);
-        if (!hr || !z || !wv || !S) { bad = 1; free(hr); free(z); free(wv); free(S); continue; }
+        if (!hr || !z || !wv) { bad = 1; free(hr); free(z); free(wv); continue; }
         for (int j = 0; j < d; ++j) hr[j] = bf16_bits_to_double(h[(int64_t)i * d + j]);
         /* logits: one dot product per vocabulary entry */
         for (int64_t v = 0; v < V; ++v) {
@@ -325,27 +317,12 @@ int orc_lm_head_topk(const uint16_t* h, const uint16_t* w, const int64_t* row_id
             const double L = orc_logsumexp(z, V, T);
             if (lse) lse[i] = L;
             if (draft) {
-                /* normalised weights, then the mass of every segment */
                 for (int64_t v = 0; v < V; ++v) wv[v] = exp(z[v] / T - L);
-                for (int64_t j = 0; j < nseg; ++j) {
-                    const int64_t lo = j * ORC_HEAD_SEGMENT;
-                    const int64_t hi = lo + ORC_HEAD_SEGMENT < V ? lo + ORC_HEAD_SEGMENT : V;
-                    double s = 0.0;
-                    for (int64_t v = lo; v < hi; ++v) s += wv[v];
-                    S[j] = s;
-                }
-                const uint64_t seed = seeds[b];
-                /* step 1: the segment; step 2: the entry inside it */
-                const int64_t J = orc_categorical(S, nseg, orc_uniform(seed, step, (uint64_t)b,
-                                                                        (uint64_t)g, 0));
-                const int64_t lo = J * ORC_HEAD_SEGMENT;
-                const int64_t len = lo + ORC_HEAD_SEGMENT < V ? ORC_HEAD_SEGMENT : V - lo;
-                const double u2 = orc_uniform(seed, step, (uint64_t)b, (uint64_t)g,
-                                              3 + 256 * (uint64_t)J);
-                draft[i] = lo + orc_categorical(wv + lo, len, u2);
+                draft[i] = orc_categorical(wv, V, orc_uniform(seeds[b], step, (uint64_t)b,
+                                                              (uint64_t)g, 0));
             }
         }
-        free(hr); free(z); free(wv); free(S);
+        free(hr); free(z); free(wv);
     }
     return bad ? -2 : 0;
 }

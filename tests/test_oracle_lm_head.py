@@ -3,12 +3,12 @@
 The drafter reuses the target's LM head ("Beam 1.0 DFlash2" model card,
 "Model"); top-k per position follows "DFlash vs DFlash 2", "The candidate
 selector"; the draft is a draw from q = softmax(z/T) ("The problem: one
-expensive token at a time"), made in two inverse-CDF steps over 128-entry
-vocabulary segments.  Pins: numpy matmul (library) for the logits, numpy
-lexsort / argmax and scipy logsumexp (library) for top-k and the normaliser,
-numpy's Philox and searchsorted (library) for each draw step on inputs where
-the other step is forced, a chi-square check that the two steps together
-sample softmax(z/T) exactly, and the row-subset invariant.
+expensive token at a time"), one inverse-CDF draw over the whole row in
+increasing vocabulary order at the row's purpose-0 uniform.  Pins: numpy
+matmul (library) for the logits, numpy lexsort / argmax and scipy logsumexp
+(library) for top-k and the normaliser, numpy's Philox and searchsorted
+(library) for the draw, a chi-square check that the draws sample
+softmax(z/T), and the row-subset invariant.
 """
 import numpy as np
 import pytest
@@ -19,7 +19,6 @@ from scipy.stats import chi2
 import oracle
 
 MASK64 = (1 << 64) - 1
-SEG = 128
 
 
 def bf16_bits(x):
@@ -80,10 +79,12 @@ def test_topk_lse_and_greedy_match_library_routines():
     np.testing.assert_array_equal(g["draft"], g["idx"][:, 0])
 
 
-def test_one_segment_draw_is_the_inverse_cdf():
-    """V <= 128: the segment step always picks segment 0, so the draft is the
-    inverse CDF of softmax(z/T) at the uniform of purpose 3."""
-    h, w = inputs(24, 32, 100, 3, w_std=0.4)
+def test_draw_is_the_inverse_cdf_over_the_row():
+    """The draft is the smallest index whose cumulative softmax(z/T) mass (in
+    increasing vocabulary order) exceeds u times the total, u the purpose-0
+    uniform of (seed, step, sequence, block row): numpy's Philox and
+    searchsorted, over rows of several hundred entries."""
+    h, w = inputs(24, 32, 700, 3, w_std=0.4)
     z = bits_to_f64(h) @ bits_to_f64(w).T
     G, T, step = 8, 0.7, 11
     seeds = np.array([5, 9, 13], dtype=np.uint64)
@@ -91,23 +92,22 @@ def test_one_segment_draw_is_the_inverse_cdf():
     for i in range(24):
         b, g = divmod(i, G)
         p = softmax(z[i] / T)
-        u = np_uniform(int(seeds[b]), step, b, g, 3)
+        u = np_uniform(int(seeds[b]), step, b, g, 0)
         assert r["draft"][i] == np.searchsorted(np.cumsum(p), u * p.sum(), side="right")
 
 
-def test_segment_step_picks_segments_by_mass():
-    """One dominant entry per 128-entry segment (every other logit 60 below):
-    the draft is the dominant entry of the segment the purpose-0 uniform picks
-    by the inverse CDF of the segment masses.  The last segment is ragged."""
-    V = 5 * SEG + 40
-    dom = np.array([7, 130, 300, 385, 600, 650])       # one per segment
+def test_draw_on_exact_logits_picks_by_mass():
+    """Exact logits (a one-hot hidden row reads one bf16 column of W): six
+    dominant entries spread over a 700-entry row, everything else 60 below; the
+    draft is the dominant entry whose cumulative mass first exceeds u."""
+    V = 700
+    dom = np.array([7, 130, 300, 385, 600, 650])
     logm = np.array([0.5, -1.0, 1.25, 0.0, 2.0, -0.5])  # bf16-exact log-masses
     zcol = np.full(V, -60.0)
     zcol[dom] = logm
     h, w = one_hot_head(zcol, 40)
-    T = 1.0
     seeds = np.arange(40, dtype=np.uint64) * 3 + 1
-    r = oracle.lm_head_topk(h, w, 1, 2, T, seeds=seeds, step=4)
+    r = oracle.lm_head_topk(h, w, 1, 2, 1.0, seeds=seeds, step=4)
     mass = np.exp(logm)
     cum = np.cumsum(mass) / mass.sum()
     for i in range(40):
@@ -115,28 +115,21 @@ def test_segment_step_picks_segments_by_mass():
         assert r["draft"][i] == dom[J]
 
 
-def test_entry_step_uses_the_segment_uniform():
-    """All mass in segment J (the rest 60 below): the draft is the inverse CDF
-    inside J at the uniform of purpose 3 + 256 J."""
-    V = 6 * SEG
-    rng = np.random.default_rng(4)
-    for J in (1, 4, 5):
-        zcol = np.full(V, -60.0)
-        zcol[J * SEG:(J + 1) * SEG] = bits_to_f64(bf16_bits(rng.standard_normal(SEG)))
-        h, w = one_hot_head(zcol, 16)
-        T = 0.8
-        r = oracle.lm_head_topk(h, w, 4, 3, T, seeds=np.arange(4) + 100, step=2)
-        p = softmax(zcol[J * SEG:(J + 1) * SEG] / T)
-        for i in range(16):
-            b, g = divmod(i, 4)
-            u = np_uniform(100 + b, 2, b, g, 3 + 256 * J)
-            assert r["draft"][i] == J * SEG + np.searchsorted(np.cumsum(p), u * p.sum(),
-                                                              side="right")
+def test_same_draft_as_the_logits_row_draw():
+    """Sampling from the LM head's logits is the logits-row draw of dflash_topk's
+    definition: with the same seeds and counters both give the same token."""
+    h, w = inputs(16, 40, 900, 8)
+    z = bits_to_f64(h) @ bits_to_f64(w).T
+    seeds = np.array([21, 22], dtype=np.uint64)
+    r = oracle.lm_head_topk(h, w, 8, 3, 0.8, seeds=seeds, step=5)
+    d = oracle.draft_rows(z.reshape(2, 8, 900), 3, 0.8, seeds=seeds, step=5)
+    np.testing.assert_array_equal(r["draft"], d["draft"].reshape(-1))
+    np.testing.assert_array_equal(r["idx"], d["idx"].reshape(16, 3))
 
 
-def test_two_step_draw_samples_softmax():
+def test_draw_samples_softmax():
     """Many rows with the same logits and distinct counters: the draft
-    frequencies match softmax(z/T) over a ragged three-segment vocabulary."""
+    frequencies match softmax(z/T) (chi-square)."""
     V, d, n, T = 300, 16, 60000, 0.9
     rng = np.random.default_rng(5)
     h1 = bf16_bits(rng.standard_normal((1, d)))
@@ -153,10 +146,6 @@ def test_two_step_draw_samples_softmax():
     ex = np.append(exp_[~small], exp_[small].sum())
     stat = ((obs - ex) ** 2 / ex).sum()
     assert stat < chi2.ppf(1 - 1e-6, len(obs) - 1), stat
-    # per-segment totals agree too (the segment step alone)
-    seg_obs = np.add.reduceat(counts, [0, SEG, 2 * SEG])
-    seg_p = np.add.reduceat(p, [0, SEG, 2 * SEG])
-    assert np.all(np.abs(seg_obs - seg_p * n) < 5 * np.sqrt(n * seg_p * (1 - seg_p)) + 1)
 
 
 def test_row_subset_matches_full_rows():
