@@ -19,9 +19,8 @@
 // hidden row i, i.e. every lane ends with 32 logits of one row and the four
 // lanes i, i+16, i+32, i+48 share that row's segment.  The epilogue reduces
 // each (row, segment) in registers across those four lanes:
-//   * m = max z and s = sum 2^((z - m) log2(e)/T);
-//   * the entry drawn inside the segment: inverse CDF of its weights in
-//     vocabulary order at the uniform of purpose 3 + 256 * segment;
+//   * m = max z and s = sum 2^((z - m) log2(e)/T), with the sums of its eight
+//     16-entry groups (kept for the draw);
 //   * top-k candidates: theta = a lower bound of the k-th largest of the
 //     segment's 32 quad maxima (quad: 4 consecutive entries in one lane's
 //     registers), taken from the four lanes' TT largest quad maxima (TT =
@@ -31,10 +30,14 @@
 //     are (ties need no special case: all of them are written).
 // A finalize kernel per row takes tau = the k-th largest segment maximum
 // (every top-k entry is >= tau, so only segments with m >= tau are read),
-// merges their records, adds the segment masses in fp64 for the
-// log-normaliser, and picks the segment by the inverse CDF of the masses at
-// the row's purpose-0 uniform; the draft is that segment's drawn entry.
-// P(v) = (S_J / S) (w_v / S_J) = w_v / S: an exact draw from softmax(z / T).
+// merges their records and adds the segment masses in fp64 for the
+// log-normaliser.  The draft is one inverse-CDF draw over the whole row in
+// increasing vocabulary order at the row's purpose-0 uniform u: the running
+// mass first exceeds u S inside the segment J found from the segment masses,
+// inside the 16-entry group of J found from its group sums, and at the entry
+// of that group found from its 16 logits, which the finalize recomputes from
+// the hidden row and 16 weight rows (32 KB per row at d = 5,120, instead of
+// keeping any logit in memory).
 #include <climits>
 #include <cmath>
 
@@ -43,7 +46,8 @@
 namespace dfl {
 namespace {
 
-constexpr int kSegW = 128;            // vocabulary segment: draw step and candidate slot
+constexpr int kSegW = 128;            // vocabulary segment: candidate slot and statistics record
+constexpr int kGrpW = 16;             // entries per group of a segment (eight group sums)
 constexpr int kHeadRows = 256;        // hidden rows per pass over the weights
 constexpr int kTileV = 2 * kSegW;     // vocabulary entries per workgroup tile
 #ifndef DFL_HEAD_BK
@@ -98,8 +102,8 @@ __device__ __forceinline__ void bare_barrier() {
 struct SegStat {
     float m;     // segment maximum
     float s;     // sum 2^((z - m) log2(e)/T) (0 when greedy)
-    int draw;    // entry drawn inside the segment (-1 when no draw)
     int mask;    // bit vb*4 + g: candidate quad (vb, g) was written (in bit order)
+    int pad;
 };
 
 struct HeadArgs {
@@ -107,9 +111,8 @@ struct HeadArgs {
     const uint16_t* w;     // [V, d] bf16
     SegStat* stats;        // [rows][nseg]
     u32x4* cand;           // [rows][nseg][kQuads]: candidate quads (4 logits each), in mask order
-    const uint64_t* seeds;
-    uint64_t step;
-    int M, row0, d, V, nseg, gamma, groups, k;
+    u32x2* gsum;           // [rows][nseg][4]: the segment's eight 16-entry group sums (fp32 pairs)
+    int M, row0, d, V, nseg, groups, k;
     float c2;              // log2(e) / T (0 when greedy)
     int want_exp, want_draw;
 };
@@ -189,6 +192,12 @@ __device__ __forceinline__ int quad_max(int v) {
 // operand fetches from the other slots with waits for every load in flight;
 // the kernel waits for its own loads explicitly.  NT: non-temporal.  m0 (the
 // LDS destination) is declared clobbered, so the compiler keeps nothing there.
+// The backend warns that m0 is a reserved register whose value it will not
+// preserve around the statement; nothing needs it preserved (no other code
+// of this file reads or writes m0, which the codegen tests check), the
+// clobber only tells the compiler that the statement overwrites it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <bool NT>
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
@@ -199,6 +208,7 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, u
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // raw byte buffer over [base, base + bytes)
 __device__ __forceinline__ i32x4 byte_buffer(const void* base, uint32_t bytes) {
@@ -313,20 +323,10 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         }
     };
 
-    // Per-lane constants of the epilogue, fixed before the loop so that no
-    // 64-bit address is carried through it: the row this lane draws the
-    // segment uniform for (row wr*64 + grp*16 + i16) and its generator seed,
-    // and the pass-relative offsets of the lane's rows in the outputs.
-    uint64_t my_seed = 0;
-    int my_b = 0, my_g = 0;
-    if (a.want_draw) {
-        const int rloc = wr * 64 + grp * 16 + i16;
-        const int R = a.row0 + min(rloc, a.M - 1);
-        my_b = R / a.gamma;
-        my_g = R - my_b * a.gamma;
-        my_seed = a.seeds[my_b];
-    }
+    // Pass-relative offsets of the lane's rows in the outputs, fixed before
+    // the loop so that no 64-bit address is carried through it.
     SegStat* const stats_p = a.stats + (size_t)a.row0 * a.nseg;
+    u32x2* const gsum_p = a.gsum + (size_t)a.row0 * a.nseg * 4;
     u32x4* const cand_p = a.cand + (size_t)a.row0 * a.nseg * kQuads;
     const uint32_t lane_row_off = (uint32_t)(wr * 64 + i16) * (uint32_t)a.nseg;
 
@@ -344,14 +344,9 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         // Opaque copies: everything derived from them is computed here, per
         // tile, instead of being hoisted out of the tile loop into registers
         // that would then live through the whole K loop.
-        int g4 = grp << 2, li16 = i16, mb = my_b, mg = my_g, gq = grp;
+        int g4 = grp << 2, li16 = i16, gq = grp;
         uint32_t lro = lane_row_off;
-        uint64_t seed = my_seed;
-        asm volatile("" : "+v"(g4), "+v"(li16), "+v"(mb), "+v"(mg), "+v"(gq), "+v"(lro), "+v"(seed));
-        double u_mine = 0.0;
-        if (a.want_draw)
-            u_mine = philox_uniform(seed, a.step, (uint64_t)mb, (uint64_t)mg,
-                                    3 + 256 * (uint64_t)seg);
+        asm volatile("" : "+v"(g4), "+v"(li16), "+v"(gq), "+v"(lro));
         const float c2 = a.c2;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
@@ -448,61 +443,38 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
                 __builtin_amdgcn_raw_buffer_store_b128(v, rec_rsrc, st_ok ? (int)(at * 16u) : (int)0x7FFFFFF0, 0, 0);
             }
 
-            // segment mass and the draw inside the segment (Z becomes the weights)
+            // segment mass and its 16-entry group sums (Z becomes the weights):
+            // group vb holds quad vb of each of the four lanes; every lane adds
+            // the same operands in the same order, so all four hold
+            // bit-identical sums, and the segment mass is their sum in group order
             float ssum = 0.f;
-            int drawn = -1;
             if (a.want_exp) {
                 const float mc = mx * c2;
 #pragma unroll
                 for (int i = 0; i < 32; ++i) Z(i) = fast_exp2(__builtin_fmaf(Z(i), c2, -mc));
-                float pre[8], qs[8];
-                float base = 0.f;
+                float gs[8];
 #pragma unroll
                 for (int vb = 0; vb < 8; ++vb) {
-                    qs[vb] = ((Z(vb * 4) + Z(vb * 4 + 1)) + Z(vb * 4 + 2)) + Z(vb * 4 + 3);
-                    float tot;
-                    pre[vb] = base + quad_scan(qs[vb], gq, tot);
-                    base += tot;
+                    const float qs = ((Z(vb * 4) + Z(vb * 4 + 1)) + Z(vb * 4 + 2)) + Z(vb * 4 + 3);
+                    float lo, hi;
+                    lo_hi<16>(qs, lo, hi);
+                    const float pair = lo + hi;
+                    lo_hi<32>(pair, lo, hi);
+                    gs[vb] = lo + hi;
+                    ssum += gs[vb];
                 }
-                ssum = base;
-                if (a.want_draw) {
-                    const double u = __shfl(u_mine, li16 + 16 * rb);
-                    const float tgt = (float)(u * (double)ssum);
-                    // the lane's first quad whose running sum passes the target, and
-                    // its last quad with positive mass (the fallback when rounding
-                    // leaves no crossing)
-                    int fq = -1, lq = -1;
+                if (a.want_draw && live) {
+                    // lane gq stores groups 2 gq and 2 gq + 1
+                    float e0 = gs[0], e1 = gs[1];
 #pragma unroll
-                    for (int vb = 7; vb >= 0; --vb) {
-                        fq = (qs[vb] > 0.f && pre[vb] + qs[vb] > tgt) ? vb : fq;
-                        lq = (lq < 0 && qs[vb] > 0.f) ? vb : lq;
+                    for (int q = 1; q < 4; ++q) {
+                        e0 = gq == q ? gs[2 * q] : e0;
+                        e1 = gq == q ? gs[2 * q + 1] : e1;
                     }
-                    const int sq = fq >= 0 ? fq : lq;
-                    float w4[4] = {0.f, 0.f, 0.f, 0.f}, p0 = 0.f;
-#pragma unroll
-                    for (int vb = 0; vb < 8; ++vb) {
-                        const bool on = vb == sq;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w4[e] = on ? Z(vb * 4 + e) : w4[e];
-                        p0 = on ? pre[vb] : p0;
-                    }
-                    int first = kNone, last = -1;
-                    float part = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        part = e == 0 ? w4[0] : part + w4[e];
-                        const int o = sq * 16 + g4 + e;
-                        const bool pos = w4[e] > 0.f;
-                        last = pos ? o : last;
-                        first = (fq >= 0 && pos && first == kNone && p0 + part > tgt) ? o : first;
-                    }
-                    if (sq < 0) last = -1;
-                    first = quad_min(first);
-                    last = quad_max(last);
-                    drawn = vseg + (first != kNone ? first : last);
+                    gsum_p[(size_t)so * 4 + gq] = u32x2{__float_as_uint(e0), __float_as_uint(e1)};
                 }
             }
-            if (live && gq == 0) stats_p[so] = SegStat{mx, ssum, drawn, (int)mask};
+            if (live && gq == 0) stats_p[so] = SegStat{mx, ssum, (int)mask, 0};
 #undef Z
         }
     };
@@ -543,6 +515,10 @@ constexpr int kFinMaxSeg = 8192;  // segments per row the finalize stages in LDS
 struct FinArgs {
     const SegStat* stats;
     const u32x4* cand;
+    const u32x2* gsum;
+    const uint16_t* h;     // [rows, d] bf16: recomputes the logits of the drawn group
+    const uint16_t* w;     // [V, d] bf16
+    int d;
     const uint64_t* seeds;
     uint64_t step;
     int nseg, gamma, k, V;
@@ -617,6 +593,9 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     __shared__ float sv[kFinThreads / 64];
     __shared__ int si[kFinThreads / 64];
     __shared__ double sd[kFinThreads / 64];
+    __shared__ float s_z[kGrpW];
+    __shared__ double s_tg;
+    __shared__ int s_v0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t R = blockIdx.x;
     const SegStat* st = a.stats + R * a.nseg;
@@ -815,25 +794,121 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     const int b = (int)(R / a.gamma), g = (int)(R % a.gamma);
     const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)g, kDraftDraw);
     const double tgt = u * total;
+    // the segment J where the running mass (vocabulary order) first exceeds
+    // u S, or the last segment with mass when rounding leaves no crossing;
+    // each thread notes the mass before its own candidates
     int first = kNone, last = -1;
+    double before_first = 0.0, before_last = 0.0;
     double cum = excl;
     for (int j = j0; j < j1; ++j) {
         const double sj = seg_mass(s_s[j], s_m[j], mx, a.c2);
-        cum += sj;
         if (sj > 0.0) {
+            if (cum + sj > tgt && first == kNone) { first = j; before_first = cum; }
             last = j;
-            if (cum > tgt && first == kNone) first = j;
+            before_last = cum;
         }
+        cum += sj;
     }
+    const int my_first = first, my_last = last;
     first = block_min(first, si);
     last = -block_min(-last, si);
     int J = first != kNone ? first : last;
     if (J < 0) J = 0;  // no positive mass (non-finite logits): any segment, never out of range
-    if (tid == 0) a.draft[R] = st[J].draw;
+    if (j0 <= J && J < j1) {
+        // the thread whose run holds J: the group inside J, from J's eight
+        // group sums (in units of J's weights 2^((z - m_J) c2))
+        const double before_J = J == my_first ? before_first : (J == my_last ? before_last : 0.0);
+        const double t = (tgt - before_J) / exp2(((double)s_m[J] - (double)mx) * a.c2);
+        const u32x2* gp = a.gsum + ((size_t)R * a.nseg + J) * 4;
+        float gs[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 x = gp[q];
+            gs[2 * q] = __uint_as_float(x[0]);
+            gs[2 * q + 1] = __uint_as_float(x[1]);
+        }
+        int G = -1, Gl = -1;
+        double bG = 0.0, bGl = 0.0, c = 0.0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (gs[q] > 0.f) {
+                if (G < 0 && c + (double)gs[q] > t) { G = q; bG = c; }
+                Gl = q;
+                bGl = c;
+            }
+            c += (double)gs[q];
+        }
+        if (G < 0) { G = Gl < 0 ? 0 : Gl; bG = Gl < 0 ? 0.0 : bGl; }
+        s_v0 = J * kSegW + G * kGrpW;
+        s_tg = t - bG;
+    }
+    __syncthreads();
+    // the group's 16 logits, recomputed: wave w takes entries 4w .. 4w+3, each
+    // lane a strided set of 16-byte chunks of the hidden row and weight rows
+    // (entries past the vocabulary read its last row and weigh nothing)
+    const int v0 = s_v0;
+    const uint16_t* hr = a.h + R * (size_t)a.d;
+    const uint16_t* wr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wr[e] = a.w + (size_t)min(v0 + wave * 4 + e, a.V - 1) * a.d;
+    // batches of kRecU chunks per lane, all loads of a batch issued together
+    // (chunk indices clamped into the row; the clamped ones are not added)
+    constexpr int kRecU = 5;
+    const int nch = a.d / 8;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = lane; c0 < nch; c0 += 64 * kRecU) {
+        u32x4 hv[kRecU], wv[kRecU][4];
+#pragma unroll
+        for (int u = 0; u < kRecU; ++u) {
+            const int c = min(c0 + 64 * u, nch - 1);
+            hv[u] = *reinterpret_cast<const u32x4*>(hr + c * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[u][e] = *reinterpret_cast<const u32x4*>(wr[e] + c * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < kRecU; ++u) {
+            if (c0 + 64 * u >= nch) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    part[e] = __builtin_fmaf(__uint_as_float(hv[u][q] << 16),
+                                             __uint_as_float(wv[u][e][q] << 16), part[e]);
+                    part[e] = __builtin_fmaf(__uint_as_float(hv[u][q] & 0xFFFF0000u),
+                                             __uint_as_float(wv[u][e][q] & 0xFFFF0000u), part[e]);
+                }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] = wave_sum(part[e]);
+    if (lane == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_z[wave * 4 + e] = part[e];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        // the entry of the group where the running weight first passes the
+        // rest of the target (weights by the epilogue's own formula)
+        const float c2f = (float)a.c2;
+        const float mc = s_m[J] * c2f;
+        const double tg = s_tg;
+        double acc = 0.0;
+        int pick = -1, lastp = -1;
+        for (int e = 0; e < kGrpW; ++e) {
+            const int v = v0 + e;
+            const float wgt = v < a.V ? fast_exp2(__builtin_fmaf(s_z[e], c2f, -mc)) : 0.f;
+            if (wgt > 0.f) {
+                acc += (double)wgt;
+                lastp = v;
+                if (pick < 0 && acc > tg) pick = v;
+            }
+        }
+        a.draft[R] = pick >= 0 ? pick : (lastp >= 0 ? lastp : min(v0, a.V - 1));
+    }
 }
 
 struct HeadLayout {
-    size_t stats, cand, bytes;
+    size_t stats, cand, gsum, bytes;
 };
 
 HeadLayout head_layout(int rows, int vocab) {
@@ -842,6 +917,7 @@ HeadLayout head_layout(int rows, int vocab) {
     Carve c;
     L.stats = c.take<SegStat>((size_t)rows * nseg);
     L.cand = c.take<u32x4>((size_t)rows * nseg * kQuads);
+    L.gsum = c.take<u32x2>((size_t)rows * nseg * 4);
     L.bytes = c.total();
     return L;
 }
@@ -894,12 +970,10 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     ha.w = w_head;
     ha.stats = reinterpret_cast<SegStat*>(ws + L.stats);
     ha.cand = reinterpret_cast<u32x4*>(ws + L.cand);
-    ha.seeds = seeds;
-    ha.step = step;
+    ha.gsum = reinterpret_cast<u32x2*>(ws + L.gsum);
     ha.d = d_model;
     ha.V = vocab;
     ha.nseg = nseg;
-    ha.gamma = gamma;
     ha.groups = min(kHeadCUs, (nseg + 1) / 2);
     ha.k = k;
     ha.c2 = sample ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
@@ -915,6 +989,10 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     FinArgs fa{};
     fa.stats = ha.stats;
     fa.cand = ha.cand;
+    fa.gsum = ha.gsum;
+    fa.h = hidden;
+    fa.w = w_head;
+    fa.d = d_model;
     fa.seeds = seeds;
     fa.step = step;
     fa.nseg = nseg;

@@ -29,6 +29,7 @@
 #include <cmath>
 
 #include "common.hpp"
+#include "verify_run.hpp"
 
 namespace dfl {
 namespace {
@@ -1003,22 +1004,31 @@ extern "C" size_t spec_verify_workspace_size(int batch, int gamma, int vocab) {
     return verify_layout(batch, gamma, vocab).bytes;
 }
 
-extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
-                           const int32_t* draft_tokens, const double* draft_lse,
-                           float temperature, const uint64_t* seeds, uint64_t step,
-                           int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
-                           int batch, int gamma, int vocab, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace dfl {
+
+int verify_check(const float* target_logits, const int32_t* draft_tokens, float temperature,
+                 const uint64_t* seeds, const int32_t* accept_len, const int32_t* out_tokens,
+                 int batch, int gamma, int vocab) {
     if (batch < 0 || gamma < 1 || vocab < 1) return DFLASH_ERR_SHAPE;
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
     if (batch == 0) return DFLASH_OK;
     if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_ERR_NULL;
     if (temperature > 0.f && !seeds) return DFLASH_ERR_NULL;
     if (gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab) return DFLASH_ERR_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
+size_t verify_scratch_bytes(int batch, int gamma, int vocab) {
+    return verify_layout(batch, gamma, vocab).bytes;
+}
+
+int verify_enqueue(const float* target_logits, const float* draft_logits,
+                   const int32_t* draft_tokens, const double* draft_lse, float temperature,
+                   const uint64_t* seeds, uint64_t step, int32_t* accept_len, int32_t* out_tokens,
+                   uint8_t* accepted, int batch, int gamma, int vocab, void* scratch_ws,
+                   hipStream_t st) {
     const VerifyLayout L = verify_layout(batch, gamma, vocab);
-    if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(scratch_ws);
     const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
     VerifyArgs v{};
     v.zp = target_logits; v.zq = draft_logits; v.drafts = draft_tokens; v.draft_lse = draft_lse;
@@ -1061,4 +1071,22 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     if (rc) return rc;
     hipLaunchKernelGGL(verify_draw_kernel, dim3(batch), dim3(64), 0, st, v);
     return launch_status();
+}
+
+}  // namespace dfl
+
+extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, const double* draft_lse,
+                           float temperature, const uint64_t* seeds, uint64_t step,
+                           int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
+                           int batch, int gamma, int vocab, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const int rc = verify_check(target_logits, draft_tokens, temperature, seeds, accept_len,
+                                out_tokens, batch, gamma, vocab);
+    if (rc || batch == 0) return rc;
+    if (!ws_ok(workspace, workspace_bytes, verify_scratch_bytes(batch, gamma, vocab)))
+        return DFLASH_ERR_WORKSPACE;
+    return verify_enqueue(target_logits, draft_logits, draft_tokens, draft_lse, temperature, seeds,
+                          step, accept_len, out_tokens, accepted, batch, gamma, vocab, workspace,
+                          reinterpret_cast<hipStream_t>(stream));
 }

@@ -310,13 +310,13 @@ int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int b
  *   lse      [rows] float64, log sum_v exp(z_v / T) (T > 0; NaN when T == 0);
  *            may be NULL.
  *   draft    [rows] int32; may be NULL.  T == 0: the row's argmax (lowest
- *            index among equal maxima).  T > 0: an exact draw from
- *            softmax(z / T) in two inverse-CDF steps over consecutive
- *            128-entry vocabulary segments: the segment J by the segment
- *            masses at the purpose-0 uniform of (seeds[b], step, b, r % gamma),
- *            then the entry inside J by its weights at the uniform of purpose
- *            3 + 256 J.  (A different realization than dflash_topk's
- *            single-step draw with the same seeds; the same distribution.)
+ *            index among equal maxima).  T > 0: a draw from softmax(z / T) by
+ *            inverse CDF over the whole row in increasing vocabulary order
+ *            with the purpose-0 uniform of (seeds[b], step, b, r % gamma),
+ *            b = r / gamma: the same rule, and with the same seeds the same
+ *            token, as dflash_topk on these logits (up to the rounding of
+ *            the logits).  The finalize recomputes the 16 logits of the
+ *            group holding the crossing from hidden and w_head.
  *   seeds    [rows / gamma rounded up] uint64 (device); may be NULL when
  *            T == 0 or draft == NULL.
  * Work: the weights are streamed from HBM once per 256 rows of hidden.

@@ -38,3 +38,23 @@ def test_no_generic_or_private_addressing(src):
         if ins.startswith(("flat_", "scratch_", "s_swappc")):
             bad.setdefault(fn, set()).add(ins)
     assert not bad, f"{src}: {bad}"
+
+
+def test_lm_head_m0_is_written_only_for_its_lds_dma():
+    """The LM head's LDS DMA is inline assembly that sets m0 (the LDS
+    destination) itself.  Nothing else in that file may read or write m0, so
+    no compiler-held value there can be overwritten: every m0 write is
+    immediately followed by the DMA that reads it."""
+    lines = [l.strip() for l in device_asm("lm_head.hip").splitlines()]
+    ins = [l for l in lines if l and not l.startswith((";", ".", "_")) and not l.endswith(":")]
+    writes = 0
+    for i, l in enumerate(ins):
+        if "m0" not in l.split(";")[0]:
+            continue
+        op = l.split()[0]
+        if op == "s_mov_b32" and l.split()[1].rstrip(",") == "m0":
+            writes += 1
+            assert i + 1 < len(ins) and re.match(r"buffer_load_dwordx4 .* lds", ins[i + 1]), ins[i + 1]
+        else:
+            raise AssertionError(f"unexpected m0 use: {l}")
+    assert writes > 0
