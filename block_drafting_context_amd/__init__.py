@@ -23,6 +23,7 @@ __all__ = [
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk", "dflash_lm_head_topk_workspace_size",
     "dflash_top_p_mask",
+    "spec_verify_noalloc", "spec_verify_noalloc_max_scratch",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk_workspace_size", "dflash_lm_head_topk",
     "dflash_top_p_mask",
+    "spec_verify_noalloc_max_scratch", "spec_verify_noalloc",
 )
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
@@ -81,6 +83,9 @@ def load():
         "dflash_top_p_mask": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
         "dflash_lm_head_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp]),
+        "spec_verify_noalloc_max_scratch": (_sz, []),
+        "spec_verify_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
+                                     _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -241,6 +246,35 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=No
           _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
           _ptr(out_tok), _ptr(accepted), B, G, V, _ptr(ws), wsb, _stream(stream))
     return {"accept_len": acc_len, "out_tokens": out_tok, "accepted": accepted[:, :G - 1]}
+
+
+def spec_verify_noalloc_max_scratch():
+    return int(load().spec_verify_noalloc_max_scratch())
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, outputs,
+                        seeds=None, step=0, draft_lse=None, stream=None):
+    """spec_verify with the library's static per-GPU scratch instead of a workspace: the
+    call allocates nothing, so the caller passes every output (dict accept_len [B] int32,
+    out_tokens [B,G] int32, accepted [B,G-1] uint8).  Calls that overlap on one GPU race."""
+    B, G, V = target_logits.shape
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, G, V), dev)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, (B, G, V), dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
+    if draft_lse is not None:
+        _need(draft_lse, "draft_lse", torch.float64, (B, G), dev)
+    if seeds is not None:
+        _need(seeds, "seeds", torch.int64, (B,), dev)
+    acc_len, out_tok, accepted = outputs["accept_len"], outputs["out_tokens"], outputs["accepted"]
+    _need(acc_len, "accept_len", torch.int32, (B,), dev)
+    _need(out_tok, "out_tokens", torch.int32, (B, G), dev)
+    _need(accepted, "accepted", torch.uint8, (B, max(G - 1, 1)), dev)
+    _call("spec_verify_noalloc", _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+          _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
+          _ptr(out_tok), _ptr(accepted), B, G, V, _stream(stream))
+    return outputs
 
 
 # ------------------------------------------------------------------- selector

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdflash.so")
 SOURCES = ["block_attn.hip", "vocab_rows.hip", "context_fuse.hip", "select_path.hip", "two_tap_conv.hip",
-           "lm_head.hip", "top_p.hip",
+           "lm_head.hip", "top_p.hip", "noalloc.hip",
            "status.cpp"]
 
 # Device code generation: no packed-fp32 instructions anywhere (the host pass

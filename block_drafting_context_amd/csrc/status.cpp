@@ -9,6 +9,7 @@ extern "C" const char* dflash_status_string(int status) {
         case DFLASH_ERR_UNSUPPORTED: return "configuration outside what this build supports";
         case DFLASH_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case DFLASH_ERR_HIP: return "HIP launch failed";
+        case DFLASH_ERR_TOO_LARGE: return "needs more scratch than the static array holds";
         default: return "unknown status";
     }
 }

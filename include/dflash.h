@@ -68,6 +68,7 @@ extern "C" {
 #define DFLASH_ERR_UNSUPPORTED  -3  /* valid, but outside what this build runs  */
 #define DFLASH_ERR_WORKSPACE    -4  /* workspace NULL, misaligned or too small  */
 #define DFLASH_ERR_HIP          -5  /* a HIP launch failed                      */
+#define DFLASH_ERR_TOO_LARGE    -6  /* needs more scratch than the static array holds */
 
 /* Element types of dflash_block_attn's Q/K/V/output tensors. */
 #define DFLASH_DTYPE_BF16 0
@@ -359,6 +360,30 @@ int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows
  * ------------------------------------------------------------------------ */
 int dflash_top_p_mask(const float* logits, float* out, int32_t* kept, int rows, int vocab,
                       float temperature, float top_p, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments and results as
+ * spec_verify, with no workspace argument.
+ *
+ * The scratch is a fixed array of spec_verify_noalloc_max_scratch() bytes
+ * (8 MiB) in device memory, one per GPU, allocated with the library's code
+ * object and held until the process ends; the call itself allocates nothing.
+ * A shape whose scratch (spec_verify_workspace_size) exceeds it returns
+ * DFLASH_ERR_TOO_LARGE before any HIP call (B = 32, gamma = 8 at 151,936
+ * entries needs about 0.5 MiB).  `stream` must belong to the device current
+ * on the calling thread.  Every call on one GPU uses that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress); DFLASH_ERR_HIP if that fails.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_noalloc_max_scratch(void);
+int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
+                        const int32_t* draft_tokens, const double* draft_lse,
+                        float temperature, const uint64_t* seeds, uint64_t step,
+                        int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
+                        int batch, int gamma, int vocab, void* stream);
 
 #ifdef __cplusplus
 }

@@ -287,3 +287,29 @@ def test_binding_checks_workspace_dtype_and_device():
     with pytest.raises(TypeError):
         dfl.dflash_topk(zq, 4, 0.7, seeds=seeds,
                         workspace=torch.zeros(1 << 20, dtype=torch.int32))
+
+
+def verify_na(**kw):
+    a = dict(zp=P, zq=P, d=P, lse=None, T=0.7, seeds=P, step=0, j=P, out=P, acc=None, B=2, G=8,
+             V=151936, st=None)
+    a.update(kw)
+    return dfl.load().spec_verify_noalloc(a["zp"], a["zq"], a["d"], a["lse"], a["T"], a["seeds"],
+                                          a["step"], a["j"], a["out"], a["acc"], a["B"], a["G"],
+                                          a["V"], a["st"])
+
+
+def test_verify_noalloc_validation_before_any_hip_call():
+    """Same checks as spec_verify, then the static scratch's limit, all before
+    the first HIP call (no GPU here)."""
+    assert verify_na(B=0) == 0
+    assert verify_na(zp=None) == -1
+    assert verify_na(seeds=None) == -1
+    assert verify_na(G=0) == -2
+    assert verify_na(T=-1.0) == -2
+    assert verify_na(G=33) == -3
+    assert verify_na(V=1001) == -3
+    cap = dfl.spec_verify_noalloc_max_scratch()
+    assert cap == 8 << 20
+    assert dfl.spec_verify_workspace_size(1024, 32, 151936) > cap
+    assert verify_na(B=1024, G=32) == -6
+    assert dfl.dflash_status_string(-6) != "unknown status"
