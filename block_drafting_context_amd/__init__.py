@@ -125,11 +125,12 @@ def _need(t, name, dtype, shape=None, device=None):
 
 
 def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, device)
     if nbytes == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    _need(workspace, "workspace", torch.uint8, None, device)
     if workspace.numel() < nbytes:
         raise ValueError(f"workspace too small: {workspace.numel()} < {nbytes}")
     return workspace, workspace.numel()

@@ -8,24 +8,38 @@
 // corrects the first rejection from [p - q]_+ and adds a bonus token when
 // every draft survives.
 //
-// Every pass over a row is one streaming read, split into 2,048-element
-// segments.  A wave owns a run of consecutive segments of one row and, per
-// segment, holds all 32 of each lane's elements in registers (8 float4
-// loads issued together), so it can take an exact wave-uniform segment
-// maximum m_s before exponentiating.  Per segment it can produce
-//   * m_s, and s_s = sum 2^((z - m_s) * log2(e)/T)   (fp32 pairwise sums,
-//     fp64 across), or
-//   * the wave's argmax.
-// Top-k needs only the segment maxima from the streaming pass: tau = the k-th
-// largest m_s of the row (counting repeats) is a lower bound of the row's k-th
-// largest entry, since those k maxima are k distinct entries, so every top-k
-// entry lies in a segment with m_s >= tau.  The finalize re-reads just those
-// segments (about k of them) with tau as the first filter: entries that can
-// still rank are compacted into an LDS buffer, whose list is rebuilt by k
-// rounds of a wave-wide (value desc, index asc) reduction when it fills.
-// An inverse-CDF draw needs only the segment sums plus one re-read of the
-// single 2,048-element segment holding the crossing, recomputing the element
-// weights with exactly the arithmetic that produced the sums.
+// One workgroup of 16 waves streams one row, split into 2,048-element
+// segments; each wave owns a contiguous run of segments and, per segment,
+// holds all 32 of each lane's elements in registers (8 float4 loads issued
+// together), so it can take an exact wave-uniform segment maximum m_s before
+// exponentiating.  Per segment it produces m_s and, at T > 0,
+// s_s = sum 2^((z - m_s) * log2(e)/T) (fp32 pairwise sums, fp64 across); the
+// greedy verify scan takes each wave's argmax instead.
+//
+// dflash_topk is one launch: after the scan the same workgroup finishes its
+// row.  tau = the k-th largest m_s of the row (counting repeats) is a lower
+// bound of the row's k-th largest entry, since those k maxima are k distinct
+// entries, so every top-k entry lies in a segment with m_s >= tau; fifteen
+// waves re-read just those segments (about k of them) with tau as the first
+// filter, keeping the entries that can still rank in LDS buffers, whose lists
+// are rebuilt by k rounds of a wave-wide (value desc, index asc) reduction
+// when they fill; the sixteenth wave meanwhile merges the segment statistics
+// into the log-normaliser and draws: an inverse-CDF draw needs only the
+// segment sums plus one re-read of the single segment holding the crossing,
+// recomputing the element weights with exactly the arithmetic that produced
+// the sums.
+//
+// spec_verify is three launches: the row scan (per-row max and fp64
+// exp-sum, or argmax, and the segment statistics the draws use); a tail with
+// a group of workgroups per sequence, each of which takes the same accept
+// decisions from the row statistics (the same arithmetic on the same values,
+// so they agree), the first writing the committed tokens and drawing the
+// bonus token, and, when a draft was rejected, each wave summing the residual
+// [p - q]_+ over one segment of the rejected row; then the correction draw,
+// one wave per rejecting sequence.  (Handing the sums to the last workgroup
+// of a sequence through a per-sequence atomic counter instead was slower:
+// the counters serialise and the device-scope handoff costs a memory round
+// trip per wave.)
 #include <cmath>
 
 #include "common.hpp"
@@ -38,25 +52,18 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSeg = 2048;             // elements per segment (8 x 64 lanes x 4)
 constexpr int kIters = kSeg / 256;     // float4 loads per lane per segment
+constexpr int kRowWaves = 16;          // waves per row workgroup
+constexpr int kRowThreads = 64 * kRowWaves;
+constexpr int kFinWaves = kRowWaves - 1;  // top-k candidate waves (the last one draws)
 constexpr int kCap = 256;              // top-k candidate buffer fill that triggers a rebuild
 constexpr int kBuf = kCap + 256;       // buffer size: one load group (4 x 64) of slack
-constexpr int kScanWaves = 4;          // waves per workgroup
-constexpr int kFinWaves = 4;           // waves per top-k finalize workgroup (one row)
-constexpr int kTargetWaves = 3072;     // waves per row-scan launch (~12 per CU)
+constexpr int kMaxTopkSeg = 4096;      // top-k: segment statistics held in LDS (V <= 2^23)
+constexpr int kTailWaves = 4;          // waves per verification tail workgroup
 constexpr int kRsrcWord3 = 0x00020000; // buffer resource word 3 for raw byte buffers on gfx9 parts
 constexpr int kMaxVocab = 1 << 29;     // a row's bytes, and a segment past it, fit 32-bit offsets
+constexpr int kMaxTopkVocab = kMaxTopkSeg * kSeg;
 
 enum : int { kArgmax = 1, kSumExp = 2, kSegMax = 4 };
-
-struct ScanArgs {
-    const float* z;  // [rows, V]
-    int rows, V, nseg, spw, wpr;
-    float c2;        // log2(e) / T
-    float* seg_m;    // [rows][nseg]
-    double* seg_s;   // [rows][nseg]
-    float* cand_v;   // [rows][wpr]: each wave's argmax
-    int* cand_i;
-};
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -70,95 +77,51 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ------------------------------------------------------- wave top-k state
-// Per-wave state of the candidate search.  The LDS arrays are indexed
-// directly from the kernel's __shared__ declarations (never through generic
-// pointers), and the scalars live in registers, so every access is a ds_*
-// instruction with a compile-time address space.
-constexpr int kNPL = (64 + kBuf + 63) / 64;  // candidates per lane in a rebuild
-
-struct TopKRegs {
-    int cnt;     // buffer fill (wave-uniform)
-    int lcount;  // list length (wave-uniform)
-    float tv;    // filter: a quad is appended when its maximum is >= tv
-};
-
-// Rebuild the sorted list of `wave` from list + buffer: k rounds of a
-// wave-wide (value desc, index asc) reduction.
-// Entries below `floor` are known not to rank, so the filter never drops under it.
-__device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (*li)[64],
-                                             float (*bv)[kBuf], int (*bi)[kBuf], int wave, int k,
-                                             int lane, float floor) {
-    wave_lds_sync();
-    const int N = s.lcount + s.cnt;
-    float cv[kNPL];
-    int ci[kNPL];
-#pragma unroll
-    for (int e = 0; e < kNPL; ++e) {
-        const int at = e * 64 + lane;
-        if (at < s.lcount) { cv[e] = lv[wave][at]; ci[e] = li[wave][at]; }
-        else if (at < N) { cv[e] = bv[wave][at - s.lcount]; ci[e] = bi[wave][at - s.lcount]; }
-        else { cv[e] = -INFINITY; ci[e] = -1; }
-    }
-    wave_lds_sync();
-    const int newcount = N < k ? N : k;
-    float lastv = -INFINITY;
-    for (int r = 0; r < newcount; ++r) {
-        float b_v = cv[0];
-        int b_i = ci[0];
-#pragma unroll
-        for (int e = 1; e < kNPL; ++e)
-            if (ranks_ahead(cv[e], ci[e], b_v, b_i)) { b_v = cv[e]; b_i = ci[e]; }
-        wave_best(b_v, b_i);
-#pragma unroll
-        for (int e = 0; e < kNPL; ++e)
-            if (ci[e] == b_i && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
-        if (lane == 0) { lv[wave][r] = b_v; li[wave][r] = b_i; }
-        lastv = b_v;
-    }
-    wave_lds_sync();
-    s.lcount = newcount;
-    s.cnt = 0;
-    s.tv = newcount == k ? fmaxf(lastv, floor) : floor;
+// raw buffer over one row (V % 4 == 0, V <= 2^29: V * 4 bytes fit 32 bits)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* zr, int V) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(zr), (short)0,
+                                             (int)((uint32_t)V * 4u), kRsrcWord3);
 }
 
-template <int MODE>
-__global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kScanWaves + wave;
-    const int row = gw / a.wpr, wr = gw % a.wpr;
-    if (row >= a.rows) return;
-    const int seg0 = wr * a.spw;
-    const int seg1 = min(seg0 + a.spw, a.nseg);
-    const float* zr = a.z + (size_t)row * a.V;
-
-    float best_v = -INFINITY;
-    int best_i = -1;
-
-    // The 32 elements of this lane in segment `seg`: base + it*256 + c.  The
-    // row is read through a raw buffer of V*4 bytes, so every load is issued
-    // unconditionally: a quad past the row's end (V % 4 == 0, so quads are
-    // whole) or of a segment past this wave's run reads as zeros without
-    // touching memory, and the compiler counts the loads in flight exactly
-    // (with the loads in branches it waited for all of them, the next
-    // segment's prefetch included, before processing the current one).
-    const __amdgpu_buffer_rsrc_t zr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(zr), (short)0, a.V * 4, kRsrcWord3);
-    auto load = [&](f32x4 (&vv)[kIters], int seg) {
-        const uint32_t base = (uint32_t)(seg * kSeg + 4 * lane) * 4u;  // < 2^32: V <= 2^29
+// The 32 elements of this lane in segment `seg`: base + it*256 + c.  Every
+// load is issued unconditionally: a quad past the row's end (V % 4 == 0, so
+// quads are whole) or of a segment past a wave's run reads as zeros without
+// touching memory, and the compiler counts the loads in flight exactly.
+__device__ __forceinline__ void load_segment(f32x4 (&v)[kIters], __amdgpu_buffer_rsrc_t rsrc, int seg,
+                                             int lane) {
+    const uint32_t base = (uint32_t)(seg * kSeg + 4 * lane) * 4u;  // < 2^32: V <= 2^29
 #pragma unroll
-        for (int it = 0; it < kIters; ++it)
-            // logits rows are streamed once: non-temporal loads
-            vv[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  zr_rsrc, (int)(base + it * 1024u), 0, kLoadStream));
-    };
+    for (int it = 0; it < kIters; ++it)
+        // logits rows are streamed once: non-temporal loads
+        v[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsrc, (int)(base + it * 1024u), 0, kLoadStream));
+}
+
+// ------------------------------------------------------------ row scan
+// Wave `wave` of a row workgroup streams its run of segments and stores each
+// segment's maximum (and, with kSumExp, its exp-sum) through lane 0 into
+// sm[seg] / ss[seg] (LDS or global); with kArgmax it keeps its argmax.
+// hook(v, qm, seg) then sees the segment's values (entries past the row's end
+// set to -inf) and the lane's quad maxima qm[it] = max of v[it].
+struct NoHook {
+    __device__ __forceinline__ void operator()(f32x4 (&)[kIters], const float (&)[kIters], int) const {}
+};
+template <int MODE, class MArr, class SArr, class Hook = NoHook>
+__device__ __forceinline__ void scan_row(const float* zr, int V, int nseg, float c2, MArr sm, SArr ss,
+                                         float& best_v, int& best_i, int wave, int lane,
+                                         Hook hook = Hook()) {
+    const int seg0 = (int)((long)wave * nseg / kRowWaves);
+    const int seg1 = (int)((long)(wave + 1) * nseg / kRowWaves);
+    const __amdgpu_buffer_rsrc_t rsrc = row_rsrc(zr, V);
+    best_v = -INFINITY;
+    best_i = -1;
     auto process = [&](f32x4 (&v)[kIters], int seg) {
         const int base = seg * kSeg + 4 * lane;
-        if (seg * kSeg + kSeg > a.V) {
+        if (seg * kSeg + kSeg > V) {
             // quads past the row's end read as zeros: they take no part
 #pragma unroll
             for (int it = 0; it < kIters; ++it)
-                if (base + it * 256 >= a.V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                if (base + it * 256 >= V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
         if (MODE & kArgmax) {
 #pragma unroll
@@ -167,20 +130,16 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                 for (int c = 0; c < 4; ++c)
                     if (v[it][c] > best_v) { best_v = v[it][c]; best_i = base + it * 256 + c; }
         }
-        float lane_m = -INFINITY;
-        if (MODE & (kSumExp | kSegMax)) {
+        float qm[kIters];
 #pragma unroll
-            for (int it = 0; it < kIters; ++it)
-                lane_m = fmaxf(lane_m, fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3])));
-        }
-        if (MODE & kSegMax) {
-            const float m = wave_max(lane_m);
-            if (lane == 0) a.seg_m[(size_t)row * a.nseg + seg] = m;
-        }
-        if (MODE & kSumExp) {
+        for (int it = 0; it < kIters; ++it) qm[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3]));
+        if (MODE & (kSumExp | kSegMax)) {
+            float lane_m = -INFINITY;
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) lane_m = fmaxf(lane_m, qm[it]);
             const float m = wave_max(lane_m);
             double sacc = 0.0;
-            if (m != -INFINITY) {
+            if ((MODE & kSumExp) && m != -INFINITY) {
 #pragma unroll
                 for (int h = 0; h < kIters / 2; ++h) {
                     float w[8];
@@ -188,38 +147,30 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
                     for (int q = 0; q < 2; ++q)
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            w[q * 4 + c] = fast_exp2((v[2 * h + q][c] - m) * a.c2);
+                            w[q * 4 + c] = fast_exp2((v[2 * h + q][c] - m) * c2);
                     const float t = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
                     sacc += (double)t;
                 }
             }
-            sacc = wave_sum(sacc);
+            if (MODE & kSumExp) sacc = wave_sum(sacc);
             if (lane == 0) {
-                a.seg_m[(size_t)row * a.nseg + seg] = m;
-                a.seg_s[(size_t)row * a.nseg + seg] = sacc;
+                sm[seg] = m;
+                if (MODE & kSumExp) ss[seg] = sacc;
             }
         }
+        hook(v, qm, seg);
     };
-
     // two segments per trip, each one's loads issued before the other is
     // processed; a segment past the run is loaded from past the row's end
-    const int dead = a.nseg;
+    const int dead = nseg;
     f32x4 va[kIters], vb[kIters];
-    load(va, seg0 < seg1 ? seg0 : dead);
+    load_segment(va, rsrc, seg0 < seg1 ? seg0 : dead, lane);
     for (int seg = seg0; seg < seg1; seg += 2) {
         const bool has_b = seg + 1 < seg1;
-        load(vb, has_b ? seg + 1 : dead);
+        load_segment(vb, rsrc, has_b ? seg + 1 : dead, lane);
         process(va, seg);
-        load(va, seg + 2 < seg1 ? seg + 2 : dead);
+        load_segment(va, rsrc, seg + 2 < seg1 ? seg + 2 : dead, lane);
         if (has_b) process(vb, seg + 1);
-    }
-
-    if (MODE & kArgmax) {
-        wave_best(best_v, best_i);
-        if (lane == 0) {
-            a.cand_v[(size_t)row * a.wpr + wr] = best_v;
-            a.cand_i[(size_t)row * a.wpr + wr] = best_i;
-        }
     }
 }
 
@@ -229,8 +180,9 @@ __global__ void __launch_bounds__(256) row_scan_kernel(ScanArgs a) {
 // first 64 * kStatRegs segments are loaded at once into registers (addresses
 // clamped into the row, so no load sits behind a branch), the rest in a loop.
 constexpr int kStatRegs = 4;
-__device__ __forceinline__ void merge_row_stats(const float* sm, const double* ss, int nseg, float c2, int lane,
-                                float& M, double& S) {
+template <class MArr, class SArr>
+__device__ __forceinline__ void merge_row_stats(MArr sm, SArr ss, int nseg, float c2, int lane, float& M,
+                                                double& S) {
     float mv[kStatRegs];
     double sv[kStatRegs];
 #pragma unroll
@@ -256,20 +208,24 @@ __device__ __forceinline__ void merge_row_stats(const float* sm, const double* s
 }
 
 // Smallest element index of segment `seg` whose running weight (increasing
-// index) exceeds tgt; wfn.w4(v) gives the fp32 weights of elements v..v+3
-// (the same arithmetic that produced the segment sums), summed in fp64.
-// Falls back to the last positive-weight element of the segment when
-// rounding leaves no crossing.  Wave-wide; every lane returns the index.
+// index) exceeds tgt; wfn.load(v) reads what elements v..v+3 need and
+// wfn.w4(raw, v) gives their fp32 weights (the same arithmetic that produced
+// the segment sums), summed in fp64.  Falls back to the last positive-weight
+// element of the segment when rounding leaves no crossing.  Wave-wide; every
+// lane returns the index.
 template <class WFn>
 __device__ __forceinline__ int draw_in_segment(int seg, int V, double tgt, const WFn& wfn, int lane) {
     const int lo = seg * kSeg + lane * 32;
     float w[32];
+    // all eight quads' loads are issued before any is used (raw buffer loads:
+    // a quad past the row's end reads zeros and weighs nothing)
+    typename WFn::Raw raw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) raw[q] = wfn.load(lo + 4 * q);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        // a quad past the row's end reads the last quad (V % 4 == 0) and weighs
-        // nothing, so the eight loads are issued together
         const int v = lo + 4 * q;
-        const f32x4 w4 = wfn.w4(v < V ? v : V - 4);
+        const f32x4 w4 = wfn.w4(raw[q], v);
 #pragma unroll
         for (int c = 0; c < 4; ++c) w[4 * q + c] = v < V ? w4[c] : 0.f;
     }
@@ -341,12 +297,19 @@ __device__ __forceinline__ int find_segment(int nseg, double target, const SegW&
     return last_pos_seg;
 }
 
+// 16 bytes at element v of a row (zeros past its end)
+__device__ __forceinline__ f32x4 load_quad(__amdgpu_buffer_rsrc_t rsrc, int v) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)((uint32_t)v * 4u), 0,
+                                                                           kLoadDefault));
+}
+
 // Weight 2^((z - m_s) * c2) of softmax(z / T) relative to a segment maximum.
 struct SoftmaxW {
-    const float* zr;
+    __amdgpu_buffer_rsrc_t zr;
     float ms, c2;
-    __device__ __forceinline__ f32x4 w4(int v) const {
-        const f32x4 z = *reinterpret_cast<const f32x4*>(zr + v);
+    typedef f32x4 Raw;
+    __device__ __forceinline__ Raw load(int v) const { return load_quad(zr, v); }
+    __device__ __forceinline__ f32x4 w4(const Raw& z, int) const {
         f32x4 r;
         r[0] = fast_exp2((z[0] - ms) * c2);
         r[1] = fast_exp2((z[1] - ms) * c2);
@@ -357,8 +320,9 @@ struct SoftmaxW {
 };
 
 // Draw from softmax(z / T) of one row using its segment statistics.
-__device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const float* sm, const double* ss,
-                                int nseg, float c2, float M, double S, double u, int lane) {
+template <class MArr, class SArr>
+__device__ __forceinline__ int draw_softmax_row(const float* zr, int V, MArr sm, SArr ss, int nseg, float c2,
+                                                float M, double S, double u, int lane) {
     const double target = u * S;
     double before = 0.0;
     auto segw = [&](int s) -> double {
@@ -369,107 +333,167 @@ __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, const fl
     const float ms = sm[seg];
     const double f = (double)fast_exp2((ms - M) * c2);
     const double tgt = (target - before) / f;
-    const SoftmaxW wfn{zr, ms, c2};
+    const SoftmaxW wfn{row_rsrc(zr, V), ms, c2};
     return draw_in_segment(seg, V, tgt, wfn, lane);
 }
 
-// ------------------------------------------------------- top-k finalize
-struct TopKFin {
-    const float* z;
-    int B, G, V, nseg, k;
-    float T, c2;
-    const uint64_t* seeds;
-    uint64_t step;
-    const float* seg_m;
-    const double* seg_s;
-    int32_t* topk_idx;
-    float* topk_val;
-    double* lse;
-    int32_t* draft;
+// ------------------------------------------------------- wave top-k state
+// Per-wave state of the candidate search.  The LDS arrays are indexed
+// directly from the kernel's __shared__ declarations (never through generic
+// pointers), and the scalars live in registers, so every access is a ds_*
+// instruction with a compile-time address space.
+constexpr int kNPL = (64 + kBuf + 63) / 64;  // candidates per lane in a rebuild
+
+struct TopKRegs {
+    int cnt;     // buffer fill (wave-uniform)
+    int lcount;  // list length (wave-uniform)
+    float tv;    // filter: a quad is appended when its maximum is >= tv
 };
 
-constexpr int kSegCache = 4;  // segment maxima per lane held in registers by the finalize
+// Rebuild the sorted list of `wave` from list + buffer: k rounds of a
+// wave-wide (value desc, index asc) reduction.
+// Entries below `floor` are known not to rank, so the filter never drops under it.
+__device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (*li)[64],
+                                             float (*bv)[kBuf], int (*bi)[kBuf], int wave, int k,
+                                             int lane, float floor) {
+    wave_lds_sync();
+    const int N = s.lcount + s.cnt;
+    float cv[kNPL];
+    int ci[kNPL];
+#pragma unroll
+    for (int e = 0; e < kNPL; ++e) {
+        const int at = e * 64 + lane;
+        if (at < s.lcount) { cv[e] = lv[wave][at]; ci[e] = li[wave][at]; }
+        else if (at < N) { cv[e] = bv[wave][at - s.lcount]; ci[e] = bi[wave][at - s.lcount]; }
+        else { cv[e] = -INFINITY; ci[e] = -1; }
+    }
+    wave_lds_sync();
+    const int newcount = N < k ? N : k;
+    float lastv = -INFINITY;
+    for (int r = 0; r < newcount; ++r) {
+        float b_v = cv[0];
+        int b_i = ci[0];
+#pragma unroll
+        for (int e = 1; e < kNPL; ++e)
+            if (ranks_ahead(cv[e], ci[e], b_v, b_i)) { b_v = cv[e]; b_i = ci[e]; }
+        wave_best(b_v, b_i);
+#pragma unroll
+        for (int e = 0; e < kNPL; ++e)
+            if (ci[e] == b_i && ci[e] != -1) { cv[e] = -INFINITY; ci[e] = -1; }
+        if (lane == 0) { lv[wave][r] = b_v; li[wave][r] = b_i; }
+        lastv = b_v;
+    }
+    wave_lds_sync();
+    s.lcount = newcount;
+    s.cnt = 0;
+    s.tv = newcount == k ? fmaxf(lastv, floor) : floor;
+}
 
-// The k-th largest of a row's segment maxima, counting repeats; -inf when
-// fewer than k of them are above -inf.  Each round takes the largest maximum
-// below the previous one and counts its copies, so at most k rounds.  The
-// first 64 * kSegCache maxima come from registers (c), the rest from memory.
-__device__ __forceinline__ float kth_segment_max(const float (&c)[kSegCache], const float* sm, int nseg,
-                                                 int k, int lane) {
+// The k-th largest of a row's segment maxima (LDS), counting repeats; -inf
+// when fewer than k of them are above -inf.  Each round takes the largest
+// maximum below the previous one and counts its copies, so at most k rounds.
+__device__ __forceinline__ float kth_segment_max(const float* sm, int nseg, int k, int lane) {
     float t = INFINITY;
     int counted = 0;
     for (;;) {
         float m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kSegCache; ++j)
-            if (c[j] < t) m = fmaxf(m, c[j]);
-        for (int s = 64 * kSegCache + lane; s < nseg; s += 64) {
+        for (int s = lane; s < nseg; s += 64) {
             const float x = sm[s];
             if (x < t) m = fmaxf(m, x);
         }
         m = wave_max(m);
         if (m == -INFINITY) return -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kSegCache; ++j) counted += __popcll(ballot(c[j] == m));
-        for (int s0 = 64 * kSegCache; s0 < nseg; s0 += 64)
+        for (int s0 = 0; s0 < nseg; s0 += 64)
             counted += __popcll(ballot(s0 + lane < nseg && sm[s0 + lane] == m));
         if (counted >= k) return m;
         t = m;
     }
 }
 
-// One row per workgroup of five waves.  Waves 0-3 find tau; the segments with
-// m_s >= tau are dealt to them in index order (the i-th such segment to wave
-// i mod 4), and each re-reads its segments (two in flight) and keeps a top-k
-// list over the quads whose maximum passes its filter (tau, raised to the
-// wave's own k-th best once it holds k entries).  Meanwhile, at T > 0, wave 4
-// merges the segment statistics into the log-normaliser and draws the drafted
-// token.  Wave 0 then merges the four lists into the row's top-k.
-__global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(TopKFin a) {
+// --------------------------------------------------------------- top-k
+struct TopKArgs {
+    const float* z;
+    int B, G, V, nseg, k;
+    float T, c2;
+    const uint64_t* seeds;
+    uint64_t step;
+    int32_t* topk_idx;
+    float* topk_val;
+    double* lse;
+    int32_t* draft;
+};
+
+// One row per workgroup of sixteen waves: the scan, then waves 0-14 find tau
+// and the top k while wave 15 merges the log-normaliser and draws.
+template <int MODE>
+__global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
+    __shared__ __attribute__((aligned(16))) float s_m[kMaxTopkSeg];
+    __shared__ double s_s[kMaxTopkSeg];
     __shared__ float s_lv[kFinWaves][64];
     __shared__ int s_li[kFinWaves][64];
     __shared__ __attribute__((aligned(16))) float s_bv[kFinWaves][kBuf];
     __shared__ __attribute__((aligned(16))) int s_bi[kFinWaves][kBuf];
     __shared__ int s_len[kFinWaves], s_lc[kFinWaves];
-    const int row = blockIdx.x, lane = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) float f_v[kRowThreads];
+    __shared__ __attribute__((aligned(16))) int f_i[kRowThreads];
+    __shared__ float s_tau;
+    __shared__ int s_nf;
+    const int row = blockIdx.x, lane = threadIdx.x & 63, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = row / a.G, r = row % a.G;
-    const float* sm = a.seg_m + (size_t)row * a.nseg;
     const float* zr = a.z + (size_t)row * a.V;
+    // the draw's uniform depends on no data: computed before the scan
+    const bool draws = wave == kFinWaves && a.T > 0.f && a.draft;
+    const double u_draw = draws ? philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw) : 0.0;
+
+    {
+        float bv;
+        int bi;
+        scan_row<MODE>(zr, a.V, a.nseg, a.c2, s_m, s_s, bv, bi, wave, lane);
+    }
+    if (tid == 0) { s_tau = -INFINITY; s_nf = 0; }
+    __syncthreads();
+
+    // tau: the k-th largest segment maximum counting repeats, i.e. the one
+    // ranked k-1 in (value desc, segment asc) order; each thread ranks its
+    // segments by counting the ones ahead (-inf stays when fewer than k
+    // segments exist).  Rows of more than 1,024 segments take k rounds of a
+    // wave-wide maximum instead.
+    if (a.nseg <= kRowThreads) {
+        if (tid < a.nseg) {
+            const float mt = s_m[tid];
+            int rank = 0;
+            int q = 0;
+            for (; q + 4 <= a.nseg; q += 4) {
+                const f32x4 m4 = *reinterpret_cast<const f32x4*>(&s_m[q]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    rank += (m4[c] > mt || (m4[c] == mt && q + c < tid)) ? 1 : 0;
+            }
+            for (; q < a.nseg; ++q) rank += (s_m[q] > mt || (s_m[q] == mt && q < tid)) ? 1 : 0;
+            if (rank == a.k - 1) s_tau = mt;
+        }
+    } else if (wave == 0) {
+        const float t = kth_segment_max(s_m, a.nseg, a.k, lane);
+        if (lane == 0) s_tau = t;
+    }
+    __syncthreads();
+    const float tau = s_tau;
 
     TopKRegs tk{0, 0, -INFINITY};
-    float tau = -INFINITY;
     if (wave == kFinWaves) {
         if (a.T > 0.f) {
             float M;
             double S;
-            const double* ss = a.seg_s + (size_t)row * a.nseg;
-            merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+            merge_row_stats(s_m, s_s, a.nseg, a.c2, lane, M, S);
             if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
             if (a.draft) {
-                const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw);
-                const int tok = draw_softmax_row(zr, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+                const int tok = draw_softmax_row(zr, a.V, s_m, s_s, a.nseg, a.c2, M, S, u_draw, lane);
                 if (lane == 0) a.draft[row] = tok;
             }
         }
     } else {
-        float cache[kSegCache];
-#pragma unroll
-        for (int j = 0; j < kSegCache; ++j) {
-            const int sj = 64 * j + lane;
-            cache[j] = sj < a.nseg ? sm[sj] : -INFINITY;
-        }
-        tau = kth_segment_max(cache, sm, a.nseg, a.k, lane);
-
-        const __amdgpu_buffer_rsrc_t zr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(zr), (short)0, a.V * 4, kRsrcWord3);
-        auto load = [&](f32x4 (&v)[kIters], int seg) {
-            const uint32_t base = (uint32_t)(seg * kSeg + 4 * lane) * 4u;  // < 2^32: V <= 2^29
-#pragma unroll
-            for (int it = 0; it < kIters; ++it)
-                v[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     zr_rsrc, (int)(base + it * 1024u), 0, kLoadStream));
-        };
+        const __amdgpu_buffer_rsrc_t zr_rsrc = row_rsrc(zr, a.V);
         tk.tv = tau;
         // a lane whose 4 elements of load group `it` include one that can pass
         // the filter appends all 4 (16-byte LDS writes); the rebuild ranks
@@ -524,8 +548,10 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
             }
         };
 
-        // Collect up to 64 of this wave's segments (lane i holds the i-th),
-        // then stream them two at a time; repeat while segments remain.
+        // The segments with m_s >= tau are dealt to the candidate waves in
+        // index order (the i-th to wave i mod kFinWaves).  Collect up to 64 of
+        // this wave's segments (lane i holds the i-th), then stream them two
+        // at a time; repeat while segments remain.
         const int dead = a.nseg;  // a segment past the row's end: loads read zeros
         int s0 = 0, group = 0, dealt = 0;
         uint64_t pick = 0;
@@ -536,10 +562,7 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
                     if (s0 >= a.nseg) break;
                     group = s0;
                     const int sl = s0 + lane;
-                    float m = sl < a.nseg && s0 >= 64 * kSegCache ? sm[sl] : -INFINITY;
-#pragma unroll
-                    for (int j = 0; j < kSegCache; ++j)
-                        if (s0 == 64 * j) m = cache[j];
+                    const float m = sl < a.nseg ? s_m[sl] : -INFINITY;
                     pick = ballot(sl < a.nseg && m >= tau);
                     s0 += 64;
                     continue;
@@ -553,13 +576,13 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
             }
             if (n_own == 0) break;
             f32x4 va[kIters], vb[kIters];
-            load(va, lane_value(my_seg, 0));
+            load_segment(va, zr_rsrc, lane_value(my_seg, 0), lane);
             for (int i = 0; i < n_own; i += 2) {
                 const int sa = lane_value(my_seg, i);
                 const int sb = i + 1 < 64 ? lane_value(my_seg, i + 1) : dead;  // dead past n_own
-                load(vb, sb);
+                load_segment(vb, zr_rsrc, sb, lane);
                 process(va, sa);
-                load(va, i + 2 < 64 ? lane_value(my_seg, i + 2) : dead);
+                load_segment(va, zr_rsrc, i + 2 < 64 ? lane_value(my_seg, i + 2) : dead, lane);
                 if (i + 1 < n_own) process(vb, sb);
             }
             if (n_own < 64) break;
@@ -568,21 +591,67 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
     }
     __syncthreads();
     // A wave's entries are its list (s_lc of them) followed by its buffer.
-    // Usually the four waves hold a few dozen in all; otherwise each wave
-    // first reduces its own to at most k.
+    // When they fit one per thread, the entries >= tau are gathered into one
+    // flat array and each thread ranks one of them by counting the entries
+    // ranked ahead of it: only entries >= tau can rank (tau is at most the
+    // row's k-th largest value), the row's top k are among them (k <= V
+    // entries exist, so no empty ranks), and every index appears once, so the
+    // ranks are 0, 1, ...
     int n_tot = 0;
 #pragma unroll
     for (int w = 0; w < kFinWaves; ++w) n_tot += s_len[w];
-    if (n_tot > 64) {
+    auto emit = [&](int rank, float v, int i) {
+        a.topk_idx[(size_t)row * a.k + rank] = i;
+        a.topk_val[(size_t)row * a.k + rank] = v;
+        if (rank == 0 && a.T == 0.f) {
+            if (a.lse) a.lse[row] = NAN;
+            if (a.draft) a.draft[row] = i;
+        }
+    };
+    if (n_tot <= kRowThreads) {
         if (wave < kFinWaves) {
-            if (tk.cnt > 0) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane, -INFINITY);
-            if (lane == 0) { s_len[wave] = tk.lcount; s_lc[wave] = tk.lcount; }
+            const int len = s_len[wave], lc = s_lc[wave];
+            for (int e0 = 0; e0 < len; e0 += 64) {
+                const int e = e0 + lane;
+                float v = -INFINITY;
+                int i = -1;
+                if (e < len) {
+                    v = e < lc ? s_lv[wave][e] : s_bv[wave][e - lc];
+                    i = e < lc ? s_li[wave][e] : s_bi[wave][e - lc];
+                }
+                const bool keep = e < len && v >= tau && i != -1;
+                const uint64_t m = ballot(keep);
+                int at = 0;
+                if (lane == 0 && m) at = atomicAdd(&s_nf, __popcll(m));
+                at = lane_value(at, 0) + lanes_below(m);
+                if (keep) { f_v[at] = v; f_i[at] = i; }
+            }
         }
         __syncthreads();
-        n_tot = 0;
+        const int nf = s_nf;
+        if (tid < nf) {
+            const float v = f_v[tid];
+            const int i = f_i[tid];
+            int rank = 0;
+            int e = 0;
+            for (; e + 4 <= nf; e += 4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(&f_v[e]);
+                const i32x4 i4 = *reinterpret_cast<const i32x4*>(&f_i[e]);
 #pragma unroll
-        for (int w = 0; w < kFinWaves; ++w) n_tot += s_len[w];
+                for (int c = 0; c < 4; ++c) rank += ranks_ahead(v4[c], i4[c], v, i) ? 1 : 0;
+            }
+            for (; e < nf; ++e) rank += ranks_ahead(f_v[e], f_i[e], v, i) ? 1 : 0;
+            if (rank < a.k) emit(rank, v, i);
+        }
+        return;
     }
+    // many entries (long runs of equal logits): each wave first reduces its
+    // own to at most k, then wave 0 takes k rounds over the lists
+    if (wave < kFinWaves) {
+        if (tk.cnt > 0) topk_compact(tk, s_lv, s_li, s_bv, s_bi, wave, a.k, lane, -INFINITY);
+        if (lane == 0) { s_len[wave] = tk.lcount; s_lc[wave] = tk.lcount; }
+    }
+    __syncthreads();
     if (wave != 0) return;
 
     // entry e of the waves' concatenated entries
@@ -600,36 +669,8 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
             off += s_len[w];
         }
     };
-    auto emit = [&](int rank, float v, int i) {
-        a.topk_idx[(size_t)row * a.k + rank] = i;
-        a.topk_val[(size_t)row * a.k + rank] = v;
-        if (rank == 0 && a.T == 0.f) {
-            if (a.lse) a.lse[row] = NAN;
-            if (a.draft) a.draft[row] = i;
-        }
-    };
-    if (n_tot <= 64) {
-        // One entry per lane.  Only entries >= tau can rank, and the row's
-        // top k are among them (k <= V entries of the row exist, so no empty
-        // ranks); each of those counts the others ranking ahead of it, so the
-        // ranks are 0, 1, ... without repeats (every index appears once).
-        float v;
-        int i;
-        entry(lane, v, i);
-        const bool keep = lane < n_tot && v >= tau && i != -1;
-        uint64_t kept = ballot(keep);
-        int rank = 0;
-        while (kept) {
-            const int j = __builtin_ctzll(kept);
-            kept &= kept - 1;
-            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
-            const int ij = __builtin_amdgcn_readlane(i, j);
-            rank += ranks_ahead(vj, ij, v, i) ? 1 : 0;
-        }
-        if (keep && rank < a.k) emit(rank, v, i);
-        return;
-    }
-    // more than 64 entries (k > 16): k rounds of a wave-wide reduction
+    // k rounds of a wave-wide reduction over the waves' lists (each at most
+    // k <= 64 entries)
     float cv[kFinWaves];
     int ci[kFinWaves];
 #pragma unroll
@@ -649,24 +690,83 @@ __global__ void __launch_bounds__(64 * (kFinWaves + 1)) topk_finalize_kernel(Top
 }
 
 // --------------------------------------------------------- verification
-struct VerifyArgs {
+struct RowArgs {
+    const float* zp;    // target logits [B, G, V]: rows 0 .. rows-1 of the launch
+    const float* zq;    // drafter logits [B, G, V]: rows rows .. 2 rows-1 (log-normaliser only)
+    int rows, V, nseg, B;
+    float c2;
+    float* seg_m;       // [launch rows][nseg]
+    double* seg_s;
+    float* row_M;       // [launch rows]
+    double* row_S;
+    int* row_arg;       // [rows] (greedy)
+};
+
+// Statistics of one target (or drafter) row per workgroup: the segment
+// statistics (global, for the draws) and the row's M and S, or its argmax.
+template <int MODE>
+__global__ void __launch_bounds__(kRowThreads) verify_row_kernel(RowArgs a) {
+    __shared__ float s_v[kRowWaves];
+    __shared__ int s_i[kRowWaves];
+    const int row = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float* zr = row < a.rows ? a.zp + (size_t)row * a.V : a.zq + (size_t)(row - a.rows) * a.V;
+    float* sm = a.seg_m + (size_t)row * a.nseg;
+    double* ss = a.seg_s + (size_t)row * a.nseg;
+    float bv;
+    int bi;
+    scan_row<MODE>(zr, a.V, a.nseg, a.c2, sm, ss, bv, bi, wave, lane);
+    if (MODE & kArgmax) {
+        wave_best(bv, bi);
+        if (lane == 0) { s_v[wave] = bv; s_i[wave] = bi; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float v = s_v[0];
+            int i = s_i[0];
+#pragma unroll
+            for (int w = 1; w < kRowWaves; ++w) best_of(v, i, s_v[w], s_i[w]);
+            a.row_arg[row] = i;
+        }
+    } else {
+        // the segment statistics were stored by the waves of this workgroup
+        __syncthreads();
+        if (wave == 0) {
+            float M;
+            double S;
+            merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
+            if (lane == 0) {
+                a.row_M[row] = M;
+                a.row_S[row] = S;
+            }
+        }
+    }
+}
+
+// What the correction draw needs of a sequence that rejected a draft (j < 0:
+// nothing to draw).
+struct SeqDraw {
+    int j, dq;              // first rejected row; the deterministic draft there (-1 with draft logits)
+    float Rp, Rq, Fp, Fq;   // residual weight constants of row j
+    float Mj;               // row j's maximum and exp-sum (fallback draw from p_j)
+    double Sj;
+};
+
+struct TailArgs {
     const float* zp;   // target logits [B, G, V]
-    const float* zq;   // draft logits  [B, G, V]
+    const float* zq;   // draft logits  [B, G, V] or null
     const int32_t* drafts;  // [B, G]
     const double* draft_lse;  // [B, G] or null
-    int B, G, V, nseg, wpr;
+    int B, G, V, nseg, nr;    // nr: workgroups per sequence
     float T, c2;
     const uint64_t* seeds;
     uint64_t step;
-    const float* p_seg_m;   // target rows' segment stats
-    const double* p_seg_s;
-    const float* q_seg_m;   // draft rows' segment stats (when draft_lse is null)
-    const double* q_seg_s;
-    const float* cand_v;    // target rows' per-wave argmax
-    const int* cand_i;
-    int* seq_j;             // [B]
-    f32x4* seq_w;           // [B]: residual weight constants (R_p, R_q, F_p, F_q) of row j
+    const float* seg_m;     // target rows' segment statistics
+    const double* seg_s;
+    const float* row_M;     // [2 B G]: target rows, then drafter rows
+    const double* row_S;
+    const int* row_arg;     // [B G]
     double* resid_s;        // [B][nseg]
+    SeqDraw* seq;           // [B]
     int32_t* accept_len;
     int32_t* out_tokens;
     uint8_t* accepted;
@@ -674,184 +774,151 @@ struct VerifyArgs {
 
 __device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >= V ? V - 1 : d); }
 
-constexpr int kCommitWaves = 8;  // one wave per block row (gamma <= 8 in one round)
-
-// Verification of one sequence.  The block's rows are spread over the eight
-// waves: each merges its rows' statistics with all 64 lanes (target argmax for
-// greedy; max and fp64 exp-sum for sampled), gathers p and q at the draft and
-// takes the fp64 accept decision.  Wave 0 then forms the accepted prefix and,
-// when every draft survived, draws the bonus token from the target's last row.
-__global__ void __launch_bounds__(64 * kCommitWaves) verify_commit_kernel(VerifyArgs a) {
-    __shared__ int s_acc[32], s_tok[32];
-    __shared__ float s_M[32];
-    __shared__ double s_S[32], s_lsep[32], s_lseq[32];
-    const int b = blockIdx.x, lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = a.G;
-    const double Td = (double)a.T;
-    for (int r = wave; r < G; r += kCommitWaves) {
-        const bool is_draft = r < G - 1;
-        // the row's inputs that do not depend on each other are loaded together
-        const int d = is_draft ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : 0;
-        const double lseq_in =
-            is_draft && a.zq && a.draft_lse && a.T > 0.f ? a.draft_lse[(size_t)b * G + r] : 0.0;
-        if (a.T == 0.f) {
-            const size_t cb = ((size_t)b * G + r) * a.wpr;
-            float bv = -INFINITY;
-            int bi = -1;
-            for (int w = lane; w < a.wpr; w += 64)
-                if (ranks_ahead(a.cand_v[cb + w], a.cand_i[cb + w], bv, bi)) {
-                    bv = a.cand_v[cb + w];
-                    bi = a.cand_i[cb + w];
-                }
-            wave_best(bv, bi);
-            if (lane == 0) {
-                s_tok[r] = bi;
-                s_acc[r] = is_draft && d == bi;
-            }
-            continue;
-        }
-        // the two logits at the draft are loaded before the row statistics are merged
-        float zpd = 0.f, zqd = 0.f;
-        if (is_draft && lane == 0) {
-            const size_t off = ((size_t)b * G + r) * a.V + d;
-            zpd = a.zp[off];
-            if (a.zq) zqd = a.zq[off];
-        }
-        const size_t rb = ((size_t)b * G + r) * a.nseg;
-        float M;
-        double S;
-        merge_row_stats(a.p_seg_m + rb, a.p_seg_s + rb, a.nseg, a.c2, lane, M, S);
-        const double lsep = (double)M / Td + log(S);
-        double lseq = 0.0;
-        if (is_draft && a.zq) {
-            if (a.draft_lse) {
-                lseq = lseq_in;
-            } else {
-                float Mq;
-                double Sq;
-                merge_row_stats(a.q_seg_m + rb, a.q_seg_s + rb, a.nseg, a.c2, lane, Mq, Sq);
-                lseq = (double)Mq / Td + log(Sq);
-            }
-        }
-        if (lane == 0) {
-            int acc = 0;
-            if (is_draft) {
-                // deterministic drafts (no draft logits): q is the point mass at d
-                const double ratio = a.zq ? exp(((double)zpd - (double)zqd) / Td - lsep + lseq)
-                                          : exp((double)zpd / Td - lsep);
-                const double u =
-                    philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
-                // u < min(1, ratio); a ratio that is NaN (p and q both zero at the
-                // draft, e.g. a draft outside a truncated target row) rejects
-                acc = ratio >= 1.0 || u < ratio;
-            }
-            s_acc[r] = acc;
-            s_M[r] = M;
-            s_S[r] = S;
-            s_lsep[r] = lsep;
-            s_lseq[r] = lseq;
-        }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    const int r = lane;
-    const bool is_row = r < G, is_draft = r < G - 1;
-    const bool acc = is_draft && s_acc[r];
-    const uint64_t accmask = ballot(acc);
-    const int lead = __builtin_ctzll(~accmask);
-    const int j = lead < G - 1 ? lead : G - 1;
-    if (is_draft && a.accepted) a.accepted[(size_t)b * (G - 1) + r] = acc ? 1 : 0;
-    int final_tok = -1;
-    bool final_known = true;
-    if (a.T == 0.f) {
-        final_tok = s_tok[j];
-    } else if (j == G - 1) {
-        const int row = b * G + (G - 1);
-        const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
-        final_tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, a.p_seg_m + (size_t)row * a.nseg,
-                                     a.p_seg_s + (size_t)row * a.nseg, a.nseg, a.c2, s_M[G - 1],
-                                     s_S[G - 1], u, lane);
-    } else {
-        final_known = false;  // correction drawn by the residual kernels
-        if (lane == 0) {
-            // 2^((z - R) c2) F = exp(z / T - LSE) with R = LSE T rounded to fp32, so that the
-            // exponent stays near zero; computed once here, loaded by the residual passes
-            const double lp = s_lsep[j], lq = s_lseq[j];
-            const float Rp = (float)(lp * Td), Rq = (float)(lq * Td);
-            a.seq_w[b] = f32x4{Rp, Rq, (float)exp((double)Rp / Td - lp), (float)exp((double)Rq / Td - lq)};
-        }
-    }
-    if (lane == 0) {
-        a.accept_len[b] = j;
-        a.seq_j[b] = final_known ? -1 : j;
-    }
-    if (is_row) {
-        int tok = r < j ? clamp_tok(a.drafts[(size_t)b * G + r], a.V) : -1;
-        if (r == j) tok = final_known ? final_tok : -1;
-        a.out_tokens[(size_t)b * G + r] = tok;
-    }
-}
-
-// Element weight of the residual [p - q]_+ at row j, from the row log-normalisers.
+// Element weight of the residual [p - q]_+ at row j, from the row
+// log-normalisers.  Both rows are read through raw buffers; without draft
+// logits (deterministic draft, q = point mass at dq) the drafter's buffer is
+// empty and reads as zeros.
 struct ResidualW {
-    const float* zpr;
-    const float* zqr;  // null: deterministic draft, q = point mass at dq
+    __amdgpu_buffer_rsrc_t zp, zq;
+    bool has_q;
     int dq;
     float Rp, Rq, Fp, Fq, c2;
-    __device__ __forceinline__ f32x4 w4(int v) const {
-        const f32x4 zp = *reinterpret_cast<const f32x4*>(zpr + v);
+    struct Raw {
+        f32x4 p, q;
+    };
+    __device__ __forceinline__ Raw load(int v) const { return Raw{load_quad(zp, v), load_quad(zq, v)}; }
+    __device__ __forceinline__ f32x4 w4(const Raw& z, int v) const {
         f32x4 r;
-        if (zqr) {
-            const f32x4 zq = *reinterpret_cast<const f32x4*>(zqr + v);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
-                const float q = fast_exp2((zq[c] - Rq) * c2) * Fq;
-                r[c] = fmaxf(p - q, 0.f);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float p = fast_exp2((zp[c] - Rp) * c2) * Fp;
-                r[c] = v + c == dq ? 0.f : p;  // p - 1 < 0 at the draft, p - 0 elsewhere
-            }
+        for (int c = 0; c < 4; ++c) {
+            const float p = fast_exp2((z.p[c] - Rp) * c2) * Fp;
+            const float q = fast_exp2((z.q[c] - Rq) * c2) * Fq;
+            // point-mass q: p - 1 < 0 at the draft, p - 0 elsewhere
+            r[c] = has_q ? fmaxf(p - q, 0.f) : (v + c == dq ? 0.f : p);
         }
         return r;
     }
 };
 
-__device__ __forceinline__ ResidualW make_residual(const VerifyArgs& a, int b, int j) {
-    ResidualW w;
-    const size_t row = (size_t)b * a.G + j;
-    w.zpr = a.zp + row * a.V;
-    w.zqr = a.zq ? a.zq + row * a.V : nullptr;
-    w.dq = a.zq ? -1 : clamp_tok(a.drafts[row], a.V);
-    const f32x4 c = a.seq_w[b];
-    w.Rp = c[0];
-    w.Rq = c[1];
-    w.Fp = c[2];
-    w.Fq = c[3];
-    w.c2 = a.c2;
-    return w;
-}
+// Verification tail: a group of a.nr workgroups per sequence (one when
+// greedy).  Every wave takes the accept decisions of the whole block, lane r
+// for block row r (the same arithmetic on the same values in every wave, so
+// all agree); workgroup 0's first wave writes the committed tokens, draws the
+// bonus and records what the correction draw needs; on a rejection every wave
+// sums the residual over one segment of the rejected row.
+__global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a) {
+    const int b = blockIdx.x / a.nr, n = blockIdx.x % a.nr;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.G;
+    const double Td = (double)a.T;
+    const size_t BG = (size_t)a.B * G;
 
-// Residual mass per segment of row j, for sequences that rejected a draft.
-__global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kScanWaves + wave;
-    const int b = gw / a.nseg, seg = gw % a.nseg;
-    if (b >= a.B) return;
-    const int j = a.seq_j[b];
-    if (j < 0) return;
-    const ResidualW w = make_residual(a, b, j);
+    // ---- the block's decisions: lane r for row r.  Every load that does not
+    // depend on the draft is issued with it, unconditionally (pointers that
+    // do not apply are replaced by valid ones whose values go unused), then
+    // the two logits at the draft.
+    const int r = lane;
+    const bool is_row = r < G, is_draft = r < G - 1;
+    const size_t row = (size_t)b * G + (is_row ? r : G - 1);
+    const int d_raw = a.drafts[row];
+    const int tok_arg = a.row_arg[row];
+    const float M = a.row_M[row];
+    const double S = a.row_S[row];
+    const float Mq = a.row_M[BG + row];
+    const double Sq = a.row_S[BG + row];
+    const double lse_given = (a.draft_lse ? a.draft_lse : a.row_S)[row];
+    const uint64_t seed = *(a.seeds ? a.seeds + b : reinterpret_cast<const uint64_t*>(a.row_S));
+    const int d = is_draft ? clamp_tok(d_raw, a.V) : 0;
+    const float zpd = a.zp[row * a.V + d];
+    const float zqd = (a.zq ? a.zq : a.zp)[row * a.V + d];
+    int acc = 0;
+    double lsep = 0.0, lseq = 0.0;
+    if (a.T == 0.f) {
+        acc = is_draft && d == tok_arg;
+    } else {
+        lsep = (double)M / Td + log(S);
+        if (a.zq) lseq = a.draft_lse ? lse_given : (double)Mq / Td + log(Sq);
+        if (is_draft) {
+            // deterministic drafts (no draft logits): q is the point mass at d
+            const double ratio = a.zq ? exp(((double)zpd - (double)zqd) / Td - lsep + lseq)
+                                      : exp((double)zpd / Td - lsep);
+            const double u = philox_uniform(seed, a.step, (uint64_t)b, (uint64_t)r, kAcceptTest);
+            // u < min(1, ratio); a ratio that is NaN (p and q both zero at the
+            // draft, e.g. a draft outside a truncated target row) rejects
+            acc = ratio >= 1.0 || u < ratio;
+        }
+    }
+    const uint64_t accmask = ballot(is_draft && acc);
+    const int lead = __builtin_ctzll(~accmask);
+    const int j = lead < G - 1 ? lead : G - 1;
+    const bool rejected = a.T > 0.f && j < G - 1;
+
+    if (n == 0 && wave == 0) {
+        if (is_draft && a.accepted) a.accepted[(size_t)b * (G - 1) + r] = acc ? 1 : 0;
+        int final_tok = -1;
+        if (a.T == 0.f) {
+            final_tok = lane_value(tok_arg, j);
+        } else if (!rejected) {
+            const size_t rl = (size_t)b * G + (G - 1);
+            const float Ml = __builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, M), G - 1));
+            const double Sl = lane_value(S, G - 1);
+            const double u = philox_uniform(seed, a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
+            final_tok = draw_softmax_row(a.zp + rl * a.V, a.V, a.seg_m + rl * a.nseg, a.seg_s + rl * a.nseg,
+                                         a.nseg, a.c2, Ml, Sl, u, lane);
+        }
+        if (lane == 0) a.accept_len[b] = j;
+        if (a.T > 0.f) {
+            // the correction draw's record (j = -1: nothing to draw)
+            const double lpj = lane_value(lsep, j), lqj = lane_value(lseq, j);
+            SeqDraw sd;
+            sd.j = rejected ? j : -1;
+            sd.dq = a.zq ? -1 : lane_value(d, j);
+            sd.Rp = (float)(lpj * Td);
+            sd.Rq = (float)(lqj * Td);
+            sd.Fp = (float)exp((double)sd.Rp / Td - lpj);
+            sd.Fq = (float)exp((double)sd.Rq / Td - lqj);
+            sd.Mj = __builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, M), j));
+            sd.Sj = lane_value(S, j);
+            if (lane == 0) a.seq[b] = sd;
+        }
+        // position j of a rejecting sequence is written by the correction draw
+        if (is_row && !(rejected && r == j)) {
+            int tok = r < j ? d : -1;
+            if (r == j) tok = final_tok;
+            a.out_tokens[(size_t)b * G + r] = tok;
+        }
+    }
+    if (!rejected) return;
+    const int seg = n * kTailWaves + wave;
+    if (seg >= a.nseg) return;
+
+    // residual [p_j - q_j]_+: weights 2^((z - R) c2) F = exp(z / T - LSE) with
+    // R = LSE T rounded to fp32, so that the exponent stays near zero
+    const double lp = lane_value(lsep, j), lq = lane_value(lseq, j);
+    ResidualW w;
+    const size_t rowj = (size_t)b * G + j;
+    const float* zpr = a.zp + rowj * a.V;
+    w.zp = row_rsrc(zpr, a.V);
+    w.zq = row_rsrc(a.zq ? a.zq + rowj * a.V : zpr, a.zq ? a.V : 0);
+    w.has_q = a.zq != nullptr;
+    w.dq = a.zq ? -1 : lane_value(d, j);
+    w.Rp = (float)(lp * Td);
+    w.Rq = (float)(lq * Td);
+    w.Fp = (float)exp((double)w.Rp / Td - lp);
+    w.Fq = (float)exp((double)w.Rq / Td - lq);
+    w.c2 = a.c2;
     const int base = seg * kSeg + 4 * lane;
+    // the segment's loads of both rows are issued before any is used (a quad
+    // past the row's end reads zeros and weighs nothing)
+    ResidualW::Raw raw[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) raw[it] = w.load(base + it * 256);
     f32x4 t4[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-        // a quad past the row's end reads the last quad and weighs nothing
         const int e = base + it * 256;
-        const f32x4 x = w.w4(e < a.V ? e : a.V - 4);
+        const f32x4 x = w.w4(raw[it], e);
         t4[it] = e < a.V ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     double s = 0.0;
@@ -864,88 +931,83 @@ __global__ void __launch_bounds__(256) verify_residual_kernel(VerifyArgs a) {
     if (lane == 0) a.resid_s[(size_t)b * a.nseg + seg] = s;
 }
 
-// Correction draw from [p_j - q_j]_+ (or from p_j when it has no mass).
-__global__ void __launch_bounds__(64) verify_draw_kernel(VerifyArgs a) {
+// Correction draw of one rejecting sequence per workgroup (one wave): the
+// segment where the running residual mass first exceeds u times the total,
+// then the element inside it, by the residual weights recomputed with the
+// arithmetic that produced the segment sums.  Falls back to p_j when the
+// residual has no mass.
+constexpr int kResidRegs = 4;  // residual sums per lane held in registers
+__global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
     const int b = blockIdx.x, lane = threadIdx.x;
-    const int j = a.seq_j[b];
-    if (j < 0) return;
-    const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)j, kFinalDraw);
+    // every load that does not depend on the record is issued with it
+    const SeqDraw sd = a.seq[b];
     const double* rs = a.resid_s + (size_t)b * a.nseg;
+    double rv[kResidRegs];
+#pragma unroll
+    for (int c = 0; c < kResidRegs; ++c) {
+        const int q = c * 64 + lane;
+        rv[c] = rs[q < a.nseg ? q : a.nseg - 1];
+        if (q >= a.nseg) rv[c] = 0.0;
+    }
+    const uint64_t seed = a.seeds[b];
+    if (sd.j < 0) return;
+    const int j = sd.j;
     double tot = 0.0;
-    for (int s = lane; s < a.nseg; s += 64) tot += rs[s];
+#pragma unroll
+    for (int c = 0; c < kResidRegs; ++c) tot += rv[c];
+    for (int q = 64 * kResidRegs + lane; q < a.nseg; q += 64) tot += rs[q];
     tot = wave_sum(tot);
+    const double u = philox_uniform(seed, a.step, (uint64_t)b, (uint64_t)j, kFinalDraw);
+    const size_t rowj = (size_t)b * a.G + j;
+    const float* zpr = a.zp + rowj * a.V;
     int tok;
     if (tot > 0.0) {
-        const ResidualW w = make_residual(a, b, j);
+        ResidualW w;
+        w.zp = row_rsrc(zpr, a.V);
+        w.zq = row_rsrc(a.zq ? a.zq + rowj * a.V : zpr, a.zq ? a.V : 0);
+        w.has_q = a.zq != nullptr;
+        w.dq = sd.dq;
+        w.Rp = sd.Rp;
+        w.Rq = sd.Rq;
+        w.Fp = sd.Fp;
+        w.Fq = sd.Fq;
+        w.c2 = a.c2;
         double before = 0.0;
-        auto segw = [&](int s) -> double { return rs[s]; };
+        auto segw = [&](int q) -> double {
+            const int c = q >> 6;
+            double v = 0.0;
+#pragma unroll
+            for (int cc = 0; cc < kResidRegs; ++cc) v = c == cc ? rv[cc] : v;
+            return c < kResidRegs ? v : rs[q];
+        };
         const double target = u * tot;
-        const int seg = find_segment(a.nseg, target, segw, lane, before);
-        tok = seg < 0 ? 0 : draw_in_segment(seg, a.V, target - before, w, lane);
+        const int sj = find_segment(a.nseg, target, segw, lane, before);
+        tok = sj < 0 ? 0 : draw_in_segment(sj, a.V, target - before, w, lane);
     } else {
-        const int row = b * a.G + j;
-        const float* sm = a.p_seg_m + (size_t)row * a.nseg;
-        const double* ss = a.p_seg_s + (size_t)row * a.nseg;
-        float M;
-        double S;
-        merge_row_stats(sm, ss, a.nseg, a.c2, lane, M, S);
-        tok = draw_softmax_row(a.zp + (size_t)row * a.V, a.V, sm, ss, a.nseg, a.c2, M, S, u, lane);
+        tok = draw_softmax_row(zpr, a.V, a.seg_m + rowj * a.nseg, a.seg_s + rowj * a.nseg, a.nseg, a.c2, sd.Mj,
+                               sd.Sj, u, lane);
     }
-    if (lane == 0) a.out_tokens[(size_t)b * a.G + j] = tok;
+    if (lane == 0) a.out_tokens[rowj] = tok;
 }
 
 // ------------------------------------------------------------- planning
-struct ScanPlan {
-    int nseg, spw, wpr;
-};
-
-ScanPlan plan_scan(long rows, int V) {
-    ScanPlan p;
-    p.nseg = (V + kSeg - 1) / kSeg;
-    long spw = (rows * p.nseg + kTargetWaves - 1) / kTargetWaves;
-    if (spw < 1) spw = 1;
-    if (spw > p.nseg) spw = p.nseg;
-    p.spw = (int)spw;
-    p.wpr = (p.nseg + p.spw - 1) / p.spw;
-    return p;
-}
-
-struct TopKLayout {
-    ScanPlan sp;
-    size_t seg_m, seg_s, bytes;
-};
-
-TopKLayout topk_layout(int batch, int gamma, int vocab) {
-    TopKLayout L{};
-    const long rows = (long)batch * gamma;
-    L.sp = plan_scan(rows, vocab);
-    Carve c;
-    L.seg_m = c.take<float>((size_t)rows * L.sp.nseg);
-    L.seg_s = c.take<double>((size_t)rows * L.sp.nseg);
-    L.bytes = c.total();
-    return L;
-}
-
 struct VerifyLayout {
-    ScanPlan sp;
-    size_t p_m, p_s, q_m, q_s, cand_v, cand_i, seq_j, seq_w, resid, bytes;
+    int nseg;
+    size_t seg_m, seg_s, row_M, row_S, row_arg, resid, seq, bytes;
 };
 
 VerifyLayout verify_layout(int batch, int gamma, int vocab) {
     VerifyLayout L{};
-    const long rows = (long)batch * gamma;
-    L.sp = plan_scan(rows, vocab);
-    const size_t rs = (size_t)rows * L.sp.nseg;
+    const size_t rows = (size_t)batch * gamma;
+    L.nseg = (vocab + kSeg - 1) / kSeg;
     Carve c;
-    L.p_m = c.take<float>(rs);
-    L.p_s = c.take<double>(rs);
-    L.q_m = c.take<float>(rs);
-    L.q_s = c.take<double>(rs);
-    L.cand_v = c.take<float>((size_t)rows * L.sp.wpr);
-    L.cand_i = c.take<int>((size_t)rows * L.sp.wpr);
-    L.seq_j = c.take<int>((size_t)batch);
-    L.seq_w = c.take<f32x4>((size_t)batch);
-    L.resid = c.take<double>((size_t)batch * L.sp.nseg);
+    L.seg_m = c.take<float>(2 * rows * L.nseg);
+    L.seg_s = c.take<double>(2 * rows * L.nseg);
+    L.row_M = c.take<float>(2 * rows);
+    L.row_S = c.take<double>(2 * rows);
+    L.row_arg = c.take<int>(rows);
+    L.resid = c.take<double>((size_t)batch * L.nseg);
+    L.seq = c.take<SeqDraw>((size_t)batch);
     L.bytes = c.total();
     return L;
 }
@@ -954,48 +1016,50 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
     return ws && !(reinterpret_cast<uintptr_t>(ws) & 255) && have >= need;
 }
 
-template <int MODE>
-void launch_scan(const ScanArgs& s, hipStream_t st) {
-    const long waves = (long)s.rows * s.wpr;
-    hipLaunchKernelGGL((row_scan_kernel<MODE>), dim3((unsigned)((waves + kScanWaves - 1) / kScanWaves)),
-                       dim3(64 * kScanWaves), 0, st, s);
-}
-
 }  // namespace
 }  // namespace dfl
 
 using namespace dfl;
 
 extern "C" size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k) {
-    if (batch < 0 || gamma < 1 || vocab < 1 || k < 1) return 0;
-    return topk_layout(batch, gamma, vocab).bytes;
+    (void)batch;
+    (void)gamma;
+    (void)vocab;
+    (void)k;
+    return 0;  // everything lives in the row workgroup's LDS
 }
 
 extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
                            float temperature, const uint64_t* seeds, uint64_t step,
                            int32_t* topk_idx, float* topk_val, double* lse, int32_t* draft,
                            void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
     if (batch < 0 || gamma < 1 || vocab < 1 || k < 1 || k > vocab) return DFLASH_ERR_SHAPE;
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DFLASH_ERR_SHAPE;
     if (batch == 0) return DFLASH_OK;
     if (!logits || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     if (temperature > 0.f && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > 64 || gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab) return DFLASH_ERR_UNSUPPORTED;
-    const TopKLayout L = topk_layout(batch, gamma, vocab);
-    if (!ws_ok(workspace, workspace_bytes, L.bytes)) return DFLASH_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
+    if (k > 64 || gamma > 32 || vocab % 4 != 0 || vocab > kMaxTopkVocab) return DFLASH_ERR_UNSUPPORTED;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
-    ScanArgs s{logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, c2,
-               reinterpret_cast<float*>(ws + L.seg_m), reinterpret_cast<double*>(ws + L.seg_s),
-               nullptr, nullptr};
-    if (temperature > 0.f) launch_scan<kSumExp>(s, st);
-    else launch_scan<kSegMax>(s, st);
-    int rc = launch_status();
-    if (rc) return rc;
-    TopKFin f{logits, batch, gamma, vocab, L.sp.nseg, k, temperature, c2, seeds, step,
-              s.seg_m, s.seg_s, topk_idx, topk_val, lse, draft};
-    hipLaunchKernelGGL(topk_finalize_kernel, dim3(batch * gamma), dim3(64 * (kFinWaves + 1)), 0, st, f);
+    TopKArgs f{};
+    f.z = logits;
+    f.B = batch;
+    f.G = gamma;
+    f.V = vocab;
+    f.nseg = (vocab + kSeg - 1) / kSeg;
+    f.k = k;
+    f.T = temperature;
+    f.c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
+    f.seeds = seeds;
+    f.step = step;
+    f.topk_idx = topk_idx;
+    f.topk_val = topk_val;
+    f.lse = lse;
+    f.draft = draft;
+    const dim3 grid((unsigned)(batch * gamma)), block(kRowThreads);
+    if (temperature > 0.f) hipLaunchKernelGGL(topk_row_kernel<kSumExp>, grid, block, 0, st, f);
+    else hipLaunchKernelGGL(topk_row_kernel<kSegMax>, grid, block, 0, st, f);
     return launch_status();
 }
 
@@ -1030,46 +1094,59 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
     const VerifyLayout L = verify_layout(batch, gamma, vocab);
     char* ws = static_cast<char*>(scratch_ws);
     const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
-    VerifyArgs v{};
-    v.zp = target_logits; v.zq = draft_logits; v.drafts = draft_tokens; v.draft_lse = draft_lse;
-    v.B = batch; v.G = gamma; v.V = vocab; v.nseg = L.sp.nseg; v.wpr = L.sp.wpr;
-    v.T = temperature; v.c2 = c2; v.seeds = seeds; v.step = step;
-    v.p_seg_m = reinterpret_cast<float*>(ws + L.p_m);
-    v.p_seg_s = reinterpret_cast<double*>(ws + L.p_s);
-    v.q_seg_m = reinterpret_cast<float*>(ws + L.q_m);
-    v.q_seg_s = reinterpret_cast<double*>(ws + L.q_s);
-    v.cand_v = reinterpret_cast<float*>(ws + L.cand_v);
-    v.cand_i = reinterpret_cast<int*>(ws + L.cand_i);
-    v.seq_j = reinterpret_cast<int*>(ws + L.seq_j);
-    v.seq_w = reinterpret_cast<f32x4*>(ws + L.seq_w);
-    v.resid_s = reinterpret_cast<double*>(ws + L.resid);
-    v.accept_len = accept_len; v.out_tokens = out_tokens; v.accepted = accepted;
-    ScanArgs s{target_logits, batch * gamma, vocab, L.sp.nseg, L.sp.spw, L.sp.wpr, c2,
-               const_cast<float*>(v.p_seg_m), const_cast<double*>(v.p_seg_s),
-               const_cast<float*>(v.cand_v), const_cast<int*>(v.cand_i)};
+    const int rows = batch * gamma;
+    RowArgs ra{};
+    ra.zp = target_logits;
+    ra.zq = draft_logits;
+    ra.rows = rows;
+    ra.V = vocab;
+    ra.nseg = L.nseg;
+    ra.B = batch;
+    ra.c2 = c2;
+    ra.seg_m = reinterpret_cast<float*>(ws + L.seg_m);
+    ra.seg_s = reinterpret_cast<double*>(ws + L.seg_s);
+    ra.row_M = reinterpret_cast<float*>(ws + L.row_M);
+    ra.row_S = reinterpret_cast<double*>(ws + L.row_S);
+    ra.row_arg = reinterpret_cast<int*>(ws + L.row_arg);
     if (temperature == 0.f) {
-        launch_scan<kArgmax>(s, st);
+        hipLaunchKernelGGL(verify_row_kernel<kArgmax>, dim3((unsigned)rows), dim3(kRowThreads), 0, st, ra);
     } else {
-        launch_scan<kSumExp>(s, st);
-        if (!draft_lse && draft_logits) {
-            ScanArgs q = s;
-            q.z = draft_logits;
-            q.seg_m = const_cast<float*>(v.q_seg_m);
-            q.seg_s = const_cast<double*>(v.q_seg_s);
-            launch_scan<kSumExp>(q, st);
-        }
+        // the drafter rows' log-normalisers come from the same launch when
+        // they are not given
+        const int launch_rows = (!draft_lse && draft_logits) ? 2 * rows : rows;
+        hipLaunchKernelGGL(verify_row_kernel<kSumExp>, dim3((unsigned)launch_rows), dim3(kRowThreads), 0, st,
+                           ra);
     }
     int rc = launch_status();
     if (rc) return rc;
-    hipLaunchKernelGGL(verify_commit_kernel, dim3(batch), dim3(64 * kCommitWaves), 0, st, v);
+    TailArgs t{};
+    t.zp = target_logits;
+    t.zq = draft_logits;
+    t.drafts = draft_tokens;
+    t.draft_lse = draft_lse;
+    t.B = batch;
+    t.G = gamma;
+    t.V = vocab;
+    t.nseg = L.nseg;
+    t.nr = temperature > 0.f ? (L.nseg + kTailWaves - 1) / kTailWaves : 1;
+    t.T = temperature;
+    t.c2 = c2;
+    t.seeds = seeds;
+    t.step = step;
+    t.seg_m = ra.seg_m;
+    t.seg_s = ra.seg_s;
+    t.row_M = ra.row_M;
+    t.row_S = ra.row_S;
+    t.row_arg = ra.row_arg;
+    t.resid_s = reinterpret_cast<double*>(ws + L.resid);
+    t.seq = reinterpret_cast<SeqDraw*>(ws + L.seq);
+    t.accept_len = accept_len;
+    t.out_tokens = out_tokens;
+    t.accepted = accepted;
+    hipLaunchKernelGGL(verify_tail_kernel, dim3((unsigned)(batch * t.nr)), dim3(64 * kTailWaves), 0, st, t);
     rc = launch_status();
     if (rc || temperature == 0.f) return rc;
-    const long waves = (long)batch * L.sp.nseg;
-    hipLaunchKernelGGL(verify_residual_kernel, dim3((unsigned)((waves + kScanWaves - 1) / kScanWaves)),
-                       dim3(64 * kScanWaves), 0, st, v);
-    rc = launch_status();
-    if (rc) return rc;
-    hipLaunchKernelGGL(verify_draw_kernel, dim3(batch), dim3(64), 0, st, v);
+    hipLaunchKernelGGL(verify_draw_kernel, dim3((unsigned)batch), dim3(64), 0, st, t);
     return launch_status();
 }
 

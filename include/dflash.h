@@ -140,7 +140,11 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
  *            softmax(logits / T) by inverse CDF in increasing vocabulary order
  *            with the purpose-0 uniform of (seeds[b], step, b, r).
  *   seeds    [batch] uint64 (device); may be NULL when T == 0.
- * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, vocab <= 2^29, 1 <= gamma <= 32.
+ * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, vocab <= 2^23 (the
+ * row's segment statistics live in one workgroup's LDS), 1 <= gamma <= 32.
+ * Workspace: none (dflash_topk_workspace_size returns 0; workspace may be
+ * NULL and is ignored).  One workgroup per row does the whole row in one
+ * launch.
  * ------------------------------------------------------------------------ */
 size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k);
 int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,

@@ -39,7 +39,7 @@ def test_workspace_queries():
     assert dfl.dflash_block_attn_workspace_size(1, 8, 40, 8, 128, 4096) > 0   # split keys at B=1
     assert dfl.dflash_block_attn_workspace_size(32, 8, 40, 8, 128, 4096, 1) == 0  # fp32: none
     assert dfl.dflash_block_attn_workspace_size(32, 8, 41, 8, 128, 4096) == 0      # bad GQA
-    assert dfl.dflash_topk_workspace_size(32, 8, 151936, 8) > 0
+    assert dfl.dflash_topk_workspace_size(32, 8, 151936, 8) == 0   # all in LDS
     assert dfl.spec_verify_workspace_size(32, 8, 151936) > 0
     assert dfl.dflash_context_fuse_workspace_size(512, 5, 5120, 5120, 5, 8, 128) > 0
     assert dfl.dflash_context_fuse_workspace_size(512, 5, 5120, 5100, 5, 8, 128) == 0
@@ -90,9 +90,9 @@ def test_topk_validation():
     assert topk(k=65) == -3
     assert topk(V=151935) == -3
     assert topk(V=(1 << 29) + 4) == -3     # row bytes past 32-bit buffer offsets
+    assert topk(V=(1 << 23) + 4) == -3     # segment statistics past the workgroup's LDS
     assert topk(G=40) == -3
-    assert topk() == -4
-    assert topk(seeds=None, T=0.0) == -4   # greedy needs no seeds; fails on workspace only
+    assert topk(seeds=None, T=0.0, k=65) == -3  # greedy needs no seeds: fails on k only
 
 
 def verify(**kw):
