@@ -530,6 +530,14 @@ struct FinArgs {
     int32_t* draft;
 };
 
+// A workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it (a full barrier waits for every one of them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si) {
     wave_best(v, i);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -659,10 +667,108 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
         }
     }
 
+    // ---- log-normaliser and the draw's location (before the top-k, so the
+    // loads of the drawn group's weight rows are in flight while it runs)
+    const int j0 = (int)((long)tid * a.nseg / kFinThreads);
+    const int j1 = (int)((long)(tid + 1) * a.nseg / kFinThreads);
+    int J = 0;
+    // the group's 16 logits are recomputed: wave w takes entries 4w .. 4w+3,
+    // each lane a strided set of 16-byte chunks of the hidden row and weight
+    // rows (entries past the vocabulary read its last row and weigh nothing);
+    // the first kRecHold chunks per lane are loaded before the top-k runs
+    constexpr int kRecHold = 10;
+    const int nch = a.d / 8;
+    const uint16_t* hr = a.h + R * (size_t)a.d;
+    const uint16_t* wr[4] = {hr, hr, hr, hr};
+    u32x4 hv[kRecHold], wv[kRecHold][4];
+    int v0 = 0;
+    if (a.want_exp) {
+        // segment masses in vocabulary order: contiguous runs per thread, fp64
+        double run = 0.0;
+        for (int j = j0; j < j1; ++j) run += seg_mass(s_s[j], s_m[j], mx, a.c2);
+        const double incl = wave_inclusive_scan(run);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;
+        if (lane == 63) sd[wave] = incl;
+        __syncthreads();
+        double before = 0.0, total = 0.0;
+#pragma unroll
+        for (int w = 0; w < kFinThreads / 64; ++w) {
+            if (w < wave) before += sd[w];
+            total += sd[w];
+        }
+        excl += before;
+        if (tid == 0 && a.lse) a.lse[R] = (double)mx * a.c2 * kLn2 + log(total);
+        if (a.want_draw) {
+            const int b = (int)(R / a.gamma), g = (int)(R % a.gamma);
+            const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)g, kDraftDraw);
+            const double tgt = u * total;
+            // the segment J where the running mass (vocabulary order) first
+            // exceeds u S, or the last segment with mass when rounding leaves no
+            // crossing; each thread notes the mass before its own candidates
+            int first = kNone, last = -1;
+            double before_first = 0.0, before_last = 0.0;
+            double cum = excl;
+            for (int j = j0; j < j1; ++j) {
+                const double sj = seg_mass(s_s[j], s_m[j], mx, a.c2);
+                if (sj > 0.0) {
+                    if (cum + sj > tgt && first == kNone) { first = j; before_first = cum; }
+                    last = j;
+                    before_last = cum;
+                }
+                cum += sj;
+            }
+            const int my_first = first, my_last = last;
+            first = block_min(first, si);
+            last = -block_min(-last, si);
+            J = first != kNone ? first : last;
+            if (J < 0) J = 0;  // no positive mass (non-finite logits): any segment, never out of range
+            if (j0 <= J && J < j1) {
+                // the thread whose run holds J: the group inside J, from J's eight
+                // group sums (in units of J's weights 2^((z - m_J) c2))
+                const double before_J = J == my_first ? before_first : (J == my_last ? before_last : 0.0);
+                const double t = (tgt - before_J) / exp2(((double)s_m[J] - (double)mx) * a.c2);
+                const u32x2* gp = a.gsum + ((size_t)R * a.nseg + J) * 4;
+                float gs[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 x = gp[q];
+                    gs[2 * q] = __uint_as_float(x[0]);
+                    gs[2 * q + 1] = __uint_as_float(x[1]);
+                }
+                int G = -1, Gl = -1;
+                double bG = 0.0, bGl = 0.0, c = 0.0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (gs[q] > 0.f) {
+                        if (G < 0 && c + (double)gs[q] > t) { G = q; bG = c; }
+                        Gl = q;
+                        bGl = c;
+                    }
+                    c += (double)gs[q];
+                }
+                if (G < 0) { G = Gl < 0 ? 0 : Gl; bG = Gl < 0 ? 0.0 : bGl; }
+                s_v0 = J * kSegW + G * kGrpW;
+                s_tg = t - bG;
+            }
+            __syncthreads();
+            v0 = s_v0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wr[e] = a.w + (size_t)min(v0 + wave * 4 + e, a.V - 1) * a.d;
+#pragma unroll
+            for (int u = 0; u < kRecHold; ++u) {
+                const int c = min(lane + 64 * u, nch - 1);  // clamped: not added
+                hv[u] = *reinterpret_cast<const u32x4*>(hr + c * 8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wv[u][e] = *reinterpret_cast<const u32x4*>(wr[e] + c * 8);
+            }
+        }
+    }
+
     // the segments that can hold a top-k entry (m >= tau), in any order
     for (int j = tid; j < a.nseg; j += kFinThreads)
         if (s_m[j] >= tau) q_seg[atomicAdd(&n_q, 1)] = j;
-    __syncthreads();
+    lds_barrier();
     const int nq = n_q;
 
     // Only entries >= tau can rank (tau is at most the row's k-th largest
@@ -673,7 +779,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     // appears once, so the ranks are 0, 1, ... without repeats).
     const int k = a.k;
     if (tid == 0) n_s = 0;
-    __syncthreads();
+    lds_barrier();
     for (int slot = tid; slot < nq * kQuads; slot += kFinThreads) {
         const int j = q_seg[slot / kQuads], r = slot % kQuads;
         // the record slot is read with the mask (slots past the mask's count
@@ -693,7 +799,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int ns = n_s;
     int top1;
     if (ns <= kFinThreads) {
@@ -707,7 +813,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
             a.val[R * k + rank] = v;
             if (rank == 0) w_i[0] = i;
         }
-        __syncthreads();
+        lds_barrier();
         top1 = w_i[0];
     } else {
         // many entries >= tau (long runs of equal logits): chunks of kFinChunk
@@ -765,6 +871,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
         top1 = c_i[kFinCand];
     }
 
+
     if (!a.want_exp) {
         if (tid == 0) {
             if (a.lse) a.lse[R] = NAN;
@@ -772,112 +879,27 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
         }
         return;
     }
-    // segment masses in vocabulary order: contiguous runs per thread, fp64
-    const int j0 = (int)((long)tid * a.nseg / kFinThreads);
-    const int j1 = (int)((long)(tid + 1) * a.nseg / kFinThreads);
-    double run = 0.0;
-    for (int j = j0; j < j1; ++j) run += seg_mass(s_s[j], s_m[j], mx, a.c2);
-    const double incl = wave_inclusive_scan(run);
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0;
-    if (lane == 63) sd[wave] = incl;
-    __syncthreads();
-    double before = 0.0, total = 0.0;
-#pragma unroll
-    for (int w = 0; w < kFinThreads / 64; ++w) {
-        if (w < wave) before += sd[w];
-        total += sd[w];
-    }
-    excl += before;
-    if (tid == 0 && a.lse) a.lse[R] = (double)mx * a.c2 * kLn2 + log(total);
     if (!a.want_draw) return;
-    const int b = (int)(R / a.gamma), g = (int)(R % a.gamma);
-    const double u = philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)g, kDraftDraw);
-    const double tgt = u * total;
-    // the segment J where the running mass (vocabulary order) first exceeds
-    // u S, or the last segment with mass when rounding leaves no crossing;
-    // each thread notes the mass before its own candidates
-    int first = kNone, last = -1;
-    double before_first = 0.0, before_last = 0.0;
-    double cum = excl;
-    for (int j = j0; j < j1; ++j) {
-        const double sj = seg_mass(s_s[j], s_m[j], mx, a.c2);
-        if (sj > 0.0) {
-            if (cum + sj > tgt && first == kNone) { first = j; before_first = cum; }
-            last = j;
-            before_last = cum;
-        }
-        cum += sj;
-    }
-    const int my_first = first, my_last = last;
-    first = block_min(first, si);
-    last = -block_min(-last, si);
-    int J = first != kNone ? first : last;
-    if (J < 0) J = 0;  // no positive mass (non-finite logits): any segment, never out of range
-    if (j0 <= J && J < j1) {
-        // the thread whose run holds J: the group inside J, from J's eight
-        // group sums (in units of J's weights 2^((z - m_J) c2))
-        const double before_J = J == my_first ? before_first : (J == my_last ? before_last : 0.0);
-        const double t = (tgt - before_J) / exp2(((double)s_m[J] - (double)mx) * a.c2);
-        const u32x2* gp = a.gsum + ((size_t)R * a.nseg + J) * 4;
-        float gs[8];
+    auto dot8 = [](const u32x4& h, const u32x4& w, float acc) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const u32x2 x = gp[q];
-            gs[2 * q] = __uint_as_float(x[0]);
-            gs[2 * q + 1] = __uint_as_float(x[1]);
+            acc = __builtin_fmaf(__uint_as_float(h[q] << 16), __uint_as_float(w[q] << 16), acc);
+            acc = __builtin_fmaf(__uint_as_float(h[q] & 0xFFFF0000u), __uint_as_float(w[q] & 0xFFFF0000u), acc);
         }
-        int G = -1, Gl = -1;
-        double bG = 0.0, bGl = 0.0, c = 0.0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (gs[q] > 0.f) {
-                if (G < 0 && c + (double)gs[q] > t) { G = q; bG = c; }
-                Gl = q;
-                bGl = c;
-            }
-            c += (double)gs[q];
-        }
-        if (G < 0) { G = Gl < 0 ? 0 : Gl; bG = Gl < 0 ? 0.0 : bGl; }
-        s_v0 = J * kSegW + G * kGrpW;
-        s_tg = t - bG;
-    }
-    __syncthreads();
-    // the group's 16 logits, recomputed: wave w takes entries 4w .. 4w+3, each
-    // lane a strided set of 16-byte chunks of the hidden row and weight rows
-    // (entries past the vocabulary read its last row and weigh nothing)
-    const int v0 = s_v0;
-    const uint16_t* hr = a.h + R * (size_t)a.d;
-    const uint16_t* wr[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wr[e] = a.w + (size_t)min(v0 + wave * 4 + e, a.V - 1) * a.d;
-    // batches of kRecU chunks per lane, all loads of a batch issued together
-    // (chunk indices clamped into the row; the clamped ones are not added)
-    constexpr int kRecU = 5;
-    const int nch = a.d / 8;
+        return acc;
+    };
     float part[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = lane; c0 < nch; c0 += 64 * kRecU) {
-        u32x4 hv[kRecU], wv[kRecU][4];
 #pragma unroll
-        for (int u = 0; u < kRecU; ++u) {
-            const int c = min(c0 + 64 * u, nch - 1);
-            hv[u] = *reinterpret_cast<const u32x4*>(hr + c * 8);
+    for (int u = 0; u < kRecHold; ++u) {
+        if (lane + 64 * u >= nch) continue;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[u][e] = *reinterpret_cast<const u32x4*>(wr[e] + c * 8);
-        }
+        for (int e = 0; e < 4; ++e) part[e] = dot8(hv[u], wv[u][e], part[e]);
+    }
+    // chunks past the first kRecHold per lane (d_model > 5,120)
+    for (int c = lane + 64 * kRecHold; c < nch; c += 64) {
+        const u32x4 h1 = *reinterpret_cast<const u32x4*>(hr + c * 8);
 #pragma unroll
-        for (int u = 0; u < kRecU; ++u) {
-            if (c0 + 64 * u >= nch) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    part[e] = __builtin_fmaf(__uint_as_float(hv[u][q] << 16),
-                                             __uint_as_float(wv[u][e][q] << 16), part[e]);
-                    part[e] = __builtin_fmaf(__uint_as_float(hv[u][q] & 0xFFFF0000u),
-                                             __uint_as_float(wv[u][e][q] & 0xFFFF0000u), part[e]);
-                }
-        }
+        for (int e = 0; e < 4; ++e) part[e] = dot8(h1, *reinterpret_cast<const u32x4*>(wr[e] + c * 8), part[e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) part[e] = wave_sum(part[e]);
@@ -885,7 +907,7 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) s_z[wave * 4 + e] = part[e];
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         // the entry of the group where the running weight first passes the
         // rest of the target (weights by the epilogue's own formula)
