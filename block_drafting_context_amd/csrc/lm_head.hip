@@ -678,8 +678,8 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     // the first kRecHold chunks per lane are loaded before the top-k runs
     constexpr int kRecHold = 10;
     const int nch = a.d / 8;
-    const uint16_t* hr = a.h + R * (size_t)a.d;
-    const uint16_t* wr[4] = {hr, hr, hr, hr};
+    const size_t hoff = R * (size_t)a.d;
+    size_t woff[4] = {0, 0, 0, 0};  // element offsets of the 4 weight rows of this wave
     u32x4 hv[kRecHold], wv[kRecHold][4];
     int v0 = 0;
     if (a.want_exp) {
@@ -754,13 +754,13 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
             __syncthreads();
             v0 = s_v0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wr[e] = a.w + (size_t)min(v0 + wave * 4 + e, a.V - 1) * a.d;
+            for (int e = 0; e < 4; ++e) woff[e] = (size_t)min(v0 + wave * 4 + e, a.V - 1) * a.d;
 #pragma unroll
             for (int u = 0; u < kRecHold; ++u) {
                 const int c = min(lane + 64 * u, nch - 1);  // clamped: not added
-                hv[u] = *reinterpret_cast<const u32x4*>(hr + c * 8);
+                hv[u] = *reinterpret_cast<const u32x4*>(a.h + hoff + c * 8);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) wv[u][e] = *reinterpret_cast<const u32x4*>(wr[e] + c * 8);
+                for (int e = 0; e < 4; ++e) wv[u][e] = *reinterpret_cast<const u32x4*>(a.w + woff[e] + c * 8);
             }
         }
     }
@@ -897,9 +897,10 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
     }
     // chunks past the first kRecHold per lane (d_model > 5,120)
     for (int c = lane + 64 * kRecHold; c < nch; c += 64) {
-        const u32x4 h1 = *reinterpret_cast<const u32x4*>(hr + c * 8);
+        const u32x4 h1 = *reinterpret_cast<const u32x4*>(a.h + hoff + c * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part[e] = dot8(h1, *reinterpret_cast<const u32x4*>(wr[e] + c * 8), part[e]);
+        for (int e = 0; e < 4; ++e)
+            part[e] = dot8(h1, *reinterpret_cast<const u32x4*>(a.w + woff[e] + c * 8), part[e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) part[e] = wave_sum(part[e]);
