@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libdflash.so")
+# DFLASH_LIB names another build of the same sources (the sanitizer test loads a
+# host-only build with AddressSanitizer and UndefinedBehaviorSanitizer).
+lib_path = os.environ.get("DFLASH_LIB") or os.path.join(_HERE, "libdflash.so")
 _lib = None
 
 EXPORTED_SYMBOLS = (

@@ -38,6 +38,8 @@ constexpr int kMaxNCT = 3;         // 16-column query tiles per wave
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kMinKeysPerSplit = 512;  // at least 4 tiles per wave in every key split
+constexpr int kMaxWindow = 1 << 28;        // ring slots per (sequence, KV head)
+constexpr int64_t kMaxQueryRows = 1 << 28;  // batch * gamma * n_q
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may trail the true max
 
 struct AttnArgs {
@@ -577,9 +579,33 @@ void launch_bf16_nct(const AttnArgs& a, int nct, int n_qgroups, hipStream_t st) 
 
 using namespace dfl;
 
+namespace dfl {
+namespace {
+
+// Shape part of the checks: DFLASH_ERR_SHAPE, DFLASH_ERR_UNSUPPORTED or OK.
+// The caps keep every count the host forms (query rows, window + gamma, grid
+// extents) far inside 32 bits.
+int attn_shape(int batch, int gamma, int n_q, int n_kv, int d_head, int window, int dtype) {
+    if (batch < 0 || gamma < 1 || n_q < 1 || n_kv < 1 || d_head < 1 || window < 1)
+        return DFLASH_ERR_SHAPE;
+    if (n_q % n_kv != 0) return DFLASH_ERR_SHAPE;
+    if (dtype != DFLASH_DTYPE_BF16 && dtype != DFLASH_DTYPE_FP32) return DFLASH_ERR_SHAPE;
+    if (gamma > 32 || window % 64 != 0 || window > kMaxWindow ||
+        capped_product(kMaxQueryRows, {batch, gamma, n_q}) < 0)
+        return DFLASH_ERR_UNSUPPORTED;
+    if (dtype == DFLASH_DTYPE_BF16 && d_head != 64 && d_head != 128) return DFLASH_ERR_UNSUPPORTED;
+    if (dtype == DFLASH_DTYPE_FP32 && (d_head > 128 || window + gamma > kMaxKeys32))
+        return DFLASH_ERR_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
+}  // namespace
+}  // namespace dfl
+
 extern "C" size_t dflash_block_attn_workspace_size(int batch, int gamma, int n_q, int n_kv,
                                                    int d_head, int window, int dtype) {
-    if (batch < 0 || gamma < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || window < 1) return 0;
+    if (batch == 0 || attn_shape(batch, gamma, n_q, n_kv, d_head, window, dtype) != DFLASH_OK)
+        return 0;
     return plan_attn(batch, gamma, n_q, n_kv, d_head, window, dtype).bytes;
 }
 
@@ -588,16 +614,11 @@ extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v
                                  float scale, void* out, float* lse, int dtype, int batch,
                                  int gamma, int n_q, int n_kv, int d_head, int window,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-    if (batch < 0 || gamma < 1 || n_q < 1 || n_kv < 1 || d_head < 1 || window < 1)
-        return DFLASH_ERR_SHAPE;
-    if (n_q % n_kv != 0 || !(scale > 0.f) || !std::isfinite(scale)) return DFLASH_ERR_SHAPE;
-    if (dtype != DFLASH_DTYPE_BF16 && dtype != DFLASH_DTYPE_FP32) return DFLASH_ERR_SHAPE;
+    const int shape = attn_shape(batch, gamma, n_q, n_kv, d_head, window, dtype);
+    if (shape == DFLASH_ERR_SHAPE || !(scale > 0.f) || !std::isfinite(scale)) return DFLASH_ERR_SHAPE;
     if (batch == 0) return DFLASH_OK;
     if (!q || !k_blk || !v_blk || !k_ring || !v_ring || !ctx_len || !out) return DFLASH_ERR_NULL;
-    if (gamma > 32 || window % 64 != 0) return DFLASH_ERR_UNSUPPORTED;
-    if (dtype == DFLASH_DTYPE_BF16 && d_head != 64 && d_head != 128) return DFLASH_ERR_UNSUPPORTED;
-    if (dtype == DFLASH_DTYPE_FP32 && (d_head > 128 || window + gamma > kMaxKeys32))
-        return DFLASH_ERR_UNSUPPORTED;
+    if (shape != DFLASH_OK) return shape;
     const AttnPlan p = plan_attn(batch, gamma, n_q, n_kv, d_head, window, dtype);
     if (p.bytes > 0) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < p.bytes)

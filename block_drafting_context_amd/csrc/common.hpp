@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <initializer_list>
 
 #include "dflash.h"
 
@@ -239,6 +240,23 @@ struct Carve {
     }
     size_t total() const { return align_up(off, 256); }
 };
+
+// Product of non-negative factors if it stays at or below `cap`, else -1; no
+// intermediate product can overflow.  Shape checks use it so that every count
+// the host derives from the caller's sizes fits the type it is computed in.
+inline int64_t capped_product(int64_t cap, std::initializer_list<int64_t> factors) {
+    int64_t p = 1;
+    for (const int64_t x : factors) {
+        if (x < 0 || (x != 0 && p > cap / x)) return -1;
+        p *= x;
+    }
+    return p;
+}
+
+// Rows of one call for the kernels that give each row its own workgroup of up
+// to 1,024 threads (twice that many rows in spec_verify's statistics launch):
+// a launch counts its work-items in 32 bits.
+constexpr int64_t kMaxRowsPerCall = 1 << 20;
 
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;

@@ -31,6 +31,8 @@ constexpr int kGConsumers = 8;               // 4 x 2 waves of 64 x 80, two per 
 constexpr int kGProducers = 3;               // A rows 0-127, A rows 128-255, B rows
 constexpr int kCUs = 256;
 constexpr int kXCDs = 8;
+constexpr int64_t kMaxFuseWidth = 1 << 30;  // n_taps * d_tgt and n_layers * 2 * n_kv * d_head
+constexpr int kMaxFuseRows = 65535;        // the K/V append spans the rows in its grid's y extent
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define DFL_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -343,13 +345,32 @@ void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, i
 
 using namespace dfl;
 
+namespace dfl {
+namespace {
+
+// Shape part of the checks (every size already >= 1): DFLASH_ERR_UNSUPPORTED
+// or OK, with the GEMMs' reduction and output widths in kx and nkvc.
+int fuse_shape(int rows, int n_taps, int d_tgt, int d_model, int n_layers, int n_kv, int d_head,
+               int64_t& kx, int64_t& nkvc) {
+    kx = capped_product(kMaxFuseWidth, {n_taps, d_tgt});
+    nkvc = capped_product(kMaxFuseWidth, {n_layers, 2, n_kv, d_head});
+    if (kx < 0 || nkvc < 0 || rows > kMaxFuseRows) return DFLASH_ERR_UNSUPPORTED;
+    if (kx % 64 || d_model % 128 || nkvc % 128 || d_model > 8192 || d_head % 4)
+        return DFLASH_ERR_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
+}  // namespace
+}  // namespace dfl
+
 extern "C" size_t dflash_context_fuse_workspace_size(int rows, int n_taps, int d_tgt, int d_model,
                                                      int n_layers, int n_kv, int d_head) {
     if (rows < 1 || n_taps < 1 || d_tgt < 1 || d_model < 1 || n_layers < 1 || n_kv < 1 ||
         d_head < 1)
         return 0;
-    const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
-    if (kx % 64 || d_model % 128 || nkvc % 128) return 0;
+    int64_t kx, nkvc;
+    if (fuse_shape(rows, n_taps, d_tgt, d_model, n_layers, n_kv, d_head, kx, nkvc) != DFLASH_OK)
+        return 0;
     return fuse_layout(rows, (int)kx, d_model, (int)nkvc).bytes;
 }
 
@@ -365,10 +386,9 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     if (!(eps >= 0.f) || !std::isfinite(eps)) return DFLASH_ERR_SHAPE;
     if (!taps || !w_c || !rms_gain || !w_kv || !row_seq || !row_pos || !kv_ring)
         return DFLASH_ERR_NULL;
-    const long kx = (long)n_taps * d_tgt, nkvc = (long)n_layers * 2 * n_kv * d_head;
-    if (kx % 64 || d_model % 128 || nkvc % 128 || d_model > 8192 || kx > (1L << 30) ||
-        nkvc > (1L << 30) || d_head % 4)
-        return DFLASH_ERR_UNSUPPORTED;
+    int64_t kx, nkvc;
+    const int shape = fuse_shape(rows, n_taps, d_tgt, d_model, n_layers, n_kv, d_head, kx, nkvc);
+    if (shape != DFLASH_OK) return shape;
     const FuseLayout L = fuse_layout(rows, (int)kx, d_model, (int)nkvc);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.bytes)
         return DFLASH_ERR_WORKSPACE;

@@ -960,8 +960,23 @@ void launch_head(int tt, dim3 grid, const HeadArgs& a, hipStream_t st) {
 
 using namespace dfl;
 
+namespace dfl {
+namespace {
+
+// Size part of the checks (every size already >= 1): true when the kernels run
+// this shape.  The row cap keeps the finalize's one workgroup per row within a
+// launch's 32-bit count of work-items and the 256-row passes within int.
+bool head_shape_ok(int rows, int d_model, int vocab, int k) {
+    return k <= kHeadMaxK && k <= vocab && d_model % kHBK == 0 && d_model <= kHeadMaxD &&
+           vocab <= kFinMaxSeg * kSegW && rows <= kMaxRowsPerCall;
+}
+
+}  // namespace
+}  // namespace dfl
+
 extern "C" size_t dflash_lm_head_topk_workspace_size(int rows, int d_model, int vocab, int k) {
-    if (rows < 1 || d_model < 1 || vocab < 1 || k < 1) return 0;
+    if (rows < 1 || d_model < 1 || vocab < 1 || k < 1 || !head_shape_ok(rows, d_model, vocab, k))
+        return 0;
     return head_layout(rows, vocab).bytes;
 }
 
@@ -977,8 +992,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     if (!hidden || !w_head || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     const bool sample = temperature > 0.f;
     if (sample && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > kHeadMaxK || d_model % kHBK || d_model > kHeadMaxD || vocab > kFinMaxSeg * kSegW ||
-        (reinterpret_cast<uintptr_t>(hidden) & 15) ||
+    if (!head_shape_ok(rows, d_model, vocab, k) || (reinterpret_cast<uintptr_t>(hidden) & 15) ||
         (reinterpret_cast<uintptr_t>(w_head) & 15))
         return DFLASH_ERR_UNSUPPORTED;
     const HeadLayout L = head_layout(rows, vocab);

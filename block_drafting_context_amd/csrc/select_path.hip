@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelTableDoubles = 12288;  // 96 KB of LDS for the score table
+constexpr int kSelMaxGamma = 4096;         // block positions: t * k stays far inside int
 
 struct SelArgs {
     const int32_t* cand;    // [B, G, k]
@@ -151,7 +152,8 @@ extern "C" int dflash_select_path(const int32_t* cand_idx, const float* cand_sco
     if (batch == 0) return DFLASH_OK;
     if (!cand_idx || !cand_score || !emb_a || !emb_b || !gate || !anchor || !path)
         return DFLASH_ERR_NULL;
-    if (k > 64 || r % 8 != 0 || r > 4096) return DFLASH_ERR_UNSUPPORTED;
+    if (k > 64 || r % 8 != 0 || r > 4096 || gamma > kSelMaxGamma || batch > kMaxRowsPerCall)
+        return DFLASH_ERR_UNSUPPORTED;
     const uintptr_t align = reinterpret_cast<uintptr_t>(emb_a) | reinterpret_cast<uintptr_t>(emb_b) |
                             reinterpret_cast<uintptr_t>(gate);
     if (align & 15) return DFLASH_ERR_UNSUPPORTED;

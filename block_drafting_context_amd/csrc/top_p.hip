@@ -313,7 +313,7 @@ extern "C" int dflash_top_p_mask(const float* logits, float* out, int32_t* kept,
     if (!logits || !out) return DFLASH_ERR_NULL;
     // every weight is at most 2^40 in fixed point, so a row's 64-bit total
     // cannot overflow below 2^24 entries
-    if (vocab >= kMaxTopPVocab) return DFLASH_ERR_UNSUPPORTED;
+    if (vocab >= kMaxTopPVocab || rows > kMaxRowsPerCall) return DFLASH_ERR_UNSUPPORTED;
     TopPArgs a{logits, out, kept, vocab, (float)(1.4426950408889634 / (double)temperature), (double)top_p};
     hipLaunchKernelGGL(top_p_kernel, dim3(rows), dim3(kPThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), a);

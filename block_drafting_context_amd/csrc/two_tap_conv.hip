@@ -16,6 +16,9 @@
 namespace dfl {
 namespace {
 
+// batch * gamma * d: one thread per 8 channels keeps the launch below 2^32 work-items
+constexpr int64_t kMaxConvElems = int64_t(1) << 34;
+
 struct ConvArgs {
     const uint16_t* x;  // [B, G, D] bf16
     const float* kern;  // [B, G, 2, n_groups]
@@ -63,6 +66,8 @@ extern "C" int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_
     if (x == y) return DFLASH_ERR_SHAPE;
     if ((d / n_groups) % 8 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15))
         return DFLASH_ERR_UNSUPPORTED;
+    // one thread per 8 channels: the launch's work-item count stays in 32 bits
+    if (capped_product(kMaxConvElems, {batch, gamma, d}) < 0) return DFLASH_ERR_UNSUPPORTED;
     ConvArgs a{x, kern, y, batch, gamma, d, n_groups, d / n_groups, (long)batch * gamma * (d / 8)};
     const long blocks = (a.n8 + 255) / 256;
     hipLaunchKernelGGL(two_tap_conv_kernel, dim3((unsigned)blocks), dim3(256), 0,

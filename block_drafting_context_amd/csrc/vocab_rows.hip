@@ -1016,6 +1016,17 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
     return ws && !(reinterpret_cast<uintptr_t>(ws) & 255) && have >= need;
 }
 
+// Shape part of spec_verify's checks: DFLASH_ERR_SHAPE, DFLASH_ERR_UNSUPPORTED
+// or OK.  The row cap keeps batch * gamma (and twice it) inside the 32-bit
+// counts of the launches.
+int verify_shape(int batch, int gamma, int vocab) {
+    if (batch < 0 || gamma < 1 || vocab < 1) return DFLASH_ERR_SHAPE;
+    if (gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab ||
+        capped_product(kMaxRowsPerCall, {batch, gamma}) < 0)
+        return DFLASH_ERR_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
 }  // namespace
 }  // namespace dfl
 
@@ -1040,7 +1051,9 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
     if (batch == 0) return DFLASH_OK;
     if (!logits || !topk_idx || !topk_val) return DFLASH_ERR_NULL;
     if (temperature > 0.f && draft && !seeds) return DFLASH_ERR_NULL;
-    if (k > 64 || gamma > 32 || vocab % 4 != 0 || vocab > kMaxTopkVocab) return DFLASH_ERR_UNSUPPORTED;
+    if (k > 64 || gamma > 32 || vocab % 4 != 0 || vocab > kMaxTopkVocab ||
+        capped_product(kMaxRowsPerCall, {batch, gamma}) < 0)
+        return DFLASH_ERR_UNSUPPORTED;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     TopKArgs f{};
     f.z = logits;
@@ -1064,7 +1077,7 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
 }
 
 extern "C" size_t spec_verify_workspace_size(int batch, int gamma, int vocab) {
-    if (batch < 0 || gamma < 1 || vocab < 1) return 0;
+    if (verify_shape(batch, gamma, vocab) != DFLASH_OK) return 0;
     return verify_layout(batch, gamma, vocab).bytes;
 }
 
@@ -1078,8 +1091,7 @@ int verify_check(const float* target_logits, const int32_t* draft_tokens, float 
     if (batch == 0) return DFLASH_OK;
     if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_ERR_NULL;
     if (temperature > 0.f && !seeds) return DFLASH_ERR_NULL;
-    if (gamma > 32 || vocab % 4 != 0 || vocab > kMaxVocab) return DFLASH_ERR_UNSUPPORTED;
-    return DFLASH_OK;
+    return verify_shape(batch, gamma, vocab);
 }
 
 size_t verify_scratch_bytes(int batch, int gamma, int vocab) {

@@ -109,7 +109,8 @@ int dflash_version(void);
  *   lse     [batch, gamma, n_q] float32, natural-log normaliser of the scaled
  *           scores; may be NULL.
  * Supported: d_head in {64, 128}; n_q % n_kv == 0; 1 <= gamma <= 32;
- *   window % 64 == 0 and window >= 64; fp32 additionally needs d_head <= 128.
+ *   window % 64 == 0, 64 <= window <= 2^28, batch*gamma*n_q <= 2^28; fp32
+ *   additionally needs d_head <= 128.
  * Accuracy: fp32 softmax and accumulation; bf16 products.
  * ------------------------------------------------------------------------ */
 size_t dflash_block_attn_workspace_size(int batch, int gamma, int n_q, int n_kv,
@@ -141,7 +142,8 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
  *            with the purpose-0 uniform of (seeds[b], step, b, r).
  *   seeds    [batch] uint64 (device); may be NULL when T == 0.
  * Supported: 1 <= k <= 64, k <= vocab, vocab % 4 == 0, vocab <= 2^23 (the
- * row's segment statistics live in one workgroup's LDS), 1 <= gamma <= 32.
+ * row's segment statistics live in one workgroup's LDS), 1 <= gamma <= 32,
+ * batch*gamma <= 2^20 (one 1,024-thread workgroup per row).
  * Workspace: none (dflash_topk_workspace_size returns 0; workspace may be
  * NULL and is ignored).  One workgroup per row does the whole row in one
  * launch.
@@ -190,7 +192,8 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
  *                 or bonus token, then -1.
  *   accepted      [batch, gamma-1] uint8 or NULL: the accept test of every
  *                 draft row (also rows after the first rejection).
- * Supported: 1 <= gamma <= 32, vocab % 4 == 0, vocab <= 2^29.
+ * Supported: 1 <= gamma <= 32, vocab % 4 == 0, vocab <= 2^29,
+ * batch*gamma <= 2^20.
  * ------------------------------------------------------------------------ */
 size_t spec_verify_workspace_size(int batch, int gamma, int vocab);
 int spec_verify(const float* target_logits, const float* draft_logits,
@@ -226,7 +229,8 @@ int spec_verify(const float* target_logits, const float* draft_logits,
  *   kv_ring  [n_layers, 2, batch, n_kv, window, d_head] bf16, in/out
  *   h_t_out  [rows, d_model] bf16, or NULL
  * Supported: d_model % 128 == 0, (n_taps*d_tgt) % 64 == 0,
- *   (n_layers*2*n_kv*d_head) % 128 == 0, d_head % 4 == 0, rows >= 1, d_model <= 8192.
+ *   (n_layers*2*n_kv*d_head) % 128 == 0, d_head % 4 == 0, 1 <= rows <= 65,535,
+ *   d_model <= 8192, n_taps*d_tgt <= 2^30, n_layers*2*n_kv*d_head <= 2^30.
  * Accuracy: bf16 products, fp32 accumulation; H_t is rounded to bf16 before
  * the K/V projection.
  * ------------------------------------------------------------------------ */
@@ -261,7 +265,7 @@ int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, const float* 
  *   path       [batch, gamma] int32 out: the chosen token of each position
  *   path_score [batch, gamma] float32 out or NULL: S_t(previous, chosen)
  * Token ids outside [0, vocab) are clamped (precondition: they are in range).
- * Supported: k <= 64, r % 8 == 0, r <= 4096.
+ * Supported: k <= 64, r % 8 == 0, r <= 4096, gamma <= 4096, batch <= 2^20.
  * Accuracy: every term is a product of three bf16 values (exact in fp64) and
  * the sum over i runs in increasing i in fp64, so the walk's choices are those
  * of the exact scores up to fp64 rounding of that sum.
@@ -287,7 +291,7 @@ int dflash_select_path(const int32_t* cand_idx, const float* cand_score, const u
  *   kern  [batch, gamma, 2, n_groups] float32 (computed from the content by
  *         the caller's projection)
  *   y     [batch, gamma, d] bf16 out (16-byte aligned; must not overlap x)
- * Supported: d % n_groups == 0, (d / n_groups) % 8 == 0.
+ * Supported: d % n_groups == 0, (d / n_groups) % 8 == 0, batch*gamma*d <= 2^34.
  * Accuracy: fp32 arithmetic, per channel one multiply (the predecessor term)
  * and one fused multiply-add (the own term added to it): two fp32
  * roundings, then the output is rounded to bf16, nearest even.
@@ -326,7 +330,7 @@ int dflash_two_tap_conv(const uint16_t* x, const float* kern, uint16_t* y, int b
  *            T == 0 or draft == NULL.
  * Work: the weights are streamed from HBM once per 256 rows of hidden.
  * Supported: 1 <= k <= 16, k <= vocab <= 1,048,576, d_model % 64 == 0,
- * d_model <= 65,536 (DFLASH_ERR_UNSUPPORTED otherwise).
+ * d_model <= 65,536, rows <= 2^20 (DFLASH_ERR_UNSUPPORTED otherwise).
  * Accuracy: bf16 products, fp32 accumulation (the GEMM); fp32 exponentials
  * and segment sums, fp64 across segments.
  * Workspace: dflash_lm_head_topk_workspace_size bytes, 256-byte aligned.
@@ -356,7 +360,7 @@ int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows
  *   kept   [rows] int32 or NULL: the nucleus size of each row
  *   temperature > 0; 0 < top_p <= 1 (top_p == 1 keeps every entry)
  * Supported: vocab < 2^24 (the fixed-point row sums below stay within 64
- * bits); DFLASH_ERR_UNSUPPORTED otherwise.
+ * bits), rows <= 2^20; DFLASH_ERR_UNSUPPORTED otherwise.
  * Accuracy: weights 2^((z - max) log2(e)/T) in fp32, summed exactly in fixed
  * point (2^-40 of the maximum's weight); the nucleus boundary is exact up to
  * that rounding of the cumulative mass.

@@ -51,6 +51,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A different build of oracle.c (the sanitizer test loads one compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer); used as given, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("DFLASH_ORACLE_LIB")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
@@ -73,10 +76,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if (not os.path.exists(_LIB_PATH)
-            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if (not os.path.exists(_LIB_PATH)
+                or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     c_int, c_i64, c_dbl, c_u64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_uint64
     sigs = {
         "orc_philox4x64_10": (None, [_U64, _U64, _U64]),

@@ -313,3 +313,48 @@ def test_verify_noalloc_validation_before_any_hip_call():
     assert dfl.spec_verify_workspace_size(1024, 32, 151936) > cap
     assert verify_na(B=1024, G=32) == -6
     assert dfl.dflash_status_string(-6) != "unknown status"
+
+
+M31 = 2**31 - 1
+
+
+def test_workspace_queries_at_extreme_sizes():
+    """Shapes an entry point rejects get 0 from its query, computed without any
+    overflowing intermediate (the sanitizer build of this file turns one into
+    a failure); an empty batch needs no workspace."""
+    assert dfl.dflash_block_attn_workspace_size(0, 8, 40, 8, 128, 4096) == 0
+    assert dfl.dflash_block_attn_workspace_size(M31, 8, 40, 8, 128, 4096) == 0
+    assert dfl.dflash_block_attn_workspace_size(1, 8, 40, 8, 128, M31 - 63) == 0
+    assert dfl.dflash_block_attn_workspace_size(1, 8, M31, 1, 128, 4096) == 0
+    assert dfl.spec_verify_workspace_size(M31, M31, M31) == 0
+    assert dfl.spec_verify_workspace_size(M31, 8, 151936) == 0
+    assert dfl.spec_verify_workspace_size(1 << 17, 8, 151936) > 0   # 2^20 rows: the cap
+    assert dfl.spec_verify_workspace_size((1 << 17) + 1, 8, 151936) == 0
+    assert dfl.dflash_context_fuse_workspace_size(M31, 5, 5120, 5120, 5, 8, 128) == 0
+    assert dfl.dflash_context_fuse_workspace_size(512, M31, M31, 5120, 5, 8, 128) == 0
+    assert dfl.dflash_context_fuse_workspace_size(512, 5, 5120, 5120, M31, M31, M31) == 0
+    assert dfl.dflash_lm_head_topk_workspace_size(M31, 5120, 151936, 8) == 0
+    assert dfl.dflash_lm_head_topk_workspace_size(256, 5120, M31, 8) == 0
+    assert dfl.dflash_lm_head_topk_workspace_size(256, M31, 151936, 8) == 0
+
+
+def test_entry_points_reject_extreme_sizes():
+    """Sizes whose derived counts (rows, products of heads and positions,
+    launch extents) would leave 32 bits are unsupported, not wrapped."""
+    assert attn(B=M31) == -3
+    assert attn(W=(1 << 28) + 64) == -3
+    assert attn(W=M31) == -3
+    assert topk(B=M31) == -3
+    assert topk(B=(1 << 17) + 1) == -3
+    assert verify(B=M31) == -3
+    assert verify_na(B=M31) == -3
+    assert select(B=M31) == -3
+    assert select(G=M31) == -3
+    assert conv(B=M31) == -3
+    assert conv(B=M31, G=M31) == -3
+    assert fuse(rows=65536) == -3
+    assert fuse(taps=M31, dt=M31) == -3
+    assert fuse(nl=M31, nkv=M31, dh=M31) == -3
+    assert head(rows=M31) == -3
+    assert head(rows=(1 << 20) + 1) == -3
+    assert topp(rows=(1 << 20) + 1) == -3
