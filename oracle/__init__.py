@@ -265,6 +265,25 @@ def top_p_mask(z, temperature, top_p):
     return out, kept
 
 
+def top_p_cut(z, temperature, top_p):
+    """z [..., V] -> (cut_logit [...], cut_index [...], kept [...]): each row's
+    top-p nucleus (the one top_p_mask keeps) named by its last entry in the rank
+    order (logit descending, index ascending).  Entry v of the row is in the
+    nucleus iff z_v > cut_logit, or z_v == cut_logit and v <= cut_index."""
+    z = _f64(z)
+    V = z.shape[-1]
+    rows = z.reshape(-1, V)
+    _, kept = top_p_mask(rows, temperature, top_p)
+    logit = np.empty(rows.shape[0])
+    index = np.empty(rows.shape[0], dtype=np.int64)
+    for r in range(rows.shape[0]):
+        order = np.lexsort((np.arange(V), -rows[r]))
+        last = order[kept[r] - 1]
+        logit[r], index[r] = rows[r, last], last
+    shape = z.shape[:-1] if z.ndim > 1 else (1,)
+    return logit.reshape(shape), index.reshape(shape), kept.reshape(shape)
+
+
 # ------------------------------------------------------------------------ verify
 def sampled_verify_seq_u(zp, zq, drafts, T, u_acc, u_draw):
     """One sequence with explicit uniforms. zp, zq [G,V] (zq None: deterministic

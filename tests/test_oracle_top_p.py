@@ -70,6 +70,48 @@ def test_top_p_one_keeps_everything_and_tiny_top_p_keeps_the_argmax():
         assert np.argmax(np.isfinite(out[r])) == np.argmax(z[r]) and np.isfinite(out[r]).sum() == 1
 
 
+def keep_rule(z, logit, index):
+    """The cut's membership rule: z_v > logit, or z_v == logit and v <= index."""
+    v = np.arange(z.shape[-1])
+    return (z > logit) | ((z == logit) & (v <= index))
+
+
+@pytest.mark.parametrize("T,top_p", [(0.7, 0.99), (1.0, 0.9), (0.5, 0.5), (0.7, 1.0), (0.7, 1e-9)])
+def test_cut_names_the_nucleus(T, top_p):
+    """The cut (last nucleus entry in rank order) reproduces the mask through
+    the membership rule, on rows with exact ties, a tied block of maxima,
+    signed zeros and -inf entries; the nucleus is the first `kept` entries of
+    numpy's rank order."""
+    rng = np.random.default_rng(zlib.crc32(repr(("cut", T, top_p)).encode()))
+    z = rng.standard_normal((10, 500)) * 2.0
+    z[2] = np.round(z[2])
+    z[4, :30] = z[4].max()
+    z[6, 100:300] = -np.inf
+    z[7, ::2] = 0.0
+    z[7, 1::2] = -0.0                               # equal values: ranked by index alone
+    out, kept = oracle.top_p_mask(z, T, top_p)
+    logit, index, kept2 = oracle.top_p_cut(z, T, top_p)
+    np.testing.assert_array_equal(kept2, kept)
+    for r in range(z.shape[0]):
+        keep = keep_rule(z[r], logit[r], index[r])
+        assert keep.sum() == kept[r]
+        first = np.zeros(z.shape[1], dtype=bool)
+        first[rank_order(z[r])[:kept[r]]] = True
+        np.testing.assert_array_equal(keep, first)
+        np.testing.assert_array_equal(out[r], np.where(keep, z[r], -np.inf))
+
+
+def test_cut_closed_forms():
+    z = np.array([[3.0, 2.0, 1.0, 0.0, -1.0], [1.0, 5.0, 5.0, 0.5, 5.0]])
+    logit, index, kept = oracle.top_p_cut(z, 1.0, 0.9)   # row 0: 0.636, 0.870, 0.956 -> 3 kept
+    assert (logit[0], index[0], kept[0]) == (1.0, 2, 3)
+    logit, index, kept = oracle.top_p_cut(z, 1.0, 1e-9)  # the argmax, lowest index among ties
+    assert (logit[1], index[1], kept[1]) == (5.0, 1, 1)
+    logit, index, kept = oracle.top_p_cut(z, 1.0, 1.0)   # everything: the last entry in rank order
+    assert (logit[0], index[0]) == (-1.0, 4) and (logit[1], index[1]) == (0.5, 3)
+    assert (kept == 5).all()
+
+
 def test_masking_is_temperature_dependent_as_defined():
     z = np.array([[3.0, 2.0, 1.0, 0.0, -1.0]])
     # T = 1: p = (0.636, 0.234, 0.086, 0.032, 0.012); cumulative 0.636, 0.870, 0.956
