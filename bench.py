@@ -603,22 +603,39 @@ def literal_vocab_figure(wl, dev, warmup, steps, attn_us, vocab=1024, k=4):
 
 def top_p_figure(wl, dev, warmup, steps, top_p=0.99):
     """NEXT row: sampled decoding with top-p 0.99 (the pages' sampled setting) at the
-    step's batch and block: both logits tensors masked to their nuclei
-    (dflash_top_p_mask, 256 + 256 rows), then the draws and verification on the
-    masked rows.  Timed with HIP events on the launching stream."""
+    step's batch and block.  The cut route: each logits tensor's nuclei as one cut per
+    row (dflash_top_p_cut, 256 + 256 rows), applied inside dflash_topk's and
+    spec_verify's own row scans.  Beside it the masking route: dflash_top_p_mask writes
+    masked copies of both tensors, which the same two calls then read.  Timed with HIP
+    events on the launching stream."""
     stream = torch.cuda.current_stream()
     mt = torch.empty_like(wl["zt"])
     md = torch.empty_like(wl["zd"])
+    tc = torch.empty((B, G, 2), dtype=torch.int32, device=dev)
+    dc = torch.empty((B, G, 2), dtype=torch.int32, device=dev)
+
+    def cut():
+        dfl.dflash_top_p_cut(wl["zt"], T, top_p, cut=tc, stream=stream)
+        dfl.dflash_top_p_cut(wl["zd"], T, top_p, cut=dc, stream=stream)
+
+    def draw_cut():
+        dfl.dflash_topk(wl["zd"], TOPK, T, seeds=wl["seeds"], step=0, outputs=wl["topk_out"],
+                        workspace=wl["ws_topk"], stream=stream, cut=dc)
+
+    def verify_cut():
+        dfl.spec_verify(wl["zt"], wl["zd"], wl["topk_out"]["draft"], T, seeds=wl["seeds"], step=0,
+                        draft_lse=wl["topk_out"]["lse"], outputs=wl["verify_out"],
+                        workspace=wl["ws_verify"], stream=stream, target_cut=tc, draft_cut=dc)
 
     def mask():
         dfl.dflash_top_p_mask(wl["zt"], T, top_p, out=mt, stream=stream)
         dfl.dflash_top_p_mask(wl["zd"], T, top_p, out=md, stream=stream)
 
-    def draw():
+    def draw_masked():
         dfl.dflash_topk(md, TOPK, T, seeds=wl["seeds"], step=0, outputs=wl["topk_out"],
                         workspace=wl["ws_topk"], stream=stream)
 
-    def verify():
+    def verify_masked():
         dfl.spec_verify(mt, md, wl["topk_out"]["draft"], T, seeds=wl["seeds"], step=0,
                         draft_lse=wl["topk_out"]["lse"], outputs=wl["verify_out"],
                         workspace=wl["ws_verify"], stream=stream)
@@ -635,16 +652,25 @@ def top_p_figure(wl, dev, warmup, steps, top_p=0.99):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
 
+    row_bytes = 2 * B * G * V * 4
     mask()
-    draw()
-    res = {"top_p": top_p, "temperature": T, "mask_512_rows_us": round(timed(mask, steps), 2),
-           "topk_masked_us": round(timed(draw, steps), 2),
-           "verify_masked_us": round(timed(verify, steps), 2)}
-    _, kept = dfl.dflash_top_p_mask(wl["zt"], T, top_p, want_kept=True, stream=stream)
+    draw_masked()
+    res = {"top_p": top_p, "temperature": T,
+           "mask_512_rows_us": round(timed(mask, steps), 2),
+           "topk_masked_us": round(timed(draw_masked, steps), 2),
+           "verify_masked_us": round(timed(verify_masked, steps), 2)}
+    cut()
+    draw_cut()
+    res.update({"cut_512_rows_us": round(timed(cut, steps), 2),
+                "topk_cut_us": round(timed(draw_cut, steps), 2),
+                "verify_cut_us": round(timed(verify_cut, steps), 2)})
+    res["cut_route_us"] = round(res["cut_512_rows_us"] + res["topk_cut_us"] + res["verify_cut_us"], 2)
+    res["mask_route_us"] = round(res["mask_512_rows_us"] + res["topk_masked_us"] + res["verify_masked_us"], 2)
+    _, kept = dfl.dflash_top_p_cut(wl["zt"], T, top_p, want_kept=True, stream=stream)
     torch.cuda.synchronize()
     res["mean_nucleus_target"] = round(float(kept.float().mean()), 1)
     res["mean_tau"] = round(wl["verify_out"]["accept_len"].float().mean().item() + 1.0, 3)
-    row_bytes = 2 * B * G * V * 4
+    res["cut_read_passes_equiv"] = round(res["cut_512_rows_us"] * 1e-6 * HBM_PEAK_GBS * 1e9 / row_bytes, 2)
     res["mask_read_passes_equiv"] = round(res["mask_512_rows_us"] * 1e-6 * HBM_PEAK_GBS * 1e9 / row_bytes, 2)
     del mt, md
     return res

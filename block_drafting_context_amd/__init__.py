@@ -22,7 +22,7 @@ __all__ = [
     "dflash_context_fuse", "dflash_context_fuse_workspace_size",
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk", "dflash_lm_head_topk_workspace_size",
-    "dflash_top_p_mask",
+    "dflash_top_p_mask", "dflash_top_p_cut", "nucleus_cut_values",
     "spec_verify_noalloc", "spec_verify_noalloc_max_scratch",
     "EXPORTED_SYMBOLS",
 ]
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "dflash_context_fuse_workspace_size", "dflash_context_fuse",
     "dflash_select_path", "dflash_two_tap_conv",
     "dflash_lm_head_topk_workspace_size", "dflash_lm_head_topk",
-    "dflash_top_p_mask",
+    "dflash_top_p_mask", "dflash_top_p_cut",
     "spec_verify_noalloc_max_scratch", "spec_verify_noalloc",
 )
 
@@ -72,9 +72,9 @@ def load():
         "dflash_block_attn_workspace_size": (_sz, [_i] * 7),
         "dflash_block_attn": (_i, [_vp] * 6 + [_f, _vp, _vp, _i] + [_i] * 6 + [_vp, _sz, _vp]),
         "dflash_topk_workspace_size": (_sz, [_i] * 4),
-        "dflash_topk": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "dflash_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "spec_verify_workspace_size": (_sz, [_i] * 3),
-        "spec_verify": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
+        "spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
                              _vp, _sz, _vp]),
         "dflash_context_fuse_workspace_size": (_sz, [_i] * 7),
         "dflash_context_fuse": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp] + [_i] * 9 +
@@ -83,10 +83,11 @@ def load():
         "dflash_two_tap_conv": (_i, [_vp] * 3 + [_i] * 4 + [_vp]),
         "dflash_lm_head_topk_workspace_size": (_sz, [_i] * 4),
         "dflash_top_p_mask": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
+        "dflash_top_p_cut": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
         "dflash_lm_head_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp]),
         "spec_verify_noalloc_max_scratch": (_sz, []),
-        "spec_verify_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
+        "spec_verify_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _u64, _vp, _vp, _vp, _i, _i, _i,
                                      _vp]),
     }
     for name, (res, args) in sig.items():
@@ -193,12 +194,15 @@ def dflash_topk_workspace_size(batch, gamma, vocab, k):
 
 
 def dflash_topk(logits, k, temperature, seeds=None, step=0, outputs=None, workspace=None,
-                stream=None):
+                stream=None, cut=None):
     """Drafter rows: logits [B,G,V] fp32 -> dict(idx [B,G,k] int32, val [B,G,k] fp32,
-    lse [B,G] fp64, draft [B,G] int32).  seeds: [B] int64 (bits read as uint64)."""
+    lse [B,G] fp64, draft [B,G] int32).  seeds: [B] int64 (bits read as uint64).
+    cut: [B,G,2] int32 nucleus cuts from dflash_top_p_cut (top-p), or None."""
     B, G, V = logits.shape
     dev = logits.device
     _need(logits, "logits", torch.float32, (B, G, V), dev)
+    if cut is not None:
+        _need(cut, "cut", torch.int32, (B, G, 2), dev)
     if seeds is not None:
         _need(seeds, "seeds", torch.int64, (B,), dev)
     o = outputs or {}
@@ -211,7 +215,7 @@ def dflash_topk(logits, k, temperature, seeds=None, step=0, outputs=None, worksp
     _need(lse, "lse", torch.float64, (B, G), dev)
     _need(draft, "draft", torch.int32, (B, G), dev)
     ws, wsb = _workspace(dflash_topk_workspace_size(B, G, V, k), dev, workspace)
-    _call("dflash_topk", _ptr(logits), B, G, V, int(k), float(temperature), _ptr(seeds),
+    _call("dflash_topk", _ptr(logits), _ptr(cut), B, G, V, int(k), float(temperature), _ptr(seeds),
           int(step), _ptr(idx), _ptr(val), _ptr(lse), _ptr(draft), _ptr(ws), wsb, _stream(stream))
     return {"idx": idx, "val": val, "lse": lse, "draft": draft}
 
@@ -222,14 +226,17 @@ def spec_verify_workspace_size(batch, gamma, vocab):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=None, step=0,
-                draft_lse=None, outputs=None, workspace=None, stream=None):
+                draft_lse=None, outputs=None, workspace=None, stream=None, target_cut=None,
+                draft_cut=None):
     """target_logits, draft_logits [B,G,V] fp32 (draft_logits None with temperature > 0:
     deterministic drafts, e.g. from dflash_select_path); draft_tokens [B,G] int32 (first G-1
-    used); draft_lse [B,G] fp64 or None.  Returns dict(accept_len [B] int32, out_tokens [B,G]
-    int32, accepted [B,G-1] uint8)."""
+    used); draft_lse [B,G] fp64 or None; target_cut, draft_cut [B,G,2] int32 nucleus cuts
+    (top-p) or None.  Returns dict(accept_len [B] int32, out_tokens [B,G] int32, accepted
+    [B,G-1] uint8)."""
     B, G, V = target_logits.shape
     dev = target_logits.device
     _need(target_logits, "target_logits", torch.float32, (B, G, V), dev)
+    _check_cuts(target_cut, draft_cut, B, G, dev)
     if draft_logits is not None:
         _need(draft_logits, "draft_logits", torch.float32, (B, G, V), dev)
     _need(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
@@ -246,9 +253,16 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seeds=No
     _need(accepted, "accepted", torch.uint8, (B, max(G - 1, 1)), dev)
     ws, wsb = _workspace(spec_verify_workspace_size(B, G, V), dev, workspace)
     _call("spec_verify", _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
-          _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
+          _ptr(draft_lse), _ptr(target_cut), _ptr(draft_cut), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
           _ptr(out_tok), _ptr(accepted), B, G, V, _ptr(ws), wsb, _stream(stream))
     return {"accept_len": acc_len, "out_tokens": out_tok, "accepted": accepted[:, :G - 1]}
+
+
+def _check_cuts(target_cut, draft_cut, B, G, dev):
+    if target_cut is not None:
+        _need(target_cut, "target_cut", torch.int32, (B, G, 2), dev)
+    if draft_cut is not None:
+        _need(draft_cut, "draft_cut", torch.int32, (B, G, 2), dev)
 
 
 def spec_verify_noalloc_max_scratch():
@@ -256,7 +270,8 @@ def spec_verify_noalloc_max_scratch():
 
 
 def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, outputs,
-                        seeds=None, step=0, draft_lse=None, stream=None):
+                        seeds=None, step=0, draft_lse=None, stream=None, target_cut=None,
+                        draft_cut=None):
     """spec_verify with the library's static per-GPU scratch instead of a workspace: the
     call allocates nothing, so the caller passes every output (dict accept_len [B] int32,
     out_tokens [B,G] int32, accepted [B,G-1] uint8).  Calls that overlap on one GPU race."""
@@ -270,12 +285,13 @@ def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, 
         _need(draft_lse, "draft_lse", torch.float64, (B, G), dev)
     if seeds is not None:
         _need(seeds, "seeds", torch.int64, (B,), dev)
+    _check_cuts(target_cut, draft_cut, B, G, dev)
     acc_len, out_tok, accepted = outputs["accept_len"], outputs["out_tokens"], outputs["accepted"]
     _need(acc_len, "accept_len", torch.int32, (B,), dev)
     _need(out_tok, "out_tokens", torch.int32, (B, G), dev)
     _need(accepted, "accepted", torch.uint8, (B, max(G - 1, 1)), dev)
     _call("spec_verify_noalloc", _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
-          _ptr(draft_lse), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
+          _ptr(draft_lse), _ptr(target_cut), _ptr(draft_cut), float(temperature), _ptr(seeds), int(step), _ptr(acc_len),
           _ptr(out_tok), _ptr(accepted), B, G, V, _stream(stream))
     return outputs
 
@@ -332,6 +348,29 @@ def dflash_top_p_mask(logits, temperature, top_p, out=None, want_kept=False, str
     _call("dflash_top_p_mask", _ptr(logits), _ptr(out), _ptr(kept), rows, V, float(temperature),
           float(top_p), _stream(stream))
     return out, kept
+
+
+def dflash_top_p_cut(logits, temperature, top_p, cut=None, want_kept=False, stream=None):
+    """logits [..., V] fp32 -> (nucleus cuts [..., 2] int32: the bits of the last nucleus
+    entry's logit, then its index; nucleus sizes [...] int32 or None).  The cuts go to
+    dflash_topk(cut=...) and spec_verify(target_cut=..., draft_cut=...)."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    dev = logits.device
+    _need(logits, "logits", torch.float32, None, dev)
+    shape = tuple(logits.shape[:-1]) + (2,)
+    cut = cut if cut is not None else torch.empty(shape, dtype=torch.int32, device=dev)
+    _need(cut, "cut", torch.int32, shape, dev)
+    kept = torch.empty(logits.shape[:-1], dtype=torch.int32, device=dev) if want_kept else None
+    _call("dflash_top_p_cut", _ptr(logits), _ptr(cut), _ptr(kept), rows, V, float(temperature),
+          float(top_p), _stream(stream))
+    return cut, kept
+
+
+def nucleus_cut_values(cut):
+    """Cuts [..., 2] int32 -> (logit [...] fp32, index [...] int32): entry v of the row is
+    in the nucleus iff z_v > logit, or z_v == logit and v <= index."""
+    return cut[..., 0].view(torch.float32), cut[..., 1]
 
 
 # -------------------------------------------------------------------- LM head

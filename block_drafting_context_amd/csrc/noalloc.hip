@@ -46,7 +46,8 @@ extern "C" size_t spec_verify_noalloc_max_scratch(void) { return kScratchBytes; 
 
 extern "C" int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
                                    const int32_t* draft_tokens, const double* draft_lse,
-                                   float temperature, const uint64_t* seeds, uint64_t step,
+                                   const dflash_nucleus_cut* target_cut,
+                                   const dflash_nucleus_cut* draft_cut, float temperature, const uint64_t* seeds, uint64_t step,
                                    int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
                                    int batch, int gamma, int vocab, void* stream) {
     int rc = verify_check(target_logits, draft_tokens, temperature, seeds, accept_len, out_tokens,
@@ -56,7 +57,7 @@ extern "C" int spec_verify_noalloc(const float* target_logits, const float* draf
     void* ws = nullptr;
     rc = scratch_address(&ws);
     if (rc) return rc;
-    return verify_enqueue(target_logits, draft_logits, draft_tokens, draft_lse, temperature, seeds,
-                          step, accept_len, out_tokens, accepted, batch, gamma, vocab, ws,
-                          reinterpret_cast<hipStream_t>(stream));
+    return verify_enqueue(target_logits, draft_logits, draft_tokens, draft_lse, target_cut, draft_cut,
+                          temperature, seeds, step, accept_len, out_tokens, accepted, batch, gamma,
+                          vocab, ws, reinterpret_cast<hipStream_t>(stream));
 }

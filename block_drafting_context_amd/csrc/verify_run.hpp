@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dflash.h"
+
 namespace dfl {
 
 // Checks every host-checkable argument of spec_verify (no HIP call); returns
@@ -21,9 +23,10 @@ size_t verify_scratch_bytes(int batch, int gamma, int vocab);
 // Enqueues the verification kernels on st, with their scratch at `scratch_ws`
 // (256-byte aligned, verify_scratch_bytes bytes).  Arguments already checked.
 int verify_enqueue(const float* target_logits, const float* draft_logits,
-                   const int32_t* draft_tokens, const double* draft_lse, float temperature,
-                   const uint64_t* seeds, uint64_t step, int32_t* accept_len, int32_t* out_tokens,
-                   uint8_t* accepted, int batch, int gamma, int vocab, void* scratch_ws,
-                   hipStream_t st);
+                   const int32_t* draft_tokens, const double* draft_lse,
+                   const dflash_nucleus_cut* target_cut, const dflash_nucleus_cut* draft_cut,
+                   float temperature, const uint64_t* seeds, uint64_t step, int32_t* accept_len,
+                   int32_t* out_tokens, uint8_t* accepted, int batch, int gamma, int vocab,
+                   void* scratch_ws, hipStream_t st);
 
 }  // namespace dfl

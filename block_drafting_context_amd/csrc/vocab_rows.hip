@@ -40,7 +40,9 @@
 // of a sequence through a per-sequence atomic counter instead was slower:
 // the counters serialise and the device-scope handoff costs a memory round
 // trip per wave.)
+#include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 #include "verify_run.hpp"
@@ -97,19 +99,68 @@ __device__ __forceinline__ void load_segment(f32x4 (&v)[kIters], __amdgpu_buffer
                                               rsrc, (int)(base + it * 1024u), 0, kLoadStream));
 }
 
+// Top-p nucleus of a row (dflash_nucleus_cut): entry (z, v) is kept iff
+// z > logit, or z == logit and v <= index; an entry outside it is taken as
+// -inf, exactly as in a row masked to its nucleus.  NoCut keeps every entry
+// and compiles to nothing.
+struct RowCut {
+    float logit;
+    int index;
+    __device__ __forceinline__ float one(float z, int v) const {
+        return (z > logit || (z == logit && v <= index)) ? z : -INFINITY;
+    }
+    __device__ __forceinline__ void quad(f32x4& q, int v0) const {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = one(q[c], v0 + c);
+    }
+    // The lane's entries v[it][c] = entry base + it*256 + c of segment `seg`
+    // (wave-uniform).  Within a segment v <= index holds for every entry or
+    // for none, except in the one segment holding `index`: one comparison
+    // per entry elsewhere.
+    __device__ __forceinline__ void segment(f32x4 (&v)[kIters], int seg, int base) const {
+        const int s0 = seg * kSeg;
+        if (s0 + kSeg - 1 <= index) {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[it][c] = v[it][c] >= logit ? v[it][c] : -INFINITY;
+        } else if (s0 > index) {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[it][c] = v[it][c] > logit ? v[it][c] : -INFINITY;
+        } else {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) quad(v[it], base + it * 256);
+        }
+    }
+};
+struct NoCut {
+    __device__ __forceinline__ float one(float z, int) const { return z; }
+    __device__ __forceinline__ void quad(f32x4&, int) const {}
+    __device__ __forceinline__ void segment(f32x4 (&)[kIters], int, int) const {}
+};
+// The cut of row `row`, or one that keeps everything when the caller gave no
+// cuts; the load is issued either way (from `valid`, any readable 8 bytes).
+__device__ __forceinline__ RowCut row_cut(const dflash_nucleus_cut* cuts, size_t row, const void* valid) {
+    const dflash_nucleus_cut c = *(cuts ? cuts + row : reinterpret_cast<const dflash_nucleus_cut*>(valid));
+    return cuts ? RowCut{c.logit, c.index} : RowCut{-INFINITY, INT_MAX};
+}
+
 // ------------------------------------------------------------ row scan
 // Wave `wave` of a row workgroup streams its run of segments and stores each
 // segment's maximum (and, with kSumExp, its exp-sum) through lane 0 into
 // sm[seg] / ss[seg] (LDS or global); with kArgmax it keeps its argmax.
 // hook(v, qm, seg) then sees the segment's values (entries past the row's end
-// set to -inf) and the lane's quad maxima qm[it] = max of v[it].
+// and, with a cut, entries outside the row's nucleus set to -inf) and the
+// lane's quad maxima qm[it] = max of v[it].
 struct NoHook {
     __device__ __forceinline__ void operator()(f32x4 (&)[kIters], const float (&)[kIters], int) const {}
 };
-template <int MODE, class MArr, class SArr, class Hook = NoHook>
+template <int MODE, class MArr, class SArr, class Hook = NoHook, class CutT = NoCut>
 __device__ __forceinline__ void scan_row(const float* zr, int V, int nseg, float c2, MArr sm, SArr ss,
                                          float& best_v, int& best_i, int wave, int lane,
-                                         Hook hook = Hook()) {
+                                         Hook hook = Hook(), CutT cut = CutT()) {
     const int seg0 = (int)((long)wave * nseg / kRowWaves);
     const int seg1 = (int)((long)(wave + 1) * nseg / kRowWaves);
     const __amdgpu_buffer_rsrc_t rsrc = row_rsrc(zr, V);
@@ -123,6 +174,7 @@ __device__ __forceinline__ void scan_row(const float* zr, int V, int nseg, float
             for (int it = 0; it < kIters; ++it)
                 if (base + it * 256 >= V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
+        cut.segment(v, seg, base);
         if (MODE & kArgmax) {
 #pragma unroll
             for (int it = 0; it < kIters; ++it)
@@ -303,26 +355,28 @@ __device__ __forceinline__ f32x4 load_quad(__amdgpu_buffer_rsrc_t rsrc, int v) {
                                                                            kLoadDefault));
 }
 
-// Weight 2^((z - m_s) * c2) of softmax(z / T) relative to a segment maximum.
+// Weight 2^((z - m_s) * c2) of softmax(z / T) relative to a segment maximum
+// (0 outside the row's nucleus).
+template <class CutT>
 struct SoftmaxW {
     __amdgpu_buffer_rsrc_t zr;
     float ms, c2;
+    CutT cut;
     typedef f32x4 Raw;
     __device__ __forceinline__ Raw load(int v) const { return load_quad(zr, v); }
-    __device__ __forceinline__ f32x4 w4(const Raw& z, int) const {
+    __device__ __forceinline__ f32x4 w4(const Raw& z, int v) const {
         f32x4 r;
-        r[0] = fast_exp2((z[0] - ms) * c2);
-        r[1] = fast_exp2((z[1] - ms) * c2);
-        r[2] = fast_exp2((z[2] - ms) * c2);
-        r[3] = fast_exp2((z[3] - ms) * c2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r[c] = fast_exp2((cut.one(z[c], v + c) - ms) * c2);
         return r;
     }
 };
 
-// Draw from softmax(z / T) of one row using its segment statistics.
-template <class MArr, class SArr>
+// Draw from softmax(z / T) of one row (restricted to its nucleus, with a
+// cut) using its segment statistics.
+template <class MArr, class SArr, class CutT = NoCut>
 __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, MArr sm, SArr ss, int nseg, float c2,
-                                                float M, double S, double u, int lane) {
+                                                float M, double S, double u, int lane, CutT cut = CutT()) {
     const double target = u * S;
     double before = 0.0;
     auto segw = [&](int s) -> double {
@@ -333,7 +387,7 @@ __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, MArr sm,
     const float ms = sm[seg];
     const double f = (double)fast_exp2((ms - M) * c2);
     const double tgt = (target - before) / f;
-    const SoftmaxW wfn{row_rsrc(zr, V), ms, c2};
+    const SoftmaxW<CutT> wfn{row_rsrc(zr, V), ms, c2, cut};
     return draw_in_segment(seg, V, tgt, wfn, lane);
 }
 
@@ -413,6 +467,7 @@ __device__ __forceinline__ float kth_segment_max(const float* sm, int nseg, int 
 // --------------------------------------------------------------- top-k
 struct TopKArgs {
     const float* z;
+    const dflash_nucleus_cut* cut;  // [rows] (CUT instantiations only)
     int B, G, V, nseg, k;
     float T, c2;
     const uint64_t* seeds;
@@ -424,8 +479,9 @@ struct TopKArgs {
 };
 
 // One row per workgroup of sixteen waves: the scan, then waves 0-14 find tau
-// and the top k while wave 15 merges the log-normaliser and draws.
-template <int MODE>
+// and the top k while wave 15 merges the log-normaliser and draws.  CUT: every
+// read of the row applies the row's nucleus cut.
+template <int MODE, bool CUT>
 __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
     __shared__ __attribute__((aligned(16))) float s_m[kMaxTopkSeg];
     __shared__ double s_s[kMaxTopkSeg];
@@ -445,11 +501,14 @@ __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
     // the draw's uniform depends on no data: computed before the scan
     const bool draws = wave == kFinWaves && a.T > 0.f && a.draft;
     const double u_draw = draws ? philox_uniform(a.seeds[b], a.step, (uint64_t)b, (uint64_t)r, kDraftDraw) : 0.0;
+    typedef typename std::conditional<CUT, RowCut, NoCut>::type CutT;
+    CutT cut{};
+    if constexpr (CUT) cut = RowCut{a.cut[row].logit, a.cut[row].index};
 
     {
         float bv;
         int bi;
-        scan_row<MODE>(zr, a.V, a.nseg, a.c2, s_m, s_s, bv, bi, wave, lane);
+        scan_row<MODE>(zr, a.V, a.nseg, a.c2, s_m, s_s, bv, bi, wave, lane, NoHook(), cut);
     }
     if (tid == 0) { s_tau = -INFINITY; s_nf = 0; }
     __syncthreads();
@@ -488,7 +547,7 @@ __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
             merge_row_stats(s_m, s_s, a.nseg, a.c2, lane, M, S);
             if (a.lse && lane == 0) a.lse[row] = (double)M / (double)a.T + log(S);
             if (a.draft) {
-                const int tok = draw_softmax_row(zr, a.V, s_m, s_s, a.nseg, a.c2, M, S, u_draw, lane);
+                const int tok = draw_softmax_row(zr, a.V, s_m, s_s, a.nseg, a.c2, M, S, u_draw, lane, cut);
                 if (lane == 0) a.draft[row] = tok;
             }
         }
@@ -514,6 +573,7 @@ __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
             bool pass[kIters];
             uint64_t mask[kIters];
             int total = 0;
+            cut.segment(v, seg, base);
 #pragma unroll
             for (int it = 0; it < kIters; ++it) {
                 // quads past the row's end read as zeros: they take no part
@@ -693,6 +753,8 @@ __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
 struct RowArgs {
     const float* zp;    // target logits [B, G, V]: rows 0 .. rows-1 of the launch
     const float* zq;    // drafter logits [B, G, V]: rows rows .. 2 rows-1 (log-normaliser only)
+    const dflash_nucleus_cut* tcut;  // [B G] or null, for the target rows (CUT only)
+    const dflash_nucleus_cut* dcut;  // [B G] or null, for the drafter rows
     int rows, V, nseg, B;
     float c2;
     float* seg_m;       // [launch rows][nseg]
@@ -704,7 +766,8 @@ struct RowArgs {
 
 // Statistics of one target (or drafter) row per workgroup: the segment
 // statistics (global, for the draws) and the row's M and S, or its argmax.
-template <int MODE>
+// CUT: the row is read through its nucleus cut (if its side has cuts).
+template <int MODE, bool CUT>
 __global__ void __launch_bounds__(kRowThreads) verify_row_kernel(RowArgs a) {
     __shared__ float s_v[kRowWaves];
     __shared__ int s_i[kRowWaves];
@@ -715,7 +778,12 @@ __global__ void __launch_bounds__(kRowThreads) verify_row_kernel(RowArgs a) {
     double* ss = a.seg_s + (size_t)row * a.nseg;
     float bv;
     int bi;
-    scan_row<MODE>(zr, a.V, a.nseg, a.c2, sm, ss, bv, bi, wave, lane);
+    if constexpr (CUT) {
+        const RowCut cut = row < a.rows ? row_cut(a.tcut, row, zr) : row_cut(a.dcut, row - a.rows, zr);
+        scan_row<MODE>(zr, a.V, a.nseg, a.c2, sm, ss, bv, bi, wave, lane, NoHook(), cut);
+    } else {
+        scan_row<MODE>(zr, a.V, a.nseg, a.c2, sm, ss, bv, bi, wave, lane);
+    }
     if (MODE & kArgmax) {
         wave_best(bv, bi);
         if (lane == 0) { s_v[wave] = bv; s_i[wave] = bi; }
@@ -756,6 +824,8 @@ struct TailArgs {
     const float* zq;   // draft logits  [B, G, V] or null
     const int32_t* drafts;  // [B, G]
     const double* draft_lse;  // [B, G] or null
+    const dflash_nucleus_cut* tcut;  // [B, G] or null: nuclei of the target rows
+    const dflash_nucleus_cut* dcut;  // [B, G] or null: nuclei of the drafter rows
     int B, G, V, nseg, nr;    // nr: workgroups per sequence
     float T, c2;
     const uint64_t* seeds;
@@ -783,6 +853,7 @@ struct ResidualW {
     bool has_q;
     int dq;
     float Rp, Rq, Fp, Fq, c2;
+    RowCut cp, cq;  // the rows' nuclei (keep everything without cuts)
     struct Raw {
         f32x4 p, q;
     };
@@ -791,8 +862,8 @@ struct ResidualW {
         f32x4 r;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float p = fast_exp2((z.p[c] - Rp) * c2) * Fp;
-            const float q = fast_exp2((z.q[c] - Rq) * c2) * Fq;
+            const float p = fast_exp2((cp.one(z.p[c], v + c) - Rp) * c2) * Fp;
+            const float q = fast_exp2((cq.one(z.q[c], v + c) - Rq) * c2) * Fq;
             // point-mass q: p - 1 < 0 at the draft, p - 0 elsewhere
             r[c] = has_q ? fmaxf(p - q, 0.f) : (v + c == dq ? 0.f : p);
         }
@@ -830,8 +901,10 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     const double lse_given = (a.draft_lse ? a.draft_lse : a.row_S)[row];
     const uint64_t seed = *(a.seeds ? a.seeds + b : reinterpret_cast<const uint64_t*>(a.row_S));
     const int d = is_draft ? clamp_tok(d_raw, a.V) : 0;
-    const float zpd = a.zp[row * a.V + d];
-    const float zqd = (a.zq ? a.zq : a.zp)[row * a.V + d];
+    const RowCut tc = row_cut(a.tcut, row, a.row_S);
+    const RowCut dc = row_cut(a.dcut, row, a.row_S);
+    const float zpd = tc.one(a.zp[row * a.V + d], d);
+    const float zqd = dc.one((a.zq ? a.zq : a.zp)[row * a.V + d], d);
     int acc = 0;
     double lsep = 0.0, lseq = 0.0;
     if (a.T == 0.f) {
@@ -864,8 +937,10 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
             const float Ml = __builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, M), G - 1));
             const double Sl = lane_value(S, G - 1);
             const double u = philox_uniform(seed, a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
+            const RowCut cl{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, tc.logit), G - 1)),
+                            lane_value(tc.index, G - 1)};
             final_tok = draw_softmax_row(a.zp + rl * a.V, a.V, a.seg_m + rl * a.nseg, a.seg_s + rl * a.nseg,
-                                         a.nseg, a.c2, Ml, Sl, u, lane);
+                                         a.nseg, a.c2, Ml, Sl, u, lane, cl);
         }
         if (lane == 0) a.accept_len[b] = j;
         if (a.T > 0.f) {
@@ -908,6 +983,10 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     w.Fp = (float)exp((double)w.Rp / Td - lp);
     w.Fq = (float)exp((double)w.Rq / Td - lq);
     w.c2 = a.c2;
+    w.cp = RowCut{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, tc.logit), j)),
+                  lane_value(tc.index, j)};
+    w.cq = RowCut{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, dc.logit), j)),
+                  lane_value(dc.index, j)};
     const int base = seg * kSeg + 4 * lane;
     // the segment's loads of both rows are issued before any is used (a quad
     // past the row's end reads zeros and weighs nothing)
@@ -952,6 +1031,9 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
     const uint64_t seed = a.seeds[b];
     if (sd.j < 0) return;
     const int j = sd.j;
+    const size_t rj = (size_t)b * a.G + j;
+    const RowCut tc = row_cut(a.tcut, rj, a.row_S);
+    const RowCut dc = row_cut(a.dcut, rj, a.row_S);
     double tot = 0.0;
 #pragma unroll
     for (int c = 0; c < kResidRegs; ++c) tot += rv[c];
@@ -972,6 +1054,8 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
         w.Fp = sd.Fp;
         w.Fq = sd.Fq;
         w.c2 = a.c2;
+        w.cp = tc;
+        w.cq = dc;
         double before = 0.0;
         auto segw = [&](int q) -> double {
             const int c = q >> 6;
@@ -985,7 +1069,7 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
         tok = sj < 0 ? 0 : draw_in_segment(sj, a.V, target - before, w, lane);
     } else {
         tok = draw_softmax_row(zpr, a.V, a.seg_m + rowj * a.nseg, a.seg_s + rowj * a.nseg, a.nseg, a.c2, sd.Mj,
-                               sd.Sj, u, lane);
+                               sd.Sj, u, lane, tc);
     }
     if (lane == 0) a.out_tokens[rowj] = tok;
 }
@@ -1040,7 +1124,8 @@ extern "C" size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, in
     return 0;  // everything lives in the row workgroup's LDS
 }
 
-extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
+extern "C" int dflash_topk(const float* logits, const dflash_nucleus_cut* cut, int batch, int gamma,
+                           int vocab, int k,
                            float temperature, const uint64_t* seeds, uint64_t step,
                            int32_t* topk_idx, float* topk_val, double* lse, int32_t* draft,
                            void* workspace, size_t workspace_bytes, void* stream) {
@@ -1057,6 +1142,7 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     TopKArgs f{};
     f.z = logits;
+    f.cut = cut;
     f.B = batch;
     f.G = gamma;
     f.V = vocab;
@@ -1071,8 +1157,13 @@ extern "C" int dflash_topk(const float* logits, int batch, int gamma, int vocab,
     f.lse = lse;
     f.draft = draft;
     const dim3 grid((unsigned)(batch * gamma)), block(kRowThreads);
-    if (temperature > 0.f) hipLaunchKernelGGL(topk_row_kernel<kSumExp>, grid, block, 0, st, f);
-    else hipLaunchKernelGGL(topk_row_kernel<kSegMax>, grid, block, 0, st, f);
+    if (temperature > 0.f) {
+        if (cut) hipLaunchKernelGGL((topk_row_kernel<kSumExp, true>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((topk_row_kernel<kSumExp, false>), grid, block, 0, st, f);
+    } else {
+        if (cut) hipLaunchKernelGGL((topk_row_kernel<kSegMax, true>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((topk_row_kernel<kSegMax, false>), grid, block, 0, st, f);
+    }
     return launch_status();
 }
 
@@ -1099,10 +1190,13 @@ size_t verify_scratch_bytes(int batch, int gamma, int vocab) {
 }
 
 int verify_enqueue(const float* target_logits, const float* draft_logits,
-                   const int32_t* draft_tokens, const double* draft_lse, float temperature,
-                   const uint64_t* seeds, uint64_t step, int32_t* accept_len, int32_t* out_tokens,
-                   uint8_t* accepted, int batch, int gamma, int vocab, void* scratch_ws,
-                   hipStream_t st) {
+                   const int32_t* draft_tokens, const double* draft_lse,
+                   const dflash_nucleus_cut* target_cut, const dflash_nucleus_cut* draft_cut,
+                   float temperature, const uint64_t* seeds, uint64_t step, int32_t* accept_len,
+                   int32_t* out_tokens, uint8_t* accepted, int batch, int gamma, int vocab,
+                   void* scratch_ws, hipStream_t st) {
+    // the argmax is always in the nucleus: cuts only matter when sampling
+    if (temperature == 0.f) target_cut = draft_cut = nullptr;
     const VerifyLayout L = verify_layout(batch, gamma, vocab);
     char* ws = static_cast<char*>(scratch_ws);
     const float c2 = temperature > 0.f ? (float)(1.4426950408889634 / (double)temperature) : 0.f;
@@ -1110,6 +1204,8 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
     RowArgs ra{};
     ra.zp = target_logits;
     ra.zq = draft_logits;
+    ra.tcut = target_cut;
+    ra.dcut = draft_cut;
     ra.rows = rows;
     ra.V = vocab;
     ra.nseg = L.nseg;
@@ -1121,13 +1217,19 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
     ra.row_S = reinterpret_cast<double*>(ws + L.row_S);
     ra.row_arg = reinterpret_cast<int*>(ws + L.row_arg);
     if (temperature == 0.f) {
-        hipLaunchKernelGGL(verify_row_kernel<kArgmax>, dim3((unsigned)rows), dim3(kRowThreads), 0, st, ra);
+        hipLaunchKernelGGL((verify_row_kernel<kArgmax, false>), dim3((unsigned)rows), dim3(kRowThreads), 0, st,
+                           ra);
     } else {
         // the drafter rows' log-normalisers come from the same launch when
         // they are not given
-        const int launch_rows = (!draft_lse && draft_logits) ? 2 * rows : rows;
-        hipLaunchKernelGGL(verify_row_kernel<kSumExp>, dim3((unsigned)launch_rows), dim3(kRowThreads), 0, st,
-                           ra);
+        const bool both = !draft_lse && draft_logits;
+        const int launch_rows = both ? 2 * rows : rows;
+        if (target_cut || (both && draft_cut))
+            hipLaunchKernelGGL((verify_row_kernel<kSumExp, true>), dim3((unsigned)launch_rows), dim3(kRowThreads),
+                               0, st, ra);
+        else
+            hipLaunchKernelGGL((verify_row_kernel<kSumExp, false>), dim3((unsigned)launch_rows),
+                               dim3(kRowThreads), 0, st, ra);
     }
     int rc = launch_status();
     if (rc) return rc;
@@ -1136,6 +1238,8 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
     t.zq = draft_logits;
     t.drafts = draft_tokens;
     t.draft_lse = draft_lse;
+    t.tcut = target_cut;
+    t.dcut = draft_logits ? draft_cut : nullptr;
     t.B = batch;
     t.G = gamma;
     t.V = vocab;
@@ -1166,6 +1270,7 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
 
 extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
                            const int32_t* draft_tokens, const double* draft_lse,
+                           const dflash_nucleus_cut* target_cut, const dflash_nucleus_cut* draft_cut,
                            float temperature, const uint64_t* seeds, uint64_t step,
                            int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
                            int batch, int gamma, int vocab, void* workspace,
@@ -1175,7 +1280,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     if (rc || batch == 0) return rc;
     if (!ws_ok(workspace, workspace_bytes, verify_scratch_bytes(batch, gamma, vocab)))
         return DFLASH_ERR_WORKSPACE;
-    return verify_enqueue(target_logits, draft_logits, draft_tokens, draft_lse, temperature, seeds,
-                          step, accept_len, out_tokens, accepted, batch, gamma, vocab, workspace,
-                          reinterpret_cast<hipStream_t>(stream));
+    return verify_enqueue(target_logits, draft_logits, draft_tokens, draft_lse, target_cut, draft_cut,
+                          temperature, seeds, step, accept_len, out_tokens, accepted, batch, gamma,
+                          vocab, workspace, reinterpret_cast<hipStream_t>(stream));
 }

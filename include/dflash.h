@@ -1,7 +1,7 @@
 /*
  * dflash.h -- C ABI of the MI355X (gfx950) DFlash2 block-drafting hot path.
  *
- * Four operations, each a stream-ordered sequence of hand-written HIP kernels:
+ * Entry points, each a stream-ordered sequence of hand-written HIP kernels:
  *
  *   dflash_context_fuse  fuse tapped target hidden states into the context
  *                        representation H_t and append every draft layer's
@@ -14,7 +14,9 @@
  *                        candidates of each block position.
  *   dflash_two_tap_conv  the two-tap dynamic convolution inside a block.
  *   dflash_top_p_mask    top-p (nucleus) truncation of logits rows, for
- *                        sampling and verifying with top-p.
+ *                        sampling and verifying with top-p;
+ *   dflash_top_p_cut     the same nucleus as one cut per row, which
+ *                        dflash_topk and spec_verify apply in their scans.
  *   dflash_lm_head_topk  the drafter's LM head with top-k, log-normaliser and
  *                        drafted token computed in the GEMM epilogue (the
  *                        logits never reach memory).
@@ -122,6 +124,20 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * A top-p nucleus of one logits row, named by its last entry in the rank
+ * order (logit descending, index ascending; -0.0 and +0.0 are equal):
+ * entry v, logit z_v, is in the nucleus iff z_v > logit, or z_v == logit
+ * and v <= index.  {-inf, INT32_MAX} keeps every entry.  Written by
+ * dflash_top_p_cut; dflash_topk and spec_verify take one per row and treat
+ * every entry outside it as -inf, exactly as on rows masked by
+ * dflash_top_p_mask, without a masked copy of the rows.
+ * ------------------------------------------------------------------------ */
+typedef struct dflash_nucleus_cut {
+    float logit;
+    int32_t index;
+} dflash_nucleus_cut;
+
+/* ------------------------------------------------------------------------
  * dflash_topk -- drafter side of one block: per-position top-k candidates,
  * log-normaliser and drafted token.
  *
@@ -131,6 +147,9 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
  *
  *   logits   [batch, gamma, vocab] float32; row r is the drafter's logits of
  *            block position r+1 (the token after anchor + r masks).
+ *   cut      [batch, gamma] nucleus cuts (top-p sampling), or NULL: every
+ *            output below is that of the row with the entries outside its
+ *            nucleus set to -inf.
  *   topk_idx [batch, gamma, k] int32, topk_val [batch, gamma, k] float32:
  *            the k largest raw logits of each row, descending; equal logits
  *            in increasing index order.
@@ -149,7 +168,8 @@ int dflash_block_attn(const void* q, const void* k_blk, const void* v_blk,
  * launch.
  * ------------------------------------------------------------------------ */
 size_t dflash_topk_workspace_size(int batch, int gamma, int vocab, int k);
-int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
+int dflash_topk(const float* logits, const dflash_nucleus_cut* cut, int batch, int gamma,
+                int vocab, int k,
                 float temperature, const uint64_t* seeds, uint64_t step,
                 int32_t* topk_idx, float* topk_val, double* lse, int32_t* draft,
                 void* workspace, size_t workspace_bytes, void* stream);
@@ -182,9 +202,14 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
  *   draft_tokens  [batch, gamma] int32 (as written by dflash_topk); entries
  *            0..gamma-2 are the drafts, in [0, vocab) (precondition); entry
  *            gamma-1 is ignored (so dflash_topk's output passes unchanged).
- *   draft_lse     [batch, gamma] float64 from dflash_topk at the same T;
- *            may be NULL (then recomputed from draft_logits; unused with
- *            deterministic drafts).
+ *   draft_lse     [batch, gamma] float64 from dflash_topk at the same T (and
+ *            the same draft_cut); may be NULL (then recomputed from
+ *            draft_logits; unused with deterministic drafts).
+ *   target_cut, draft_cut  [batch, gamma] nucleus cuts (top-p sampling), or
+ *            NULL: p_r and q_r are then the softmax of the rows with the
+ *            entries outside their nuclei set to -inf (the truncated
+ *            distributions), exactly as on rows masked by dflash_top_p_mask.
+ *            Unused when T == 0 (the argmax is always in the nucleus).
  *   seeds         [batch] uint64 (device); may be NULL when T == 0.
  *   accept_len    [batch] int32: j = accepted drafts (0..gamma-1);
  *                 tau = j + 1 tokens are committed.
@@ -198,6 +223,7 @@ int dflash_topk(const float* logits, int batch, int gamma, int vocab, int k,
 size_t spec_verify_workspace_size(int batch, int gamma, int vocab);
 int spec_verify(const float* target_logits, const float* draft_logits,
                 const int32_t* draft_tokens, const double* draft_lse,
+                const dflash_nucleus_cut* target_cut, const dflash_nucleus_cut* draft_cut,
                 float temperature, const uint64_t* seeds, uint64_t step,
                 int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
                 int batch, int gamma, int vocab,
@@ -370,6 +396,25 @@ int dflash_top_p_mask(const float* logits, float* out, int32_t* kept, int rows, 
                       float temperature, float top_p, void* stream);
 
 /* ------------------------------------------------------------------------
+ * dflash_top_p_cut -- the same nucleus as dflash_top_p_mask, returned as one
+ * cut per row instead of a masked copy of the rows.
+ *
+ * "Beam 1.0 DFlash2" model card, "Evaluation" (temperature 0.7, top-p 0.99
+ * for sampled runs); the cut is handed to dflash_topk and spec_verify, whose
+ * row scans apply it, so top-p decoding reads each row three times here
+ * (maximum, mass histogram, boundary gather) and writes nothing per entry.
+ *
+ *   logits [rows, vocab] float32 (finite or -inf)
+ *   cut    [rows] out: the last nucleus entry (logit, index); {-inf,
+ *          INT32_MAX} when top_p == 1 or the row is all -inf
+ *   kept   [rows] int32 or NULL: the nucleus size of each row
+ * Arguments, limits and accuracy as dflash_top_p_mask.
+ * No workspace; one workgroup per row.
+ * ------------------------------------------------------------------------ */
+int dflash_top_p_cut(const float* logits, dflash_nucleus_cut* cut, int32_t* kept, int rows,
+                     int vocab, float temperature, float top_p, void* stream);
+
+/* ------------------------------------------------------------------------
  * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same operation, arguments and results as
@@ -389,7 +434,8 @@ int dflash_top_p_mask(const float* logits, float* out, int32_t* kept, int rows, 
 size_t spec_verify_noalloc_max_scratch(void);
 int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
                         const int32_t* draft_tokens, const double* draft_lse,
-                        float temperature, const uint64_t* seeds, uint64_t step,
+                        const dflash_nucleus_cut* target_cut,
+                        const dflash_nucleus_cut* draft_cut, float temperature, const uint64_t* seeds, uint64_t step,
                         int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
                         int batch, int gamma, int vocab, void* stream);
 

@@ -72,10 +72,10 @@ def test_block_attn_validation():
 
 
 def topk(**kw):
-    a = dict(z=P, B=2, G=8, V=151936, k=8, T=0.7, seeds=P, step=0, idx=P, val=P, lse=None,
-             draft=P, ws=None, wsb=0, st=None)
+    a = dict(z=P, cut=None, B=2, G=8, V=151936, k=8, T=0.7, seeds=P, step=0, idx=P, val=P,
+             lse=None, draft=P, ws=None, wsb=0, st=None)
     a.update(kw)
-    return dfl.load().dflash_topk(a["z"], a["B"], a["G"], a["V"], a["k"], a["T"], a["seeds"],
+    return dfl.load().dflash_topk(a["z"], a["cut"], a["B"], a["G"], a["V"], a["k"], a["T"], a["seeds"],
                                   a["step"], a["idx"], a["val"], a["lse"], a["draft"], a["ws"],
                                   a["wsb"], a["st"])
 
@@ -96,10 +96,10 @@ def test_topk_validation():
 
 
 def verify(**kw):
-    a = dict(zp=P, zq=P, d=P, lse=None, T=0.7, seeds=P, step=0, j=P, out=P, acc=None, B=2, G=8,
-             V=151936, ws=None, wsb=0, st=None)
+    a = dict(zp=P, zq=P, d=P, lse=None, tc=None, dc=None, T=0.7, seeds=P, step=0, j=P, out=P,
+             acc=None, B=2, G=8, V=151936, ws=None, wsb=0, st=None)
     a.update(kw)
-    return dfl.load().spec_verify(a["zp"], a["zq"], a["d"], a["lse"], a["T"], a["seeds"],
+    return dfl.load().spec_verify(a["zp"], a["zq"], a["d"], a["lse"], a["tc"], a["dc"], a["T"], a["seeds"],
                                   a["step"], a["j"], a["out"], a["acc"], a["B"], a["G"], a["V"],
                                   a["ws"], a["wsb"], a["st"])
 
@@ -181,7 +181,7 @@ def test_fuse_validation():
 
 def test_binding_raises_on_bad_status():
     with pytest.raises(dfl.DFlashError) as e:
-        dfl._call("dflash_topk", P, 1, 1, 1024, 0, 0.0, None, 0, P, P, None, None, None, 0, None)
+        dfl._call("dflash_topk", P, None, 1, 1, 1024, 0, 0.0, None, 0, P, P, None, None, None, 0, None)
     assert e.value.status == -2
 
 
@@ -243,6 +243,26 @@ def test_top_p_validation():
     assert topp(out=None) == -1
 
 
+def topcut(**kw):
+    a = dict(z=P, cut=P, kept=None, rows=4, V=151936, T=0.7, p=0.99, st=None)
+    a.update(kw)
+    return dfl.load().dflash_top_p_cut(a["z"], a["cut"], a["kept"], a["rows"], a["V"], a["T"],
+                                       a["p"], a["st"])
+
+
+def test_top_p_cut_validation():
+    assert topcut(rows=0) == 0
+    assert topcut(rows=-1) == -2
+    assert topcut(T=0.0) == -2
+    assert topcut(p=1.5) == -2
+    assert topcut(p=0.0, cut=None) == -2      # shape before pointers
+    assert topcut(z=None) == -1
+    assert topcut(cut=None) == -1
+    assert topcut(V=1 << 24) == -3
+    assert topcut(rows=(1 << 20) + 1) == -3
+    assert topp(out=None, kept=P) == -1       # the mask entry still needs its rows
+
+
 def test_top_p_vocab_limit():
     """Fixed-point row sums (2^40 per maximal weight) stay within 64 bits only
     below 2^24 entries."""
@@ -290,10 +310,11 @@ def test_binding_checks_workspace_dtype_and_device():
 
 
 def verify_na(**kw):
-    a = dict(zp=P, zq=P, d=P, lse=None, T=0.7, seeds=P, step=0, j=P, out=P, acc=None, B=2, G=8,
-             V=151936, st=None)
+    a = dict(zp=P, zq=P, d=P, lse=None, tc=None, dc=None, T=0.7, seeds=P, step=0, j=P, out=P,
+             acc=None, B=2, G=8, V=151936, st=None)
     a.update(kw)
-    return dfl.load().spec_verify_noalloc(a["zp"], a["zq"], a["d"], a["lse"], a["T"], a["seeds"],
+    return dfl.load().spec_verify_noalloc(a["zp"], a["zq"], a["d"], a["lse"], a["tc"], a["dc"], a["T"],
+                                          a["seeds"],
                                           a["step"], a["j"], a["out"], a["acc"], a["B"], a["G"],
                                           a["V"], a["st"])
 

@@ -23,13 +23,15 @@ def f32(x):
     return float(np.float32(x))
 
 
-def _topk_case(zd, k, T, seeds, step=0, what=""):
+def _topk_case(zd, k, T, seeds, step=0, what="", cut=None, z_ref=None):
+    """GPU dflash_topk on zd (through nucleus cuts `cut` if given) against the
+    oracle on z_ref (the rows the GPU's reading stands for; zd by default)."""
     print(f"[topk] {what} logits{tuple(zd.shape)} k={k} T={T}", flush=True)
     dev = cuda()
     res = dfl.dflash_topk(zd.to(dev), k, T, seeds=None if seeds is None else seeds.to(dev),
-                          step=step)
+                          step=step, cut=None if cut is None else cut.to(dev))
     torch.cuda.synchronize()
-    z = to64(zd)
+    z = to64(zd) if z_ref is None else np.asarray(z_ref, dtype=np.float64)
     ref = oracle.draft_rows(z, k, f32(T), seeds=None if seeds is None else to64(seeds).astype(np.uint64),
                             step=step)
     np.testing.assert_array_equal(to64(res["idx"]), ref["idx"])
@@ -122,20 +124,27 @@ def test_topk_trained_block_size_rows():
 
 
 # --------------------------------------------------------------------- verify
-def _verify_case(zt, zd, drafts, T, seeds, step=0, use_lse=True, what=""):
+def _verify_case(zt, zd, drafts, T, seeds, step=0, use_lse=True, what="", target_cut=None,
+                 draft_cut=None, zt_ref=None, zd_ref=None):
+    """GPU spec_verify on zt, zd (through nucleus cuts if given) against the
+    oracle on zt_ref, zd_ref (zt, zd by default)."""
     print(f"[verify] {what} logits{tuple(zt.shape)} T={T} lse={use_lse}", flush=True)
     dev = cuda()
     B, G, V = zt.shape
     d_full = torch.zeros((B, G), dtype=torch.int32)
     d_full[:, :G - 1] = drafts.to(torch.int32)
+    tc = None if target_cut is None else target_cut.to(dev)
+    dc = None if draft_cut is None else draft_cut.to(dev)
     lse = None
     if T > 0 and use_lse:
-        lse = dfl.dflash_topk(zd.to(dev), 1, T, seeds=seeds.to(dev))["lse"]
+        lse = dfl.dflash_topk(zd.to(dev), 1, T, seeds=seeds.to(dev), cut=dc)["lse"]
     res = dfl.spec_verify(zt.to(dev), zd.to(dev) if T > 0 else None, d_full.to(dev), T,
                           seeds=None if seeds is None else seeds.to(dev), step=step,
-                          draft_lse=lse)
+                          draft_lse=lse, target_cut=tc, draft_cut=dc)
     torch.cuda.synchronize()
-    ref = oracle.spec_verify(to64(zt), to64(zd) if T > 0 else None, to64(drafts), f32(T),
+    zt64 = to64(zt) if zt_ref is None else np.asarray(zt_ref, dtype=np.float64)
+    zd64 = to64(zd) if zd_ref is None else np.asarray(zd_ref, dtype=np.float64)
+    ref = oracle.spec_verify(zt64, zd64 if T > 0 else None, to64(drafts), f32(T),
                              seeds=None if seeds is None else to64(seeds).astype(np.uint64),
                              step=step)
     j = to64(res["accept_len"])
@@ -147,7 +156,7 @@ def _verify_case(zt, zd, drafts, T, seeds, step=0, use_lse=True, what=""):
         np.testing.assert_array_equal(acc, ref["accepted"])
         return j
     sd = to64(seeds).astype(np.uint64)
-    z_t, z_d = to64(zt), to64(zd)
+    z_t, z_d = zt64, zd64
     for b in range(B):
         near = False
         for r in range(G - 1):

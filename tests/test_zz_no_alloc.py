@@ -2,7 +2,7 @@
 scratch, for callers that cannot allocate) against spec_verify on the same
 inputs, through the C ABI: two calls in a row, the second smaller, at the
 throughput shape and small shapes, greedy, sampled, sampled with the draft
-normaliser given, and deterministic drafts.  Both entry points run the same
+normaliser given, deterministic drafts, and top-p nucleus cuts on both sides.  Both entry points run the same
 kernels, so the outputs must be identical."""
 import numpy as np
 import pytest
@@ -27,20 +27,25 @@ def _case(B, G, V, T, mode, seed):
     zt, zd = syn.logits_pair(B, G, V, 2.0, 1.0, seed=seed)
     zt, zd = zt.to(dev), zd.to(dev)
     seeds = syn.philox_seeds(B, seed).to(dev) if T > 0 else None
-    tk = dfl.dflash_topk(zd, 4, T, seeds=seeds, step=3)
+    tc = dc = None
+    if mode == "top_p":  # nucleus cuts on both sides
+        tc, _ = dfl.dflash_top_p_cut(zt, T, 0.95)
+        dc, _ = dfl.dflash_top_p_cut(zd, T, 0.95)
+    tk = dfl.dflash_topk(zd, 4, T, seeds=seeds, step=3, cut=dc)
     drafts = tk["draft"]
     dl = None if mode == "deterministic" else zd
-    lse = tk["lse"] if mode == "with_lse" else None
-    ref = dfl.spec_verify(zt, dl, drafts, T, seeds=seeds, step=3, draft_lse=lse)
+    lse = tk["lse"] if mode in ("with_lse", "top_p") else None
+    ref = dfl.spec_verify(zt, dl, drafts, T, seeds=seeds, step=3, draft_lse=lse, target_cut=tc,
+                          draft_cut=dc)
     got = dfl.spec_verify_noalloc(zt, dl, drafts, T, _outputs(B, G, dev), seeds=seeds, step=3,
-                                  draft_lse=lse)
+                                  draft_lse=lse, target_cut=tc, draft_cut=dc)
     torch.cuda.synchronize()
     for key in ("accept_len", "out_tokens"):
         assert torch.equal(got[key].cpu(), ref[key].cpu()), key
     assert torch.equal(got["accepted"][:, :G - 1].cpu(), ref["accepted"].cpu())
 
 
-@pytest.mark.parametrize("mode", ["sampled", "with_lse", "deterministic"])
+@pytest.mark.parametrize("mode", ["sampled", "with_lse", "deterministic", "top_p"])
 def test_noalloc_matches_spec_verify_twice_second_smaller(mode):
     _case(32, 8, 151936, 0.7, mode, seed=11)
     _case(3, 5, 5000, 0.9, mode, seed=12)
@@ -58,6 +63,6 @@ def test_noalloc_rejects_a_shape_beyond_its_scratch():
     assert dfl.spec_verify_workspace_size(B, G, V) > cap
     zt = torch.empty((B, G, 4), dtype=torch.float32, device=dev)  # never read: rejected first
     with pytest.raises(dfl.DFlashError) as e:
-        dfl._call("spec_verify_noalloc", dfl._ptr(zt), None, dfl._ptr(zt), None, 0.0, None, 0,
+        dfl._call("spec_verify_noalloc", dfl._ptr(zt), None, dfl._ptr(zt), None, None, None, 0.0, None, 0,
                   dfl._ptr(zt), dfl._ptr(zt), None, B, G, V, None)
     assert e.value.status == -6
