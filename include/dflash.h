@@ -385,11 +385,12 @@ int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows
  *          entries are written)
  *   kept   [rows] int32 or NULL: the nucleus size of each row
  *   temperature > 0; 0 < top_p <= 1 (top_p == 1 keeps every entry)
- * Supported: vocab < 2^24 (the fixed-point row sums below stay within 64
- * bits), rows <= 2^20; DFLASH_ERR_UNSUPPORTED otherwise.
- * Accuracy: weights 2^((z - max) log2(e)/T) in fp32, summed exactly in fixed
- * point (2^-40 of the maximum's weight); the nucleus boundary is exact up to
- * that rounding of the cumulative mass.
+ * Supported: vocab < 2^24 (a mass bin's 64-bit fixed-point sum stays
+ * exact), rows <= 2^20; DFLASH_ERR_UNSUPPORTED otherwise.
+ * Accuracy: weights 2^((z - max) log2(e)/T) from fp32 exponentials, grouped
+ * in bins of 1/64 of a log2 unit and summed exactly in 31-bit fixed point
+ * relative to the bin's top, bin masses added in fp64; the nucleus boundary
+ * is exact up to that rounding of the cumulative mass (about 1e-7 of it).
  * No workspace; one workgroup per row.
  * ------------------------------------------------------------------------ */
 int dflash_top_p_mask(const float* logits, float* out, int32_t* kept, int rows, int vocab,
