@@ -132,6 +132,7 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     __shared__ double s_before_d;
     __shared__ unsigned long long s_before, s_prefix, s_qb;
     __shared__ int s_bin, s_n, s_sub;
+    __shared__ double s_tab[64];  // 2^(-k/64)
     static_assert(sizeof(g_w) >= kPBins * sizeof(unsigned int), "digit counts fit");
     static_assert(sizeof(h_mass) >= kPCap * 2 * sizeof(unsigned long long), "final candidates fit");
     unsigned int* const h_cnt = reinterpret_cast<unsigned int*>(g_w);
@@ -215,6 +216,7 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
             for (int u = 0; u < kPInFlight; ++u) r = fmaxf(r, z[min(tid + u * kPThreads, V - 1)]);
         }
         for (int b = tid; b < kPBins; b += kPThreads) h_mass[b] = 0;
+        if (tid < 64) s_tab[tid] = exp2(-(double)tid / 64.0);
         r = block_reduce(r, red_f, fmax_op);
         bool rebuild = true;
         if (r != -INFINITY) {
@@ -251,7 +253,7 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int b = tid * kPer + i;
-            mass[i] = ldexp((double)h_mass[b] * exp2(-(double)(b & 63) / 64.0), -31 - (b >> 6));
+            mass[i] = ldexp((double)h_mass[b] * s_tab[b & 63], -31 - (b >> 6));
             mine += mass[i];
         }
         const double total = block_reduce(mine, red_d, [](double x, double y) { return x + y; });

@@ -191,6 +191,24 @@ def test_cut_equal_logits_and_signed_zeros():
         check_cut(z, 0.7, p, what="signed zeros")
 
 
+def test_cut_paths_the_sample_does_not_predict():
+    """The cut kernel takes its histogram's reference from the first entries
+    of the row (every thread's first loads, 32,768 entries).  Rows where that
+    sample misleads give the same result through the other paths: a maximum
+    far beyond the sample (the histogram is rebuilt relative to it), a sample
+    distributed unlike the rest (higher or lower, tied values outside it),
+    and a row length that is not a multiple of 4 (no 16-byte loads)."""
+    V = 40000
+    z = syn.normal((6, V), 11, "topp_paths", std=2.0)
+    z[0, V - 3] = 60.0                        # far above the sample's maximum
+    z[1, 33000:] += 3.0                        # the unsampled part sits higher
+    z[2, :32768] -= 4.0                        # the sampled part sits lower
+    z[3, 32768:] = torch.round(z[3, 32768:] * 4) / 4   # ties outside the sample
+    for p in (0.5, 0.9, 0.99):
+        check_cut(z, 0.7, p, what="unpredicted")
+    check_cut(syn.normal((3, 5001), 12, "topp_odd", std=2.0), 0.7, 0.95, what="V % 4 != 0")
+
+
 def test_cut_full_vocabulary_rows():
     zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=3)
     rows = zt.reshape(-1, 151936)
