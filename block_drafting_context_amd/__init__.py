@@ -24,6 +24,7 @@ __all__ = [
     "dflash_lm_head_topk", "dflash_lm_head_topk_workspace_size",
     "dflash_top_p_mask", "dflash_top_p_cut", "nucleus_cut_values",
     "spec_verify_noalloc", "spec_verify_noalloc_max_scratch",
+    "dflash_device_checks", "dflash_violations",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -43,7 +44,10 @@ EXPORTED_SYMBOLS = (
     "dflash_lm_head_topk_workspace_size", "dflash_lm_head_topk",
     "dflash_top_p_mask", "dflash_top_p_cut",
     "spec_verify_noalloc_max_scratch", "spec_verify_noalloc",
+    "dflash_device_checks", "dflash_violations",
 )
+# the same library built with device-data precondition checks
+checked_lib_path = os.path.join(_HERE, "libdflash_checked.so")
 
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 
@@ -84,6 +88,8 @@ def load():
         "dflash_lm_head_topk_workspace_size": (_sz, [_i] * 4),
         "dflash_top_p_mask": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
         "dflash_top_p_cut": (_i, [_vp, _vp, _vp, _i, _i, _f, _f, _vp]),
+        "dflash_device_checks": (_i, []),
+        "dflash_violations": (_i, [_vp, _i, _vp]),
         "dflash_lm_head_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _u64, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp]),
         "spec_verify_noalloc_max_scratch": (_sz, []),
@@ -371,6 +377,21 @@ def nucleus_cut_values(cut):
     """Cuts [..., 2] int32 -> (logit [...] fp32, index [...] int32): entry v of the row is
     in the nucleus iff z_v > logit, or z_v == logit and v <= index."""
     return cut[..., 0].view(torch.float32), cut[..., 1]
+
+
+# ------------------------------------------------------------ device checks
+def dflash_device_checks():
+    """1 when the loaded library records violated device-data preconditions."""
+    return int(load().dflash_device_checks())
+
+
+def dflash_violations(clear=True, stream=None):
+    """The DFLASH_VIOLATION_* bits recorded on the current GPU (after `stream`);
+    raises DFlashError(-3) in a release build."""
+    word = ctypes.c_uint32(0)
+    st = _stream(stream) if dflash_device_checks() else None  # a release build makes no HIP call
+    _call("dflash_violations", ctypes.byref(word), int(bool(clear)), st)
+    return int(word.value)
 
 
 # -------------------------------------------------------------------- LM head

@@ -30,6 +30,7 @@
 #include "common.hpp"
 
 namespace dfl {
+DFL_VIOLATION_WORD(violations_attn)
 namespace {
 
 constexpr int TK = 32;             // keys per tile
@@ -117,6 +118,7 @@ __global__ void __launch_bounds__(256) block_attn_bf16_kernel(AttnArgs a) {
     const int g = lane >> 4, i16 = lane & 15;
 
     const int64_t cl = a.ctx_len[b];
+    if (DFLASH_DEVICE_CHECKS && cl < 0 && tid == 0) DFL_VIOLATION(DFLASH_VIOLATION_CTX_LEN);
     const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
     const int total = n + a.G;
     int per = (total + a.n_splits - 1) / a.n_splits;
@@ -483,6 +485,7 @@ __global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
     const int h = qi % a.HQ, b = qi / (a.HQ * a.G);
     const int kvh = h / (a.HQ / a.HKV);
     const int64_t cl = a.ctx_len[b];
+    if (DFLASH_DEVICE_CHECKS && cl < 0 && lane == 0) DFL_VIOLATION(DFLASH_VIOLATION_CTX_LEN);
     const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
     const int total = n + a.G;
     const int D = a.D;

@@ -258,6 +258,45 @@ inline int64_t capped_product(int64_t cap, std::initializer_list<int64_t> factor
 // a launch counts its work-items in 32 bits.
 constexpr int64_t kMaxRowsPerCall = 1 << 20;
 
+// ------------------------------------------------------ device-data checks
+// Compiled with DFLASH_DEVICE_CHECKS=1 (libdflash_checked.so), kernels record
+// the device-data preconditions they find violated (DFLASH_VIOLATION_* bits)
+// in a word per source file and GPU; dflash_violations ORs the files' words.
+// A release build compiles the checks away.  The record is a vector-memory
+// atomic OR, never a scalar store.
+#ifndef DFLASH_DEVICE_CHECKS
+#define DFLASH_DEVICE_CHECKS 0
+#endif
+// Host readers of each file's word (defined only with device checks).
+int violations_attn(uint32_t* word, bool clear, hipStream_t st);
+int violations_fuse(uint32_t* word, bool clear, hipStream_t st);
+int violations_rows(uint32_t* word, bool clear, hipStream_t st);
+int violations_select(uint32_t* word, bool clear, hipStream_t st);
+#if DFLASH_DEVICE_CHECKS
+#define DFL_VIOLATION_WORD(reader)                                                              \
+    static __device__ unsigned int g_violations;                                                 \
+    int reader(uint32_t* word, bool clear, hipStream_t st) {                                      \
+        uint32_t v = 0;                                                                           \
+        if (hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_violations), sizeof v, 0,                   \
+                                     hipMemcpyDeviceToHost, st) != hipSuccess ||                  \
+            hipStreamSynchronize(st) != hipSuccess)                                               \
+            return DFLASH_ERR_HIP;                                                                \
+        if (clear) {                                                                              \
+            const uint32_t zero = 0;                                                              \
+            if (hipMemcpyToSymbolAsync(HIP_SYMBOL(g_violations), &zero, sizeof zero, 0,           \
+                                       hipMemcpyHostToDevice, st) != hipSuccess ||                \
+                hipStreamSynchronize(st) != hipSuccess)                                           \
+                return DFLASH_ERR_HIP;                                                            \
+        }                                                                                         \
+        *word |= v;                                                                               \
+        return DFLASH_OK;                                                                         \
+    }
+#define DFL_VIOLATION(bit) atomicOr(&g_violations, (unsigned int)(bit))
+#else
+#define DFL_VIOLATION_WORD(reader)
+#define DFL_VIOLATION(bit) ((void)0)
+#endif
+
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

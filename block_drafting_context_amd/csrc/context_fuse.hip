@@ -22,6 +22,7 @@
 #include "common.hpp"
 
 namespace dfl {
+DFL_VIOLATION_WORD(violations_fuse)
 namespace {
 
 constexpr int BM = 256, BN = 160, BK = 64;   // workgroup tile and K stage
@@ -255,7 +256,10 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int M, i
     for (int s = 1; s < S; ++s) v += p[s];
     const int seq = row_seq[r];
     const int64_t pos = row_pos[r];
-    if (seq < 0 || seq >= B || pos < 0) return;  // violated precondition: row skipped
+    if (seq < 0 || seq >= B || pos < 0) {  // violated precondition: row skipped
+        if (DFLASH_DEVICE_CHECKS && c == 0) DFL_VIOLATION(DFLASH_VIOLATION_ROW);
+        return;
+    }
     const int64_t slot = pos % W;
     const int d = c % DH, h = (c / DH) % NKV, lt = c / (DH * NKV);  // lt = layer*2 + t
     const size_t at = ((((size_t)lt * B + seq) * NKV + h) * W + (size_t)slot) * DH + d;
@@ -264,6 +268,26 @@ __global__ void __launch_bounds__(256) kv_append_kernel(const float* P, int M, i
     w[1] = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<u32x2*>(ring + at) = w;
 }
+
+#if DFLASH_DEVICE_CHECKS
+// Rows of one call that address the same (sequence, slot): each row compares
+// itself with every later row (builds with device checks only: rows^2 work).
+__global__ void __launch_bounds__(256) fuse_slot_check_kernel(const int32_t* row_seq, const int64_t* row_pos,
+                                                             int rows, int B, int W) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const int s = row_seq[r];
+    const int64_t p = row_pos[r];
+    if (s < 0 || s >= B || p < 0) return;  // recorded by the append
+    const int64_t slot = p % W;
+    bool dup = false;
+    for (int q = r + 1; q < rows; ++q) {
+        const int64_t p2 = row_pos[q];
+        dup |= row_seq[q] == s && p2 >= 0 && p2 % W == slot;
+    }
+    if (dup) DFL_VIOLATION(DFLASH_VIOLATION_SLOT);
+}
+#endif
 
 // Split-K count from a two-term time model: workgroup waves of one CU each
 // times one workgroup's MFMA time, plus writing and re-reading the fp32
@@ -406,6 +430,12 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     launch_gemm(H, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
     rc = launch_status();
     if (rc) return rc;
+#if DFLASH_DEVICE_CHECKS
+    hipLaunchKernelGGL(fuse_slot_check_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, row_seq,
+                       row_pos, rows, batch, window);
+    rc = launch_status();
+    if (rc) return rc;
+#endif
     dim3 grid((unsigned)((nkvc / 4 + 255) / 256), rows);
     launch_append(L.s2, grid, P2, rows, (int)nkvc, row_seq, row_pos, kv_ring, batch, n_kv, d_head,
                   window, st);

@@ -18,6 +18,7 @@
 #include "common.hpp"
 
 namespace dfl {
+DFL_VIOLATION_WORD(violations_select)
 namespace {
 
 constexpr int kSelThreads = 1024;
@@ -76,6 +77,11 @@ __global__ void __launch_bounds__(kSelThreads) select_path_kernel(SelArgs a) {
     const int32_t* cand = a.cand + (size_t)b * G * k;
     const float* U = a.score + (size_t)b * G * k;
     const int anchor = clamp_id(a.anchor[b], a.V);
+    if (DFLASH_DEVICE_CHECKS) {
+        bool bad = tid == 0 && (a.anchor[b] < 0 || a.anchor[b] >= a.V);
+        for (int e = tid; e < G * k; e += kSelThreads) bad |= cand[e] < 0 || cand[e] >= a.V;
+        if (bad) DFL_VIOLATION(DFLASH_VIOLATION_TOKEN);
+    }
     int prev_i = 0;  // wave 0: slot of the last chosen candidate among its position's list
     for (int t0 = 0; t0 < G; t0 += a.chunk) {
         const int nt = min(a.chunk, G - t0);

@@ -48,6 +48,7 @@
 #include "verify_run.hpp"
 
 namespace dfl {
+DFL_VIOLATION_WORD(violations_rows)
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -928,6 +929,7 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     const bool rejected = a.T > 0.f && j < G - 1;
 
     if (n == 0 && wave == 0) {
+        if (DFLASH_DEVICE_CHECKS && is_draft && (d_raw < 0 || d_raw >= a.V)) DFL_VIOLATION(DFLASH_VIOLATION_TOKEN);
         if (is_draft && a.accepted) a.accepted[(size_t)b * (G - 1) + r] = acc ? 1 : 0;
         int final_tok = -1;
         if (a.T == 0.f) {

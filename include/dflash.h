@@ -440,6 +440,37 @@ int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
                         int32_t* accept_len, int32_t* out_tokens, uint8_t* accepted,
                         int batch, int gamma, int vocab, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Device-data preconditions.
+ *
+ * Values the library reads on the device (token ids, lengths, positions) are
+ * preconditions: a release build does not check them (an out-of-range id is
+ * clamped into range, a negative length counts as 0, a fused row with an
+ * invalid sequence or position is skipped, so that no access leaves its
+ * buffer, but the results are unspecified).  The library built with device
+ * checks (libdflash_checked.so: the same sources compiled with
+ * DFLASH_DEVICE_CHECKS=1, for debugging callers) computes the same results
+ * and, in addition, records every violation it meets in a word per GPU:
+ * ------------------------------------------------------------------------ */
+#define DFLASH_VIOLATION_TOKEN    1u  /* a token id outside [0, vocab): spec_verify's
+                                         drafts, dflash_select_path's candidates or anchor */
+#define DFLASH_VIOLATION_CTX_LEN  2u  /* ctx_len < 0 (dflash_block_attn) */
+#define DFLASH_VIOLATION_ROW      4u  /* row_seq outside [0, batch) or row_pos < 0
+                                         (dflash_context_fuse) */
+#define DFLASH_VIOLATION_SLOT     8u  /* two rows of one dflash_context_fuse call address
+                                         the same (sequence, slot), e.g. more than `window`
+                                         rows of one sequence */
+
+/* 1 in the build with device checks, 0 in a release build. */
+int dflash_device_checks(void);
+
+/* The word of the GPU current on the calling thread: waits for `stream`,
+ * ORs the violations recorded so far into *word (set to 0 first) and, if
+ * `clear` is non-zero, resets them.  Synchronous; not for graph capture.
+ * DFLASH_ERR_UNSUPPORTED in a release build (*word = 0), DFLASH_ERR_NULL
+ * for a NULL word, DFLASH_ERR_HIP if a copy fails. */
+int dflash_violations(uint32_t* word, int clear, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

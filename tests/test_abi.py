@@ -379,3 +379,21 @@ def test_entry_points_reject_extreme_sizes():
     assert head(rows=M31) == -3
     assert head(rows=(1 << 20) + 1) == -3
     assert topp(rows=(1 << 20) + 1) == -3
+
+
+def test_device_checks_entry_points():
+    """The release library records nothing (dflash_violations is unsupported
+    and makes no HIP call); the build with device checks says so, exports the
+    same entry points, and rejects a NULL word before any HIP call."""
+    lib = dfl.load()
+    assert lib.dflash_device_checks() == 0
+    word = ctypes.c_uint32(7)
+    assert lib.dflash_violations(ctypes.byref(word), 1, None) == -3 and word.value == 0
+    assert lib.dflash_violations(None, 1, None) == -1
+    checked = ctypes.CDLL(dfl.checked_lib_path)
+    for n in declared_functions():
+        assert hasattr(checked, n), n
+    checked.dflash_device_checks.restype = ctypes.c_int
+    checked.dflash_violations.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert checked.dflash_device_checks() == 1
+    assert checked.dflash_violations(None, 1, None) == -1

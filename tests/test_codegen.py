@@ -16,18 +16,22 @@ from block_drafting_context_amd import build as b
 SOURCES = [s for s in b.SOURCES if s.endswith(".hip")]
 
 
-def device_asm(src):
+def device_asm(src, checked=False):
+    """Device assembly of one source, as the release library or (checked) as
+    the library built with device-data checks compiles it."""
+    extra = b.CHECKED_FLAGS if checked else []
     cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--offload-arch=gfx950", "-O3",
-           "-std=c++17", "-S", "--cuda-device-only", *b.DEVICE_FLAGS, f"-I{b.INCLUDE}",
+           "-std=c++17", "-S", "--cuda-device-only", *b.DEVICE_FLAGS, *extra, f"-I{b.INCLUDE}",
            f"-I{b.CSRC}", os.path.join(b.CSRC, src), "-o", "-"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return res.stdout
 
 
+@pytest.mark.parametrize("checked", [False, True], ids=["release", "checked"])
 @pytest.mark.parametrize("src", SOURCES)
-def test_no_generic_or_private_addressing(src):
-    asm = device_asm(src)
+def test_no_generic_or_private_addressing(src, checked):
+    asm = device_asm(src, checked)
     bad = {}
     fn = None
     for line in asm.splitlines():

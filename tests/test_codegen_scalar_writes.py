@@ -12,11 +12,12 @@ from test_codegen import SOURCES, device_asm
 SCALAR_WRITES = re.compile(r"^s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb|dcache_discard)")
 
 
+@pytest.mark.parametrize("checked", [False, True], ids=["release", "checked"])
 @pytest.mark.parametrize("src", SOURCES)
-def test_no_scalar_memory_writes(src):
+def test_no_scalar_memory_writes(src, checked):
     bad = {}
     fn = None
-    for line in device_asm(src).splitlines():
+    for line in device_asm(src, checked).splitlines():
         m = re.match(r"^(_Z\w+):", line)
         if m:
             fn = m.group(1)
