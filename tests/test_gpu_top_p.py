@@ -89,8 +89,8 @@ def test_edge_top_p_values_and_neg_inf_entries():
 def test_full_vocabulary_rows():
     zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=3)
     rows = zt.reshape(-1, 151936)
-    pick = torch.tensor([0, 77, 130, 255])
-    print("[top_p] full vocabulary, 256 rows (oracle on 4)", flush=True)
+    pick = torch.tensor([0, 17, 40, 63, 77, 90, 111, 128, 130, 151, 170, 191, 200, 223, 240, 255])
+    print("[top_p] full vocabulary, 256 rows (oracle on 16)", flush=True)
     dev = cuda()
     out, kept = dfl.dflash_top_p_mask(rows.to(dev), 0.7, 0.99, want_kept=True)
     torch.cuda.synchronize()
@@ -213,12 +213,13 @@ def test_cut_full_vocabulary_rows():
     zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=3)
     rows = zt.reshape(-1, 151936)
     dev = cuda()
-    print("[top_p cut] full vocabulary, 256 rows (oracle on 4)", flush=True)
+    print("[top_p cut] full vocabulary, 256 rows (oracle on 16)", flush=True)
     cut, kept = dfl.dflash_top_p_cut(rows.to(dev), 0.7, 0.99, want_kept=True)
     _, kept_m = dfl.dflash_top_p_mask(rows.to(dev), 0.7, 0.99, want_kept=True)
     torch.cuda.synchronize()
     assert torch.equal(kept.cpu(), kept_m.cpu())
-    check_cut(rows[torch.tensor([0, 77, 130, 255])].contiguous(), 0.7, 0.99, what="full V sample")
+    pick = torch.tensor([0, 17, 40, 63, 77, 90, 111, 128, 130, 151, 170, 191, 200, 223, 240, 255])
+    check_cut(rows[pick].contiguous(), 0.7, 0.99, what="full V sample")
 
 
 def _same(a, b, what):
