@@ -147,6 +147,20 @@ __device__ __forceinline__ RowCut row_cut(const dflash_nucleus_cut* cuts, size_t
     const dflash_nucleus_cut c = *(cuts ? cuts + row : reinterpret_cast<const dflash_nucleus_cut*>(valid));
     return cuts ? RowCut{c.logit, c.index} : RowCut{-INFINITY, INT_MAX};
 }
+// Kernels that take cuts are instantiated twice: with RowCut when the caller
+// gave cuts, with NoCut (no per-entry test at all) when not.
+template <bool CUT>
+using CutOf = typename std::conditional<CUT, RowCut, NoCut>::type;
+template <bool CUT>
+__device__ __forceinline__ CutOf<CUT> cut_of(const dflash_nucleus_cut* cuts, size_t row, const void* valid) {
+    if constexpr (CUT) return row_cut(cuts, row, valid);
+    else return NoCut{};
+}
+// lane j's cut, in every lane
+__device__ __forceinline__ RowCut cut_from_lane(const RowCut& c, int j) {
+    return RowCut{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, c.logit), j)), lane_value(c.index, j)};
+}
+__device__ __forceinline__ NoCut cut_from_lane(const NoCut&, int) { return NoCut{}; }
 
 // ------------------------------------------------------------ row scan
 // Wave `wave` of a row workgroup streams its run of segments and stores each
@@ -849,12 +863,13 @@ __device__ __forceinline__ int clamp_tok(int d, int V) { return d < 0 ? 0 : (d >
 // log-normalisers.  Both rows are read through raw buffers; without draft
 // logits (deterministic draft, q = point mass at dq) the drafter's buffer is
 // empty and reads as zeros.
+template <class CutT>
 struct ResidualW {
     __amdgpu_buffer_rsrc_t zp, zq;
     bool has_q;
     int dq;
     float Rp, Rq, Fp, Fq, c2;
-    RowCut cp, cq;  // the rows' nuclei (keep everything without cuts)
+    CutT cp, cq;  // the rows' nuclei (NoCut: keep everything)
     struct Raw {
         f32x4 p, q;
     };
@@ -878,7 +893,9 @@ struct ResidualW {
 // all agree); workgroup 0's first wave writes the committed tokens, draws the
 // bonus and records what the correction draw needs; on a rejection every wave
 // sums the residual over one segment of the rejected row.
+template <bool CUT>
 __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a) {
+    typedef CutOf<CUT> CutT;
     const int b = blockIdx.x / a.nr, n = blockIdx.x % a.nr;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -902,8 +919,8 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     const double lse_given = (a.draft_lse ? a.draft_lse : a.row_S)[row];
     const uint64_t seed = *(a.seeds ? a.seeds + b : reinterpret_cast<const uint64_t*>(a.row_S));
     const int d = is_draft ? clamp_tok(d_raw, a.V) : 0;
-    const RowCut tc = row_cut(a.tcut, row, a.row_S);
-    const RowCut dc = row_cut(a.dcut, row, a.row_S);
+    const CutT tc = cut_of<CUT>(a.tcut, row, a.row_S);
+    const CutT dc = cut_of<CUT>(a.dcut, row, a.row_S);
     const float zpd = tc.one(a.zp[row * a.V + d], d);
     const float zqd = dc.one((a.zq ? a.zq : a.zp)[row * a.V + d], d);
     int acc = 0;
@@ -939,8 +956,7 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
             const float Ml = __builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, M), G - 1));
             const double Sl = lane_value(S, G - 1);
             const double u = philox_uniform(seed, a.step, (uint64_t)b, (uint64_t)(G - 1), kFinalDraw);
-            const RowCut cl{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, tc.logit), G - 1)),
-                            lane_value(tc.index, G - 1)};
+            const CutT cl = cut_from_lane(tc, G - 1);
             final_tok = draw_softmax_row(a.zp + rl * a.V, a.V, a.seg_m + rl * a.nseg, a.seg_s + rl * a.nseg,
                                          a.nseg, a.c2, Ml, Sl, u, lane, cl);
         }
@@ -973,7 +989,7 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     // residual [p_j - q_j]_+: weights 2^((z - R) c2) F = exp(z / T - LSE) with
     // R = LSE T rounded to fp32, so that the exponent stays near zero
     const double lp = lane_value(lsep, j), lq = lane_value(lseq, j);
-    ResidualW w;
+    ResidualW<CutT> w;
     const size_t rowj = (size_t)b * G + j;
     const float* zpr = a.zp + rowj * a.V;
     w.zp = row_rsrc(zpr, a.V);
@@ -985,14 +1001,12 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     w.Fp = (float)exp((double)w.Rp / Td - lp);
     w.Fq = (float)exp((double)w.Rq / Td - lq);
     w.c2 = a.c2;
-    w.cp = RowCut{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, tc.logit), j)),
-                  lane_value(tc.index, j)};
-    w.cq = RowCut{__builtin_bit_cast(float, lane_value(__builtin_bit_cast(int, dc.logit), j)),
-                  lane_value(dc.index, j)};
+    w.cp = cut_from_lane(tc, j);
+    w.cq = cut_from_lane(dc, j);
     const int base = seg * kSeg + 4 * lane;
     // the segment's loads of both rows are issued before any is used (a quad
     // past the row's end reads zeros and weighs nothing)
-    ResidualW::Raw raw[kIters];
+    typename ResidualW<CutT>::Raw raw[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) raw[it] = w.load(base + it * 256);
     f32x4 t4[kIters];
@@ -1018,7 +1032,9 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
 // arithmetic that produced the segment sums.  Falls back to p_j when the
 // residual has no mass.
 constexpr int kResidRegs = 4;  // residual sums per lane held in registers
+template <bool CUT>
 __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
+    typedef CutOf<CUT> CutT;
     const int b = blockIdx.x, lane = threadIdx.x;
     // every load that does not depend on the record is issued with it
     const SeqDraw sd = a.seq[b];
@@ -1034,8 +1050,8 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
     if (sd.j < 0) return;
     const int j = sd.j;
     const size_t rj = (size_t)b * a.G + j;
-    const RowCut tc = row_cut(a.tcut, rj, a.row_S);
-    const RowCut dc = row_cut(a.dcut, rj, a.row_S);
+    const CutT tc = cut_of<CUT>(a.tcut, rj, a.row_S);
+    const CutT dc = cut_of<CUT>(a.dcut, rj, a.row_S);
     double tot = 0.0;
 #pragma unroll
     for (int c = 0; c < kResidRegs; ++c) tot += rv[c];
@@ -1046,7 +1062,7 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
     const float* zpr = a.zp + rowj * a.V;
     int tok;
     if (tot > 0.0) {
-        ResidualW w;
+        ResidualW<CutT> w;
         w.zp = row_rsrc(zpr, a.V);
         w.zq = row_rsrc(a.zq ? a.zq + rowj * a.V : zpr, a.zq ? a.V : 0);
         w.has_q = a.zq != nullptr;
@@ -1261,10 +1277,17 @@ int verify_enqueue(const float* target_logits, const float* draft_logits,
     t.accept_len = accept_len;
     t.out_tokens = out_tokens;
     t.accepted = accepted;
-    hipLaunchKernelGGL(verify_tail_kernel, dim3((unsigned)(batch * t.nr)), dim3(64 * kTailWaves), 0, st, t);
+    const bool cut = t.tcut || t.dcut;
+    if (cut)
+        hipLaunchKernelGGL(verify_tail_kernel<true>, dim3((unsigned)(batch * t.nr)), dim3(64 * kTailWaves), 0, st, t);
+    else
+        hipLaunchKernelGGL(verify_tail_kernel<false>, dim3((unsigned)(batch * t.nr)), dim3(64 * kTailWaves), 0, st, t);
     rc = launch_status();
     if (rc || temperature == 0.f) return rc;
-    hipLaunchKernelGGL(verify_draw_kernel, dim3((unsigned)batch), dim3(64), 0, st, t);
+    if (cut)
+        hipLaunchKernelGGL(verify_draw_kernel<true>, dim3((unsigned)batch), dim3(64), 0, st, t);
+    else
+        hipLaunchKernelGGL(verify_draw_kernel<false>, dim3((unsigned)batch), dim3(64), 0, st, t);
     return launch_status();
 }
 
