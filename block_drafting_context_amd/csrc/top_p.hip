@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(kPThreads) top_p_kernel(TopPArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t R = blockIdx.x;
     const float* z = a.z + R * a.V;
-    float* out = a.out + R * a.V;
+    float* out = a.out ? a.out + R * a.V : nullptr;  // NULL when only the cut is wanted
     const int V = a.V;
     const float c2 = a.c2;
     const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0 &&

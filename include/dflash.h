@@ -145,8 +145,10 @@ typedef struct dflash_nucleus_cut {
  * of each position's draft logits.  "The problem: one expensive token at a
  * time": the drafter proposes token y from its distribution q.
  *
- *   logits   [batch, gamma, vocab] float32; row r is the drafter's logits of
- *            block position r+1 (the token after anchor + r masks).
+ *   logits   [batch, gamma, vocab] float32, finite or -inf (results are
+ *            unspecified for rows holding NaN or +inf); row r is the
+ *            drafter's logits of block position r+1 (the token after
+ *            anchor + r masks).
  *   cut      [batch, gamma] nucleus cuts (top-p sampling), or NULL: every
  *            output below is that of the row with the entries outside its
  *            nucleus set to -inf.
@@ -190,9 +192,11 @@ int dflash_topk(const float* logits, const dflash_nucleus_cut* cut, int batch, i
  * q_r = softmax(draft_logits[b,r,:] / T).  "Beam 1.0 DFlash2",
  * "Evaluation": a block of 8 verifies 7 drafts.
  *
- *   target_logits [batch, gamma, vocab] float32; row r is the target's
- *            distribution for the token after anchor + drafts 0..r-1;
- *            rows 0..gamma-2 verify, row gamma-1 gives the bonus.
+ *   target_logits [batch, gamma, vocab] float32, finite or -inf (as for
+ *            draft_logits, results are unspecified for rows holding NaN or
+ *            +inf); row r is the target's distribution for the token after
+ *            anchor + drafts 0..r-1; rows 0..gamma-2 verify, row gamma-1
+ *            gives the bonus.
  *   draft_logits  [batch, gamma, vocab] float32 (rows 0..gamma-2 are read),
  *            or NULL.  NULL with T > 0 means deterministic drafts (chosen by
  *            dflash_select_path, "The candidate selector"): q_r is the point
@@ -467,6 +471,9 @@ int dflash_device_checks(void);
 /* The word of the GPU current on the calling thread: waits for `stream`,
  * ORs the violations recorded so far into *word (set to 0 first) and, if
  * `clear` is non-zero, resets them.  Synchronous; not for graph capture.
+ * The read and the reset are two copies: a kernel still running on another
+ * stream may record a violation between them, which the reset then drops
+ * (synchronise the device first to see every one).
  * DFLASH_ERR_UNSUPPORTED in a release build (*word = 0), DFLASH_ERR_NULL
  * for a NULL word, DFLASH_ERR_HIP if a copy fails. */
 int dflash_violations(uint32_t* word, int clear, void* stream);
