@@ -45,7 +45,7 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 struct GemmArgs {
-    const uint16_t* A;  // [M, K]
+    const uint16_t* A;  // [M, K], or in K slabs [K / 64][M][64] (A_SLABS)
     const uint16_t* B;  // [N, K]
     float* C;           // [S, M, N]
     int M, N, K, S, n_mt, n_nt;
@@ -62,6 +62,7 @@ struct GemmArgs {
 // split s is computed only on the XCDs x with x % S == s, so each XCD's L2
 // holds a single K slice of A (re-read by every column block of that XCD),
 // and the M tiles of one column block run on one XCD, sharing its B slice.
+template <bool A_SLABS>
 __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16_kernel(GemmArgs g) {
     constexpr int ROWB = BK * 2;  // 128 bytes per tile row and stage
     constexpr int NIB = BN / 8;   // 1 KB load instructions per B stage
@@ -95,7 +96,9 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
                     const int c = p ^ (r % 8);
                     int m = m0 + pw * 128 + r;
                     if (m >= g.M) m = g.M - 1;  // rows beyond M: any valid row, never stored
-                    const uint16_t* src = g.A + (size_t)m * g.K + k0 + c * 8;
+                    // in K slabs, a stage's 256 rows are one contiguous 32 KB block
+                    const uint16_t* src = A_SLABS ? g.A + ((size_t)(k0 / BK) * g.M + m) * BK + c * 8
+                                                  : g.A + (size_t)m * g.K + k0 + c * 8;
                     __builtin_amdgcn_global_load_lds(DFL_GLOBAL(src), DFL_LDS(dst + ins * 1024), 16, 0,
                                                      kLoadDefault);
                 }
@@ -185,11 +188,14 @@ __global__ void __launch_bounds__(64 * (kGConsumers + kGProducers)) gemm_nt_bf16
 }
 
 
-// H_t[r] = bf16( g * y / sqrt(mean(y^2) + eps) ),  y = sum_s P1[s][r]
-// One workgroup per row; float4 loads of every split's partial row.
 // H_t row r = RMSNorm(sum_s P[s][r]) * g, one 1,024-thread workgroup per row.  The
 // S split-K partials of a thread's (at most two) float4 columns are loaded together
 // (S is a template argument, so every load is issued before the first add).
+// H_t goes to the workspace in K slabs of 64 columns, [N / 64][M][64], the layout
+// in which the K/V projection reads its activation tiles: each stage's 256 rows
+// are one contiguous block instead of 256 pieces 2 N bytes apart (measured on
+// the K/V GEMM at 256 x 5,120 -> 10,240: 43 -> 38 us); h_out, if given, gets
+// the row-major copy.
 constexpr int kNormThreads = 1024;
 constexpr int kNormChunks = 2;  // float4 columns per thread: d_model <= 8192
 template <int S>
@@ -235,7 +241,7 @@ __global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* P, i
         u32x2 w;
         w[0] = pack_bf16x2(y[0] * inv * gg[0], y[1] * inv * gg[1]);
         w[1] = pack_bf16x2(y[2] * inv * gg[2], y[3] * inv * gg[3]);
-        *reinterpret_cast<u32x2*>(H + (size_t)r * N + 4 * n4) = w;
+        *reinterpret_cast<u32x2*>(H + ((size_t)(n4 >> 4) * M + r) * 64 + 4 * (n4 & 15)) = w;
         if (h_out) *reinterpret_cast<u32x2*>(h_out + (size_t)r * N + 4 * n4) = w;
     }
 }
@@ -355,13 +361,14 @@ void launch_append(int S, dim3 grid, const float* P, int M, int NC, const int32_
     }
 }
 
-void launch_gemm(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K, int S,
+void launch_gemm(const uint16_t* A, bool a_slabs, const uint16_t* B, float* C, int M, int N, int K, int S,
                  hipStream_t st) {
     GemmArgs g{A, B, C, M, N, K, S, (M + BM - 1) / BM, (N + BN - 1) / BN};
     const int per_round = kXCDs / S;  // column blocks per round of 8 workgroups
     const int rounds = (g.n_nt + per_round - 1) / per_round;
-    hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(kXCDs * rounds * g.n_mt),
-                       dim3(64 * (kGConsumers + kGProducers)), 0, st, g);
+    const dim3 grid(kXCDs * rounds * g.n_mt), block(64 * (kGConsumers + kGProducers));
+    if (a_slabs) hipLaunchKernelGGL(gemm_nt_bf16_kernel<true>, grid, block, 0, st, g);
+    else hipLaunchKernelGGL(gemm_nt_bf16_kernel<false>, grid, block, 0, st, g);
 }
 
 }  // namespace
@@ -421,13 +428,13 @@ extern "C" int dflash_context_fuse(const uint16_t* taps, const uint16_t* w_c, co
     uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
     float* P2 = reinterpret_cast<float*>(ws + L.p2);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    launch_gemm(taps, w_c, P1, rows, d_model, (int)kx, L.s1, st);
+    launch_gemm(taps, false, w_c, P1, rows, d_model, (int)kx, L.s1, st);
     int rc = launch_status();
     if (rc) return rc;
     launch_rmsnorm(L.s1, P1, rows, d_model, rms_gain, eps, H, h_t_out, st);
     rc = launch_status();
     if (rc) return rc;
-    launch_gemm(H, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
+    launch_gemm(H, true, w_kv, P2, rows, (int)nkvc, d_model, L.s2, st);
     rc = launch_status();
     if (rc) return rc;
 #if DFLASH_DEVICE_CHECKS
