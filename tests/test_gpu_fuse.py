@@ -62,6 +62,16 @@ def test_fuse_small_ragged_rows():
     _case(rows, 5, 128, 256, 2, 2, 64, W, B, seqs, pos, seed=1)
 
 
+def test_fuse_partial_second_row_tile():
+    """300 rows: two 256-row tiles of the GEMMs, the second one partial (its
+    missing rows read a valid row and are never stored), including the K/V
+    projection's reads of H_t in K slabs; every row against the oracle."""
+    rows, B, W = 300, 5, 128
+    seqs = np.arange(rows) % B
+    pos = np.arange(rows) // B + 7
+    _case(rows, 5, 128, 256, 2, 2, 64, W, B, seqs, pos, seed=5)
+
+
 def test_fuse_wraps_ring():
     """Positions 36..99 of one sequence in a 64-slot ring: every slot is written
     once and the row at position p lands in slot p mod 64."""
