@@ -913,8 +913,8 @@ def main():
             "rocprof_avg_us": None if trace is None else trace["avg_us"],
             "rocprof_timing": None if trace is None else
             "rocprofv3 kernel trace of bench.py --steps 5 --warmup 2, committed summary: "
-            f"{trace['avg_us_dispatches']}; in that profiled run the HIP events gave "
-            f"{trace['bench_events_avg_us_same_run']} us",
+            f"{trace.get('avg_us_dispatches', 'every dispatch')}; in that profiled run the HIP "
+            f"events gave {trace.get('bench_events_avg_us_same_run')} us",
             "frac_rocprof": None if trace is None else
             round(ab["block_attn"] / (trace["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
