@@ -471,57 +471,190 @@ struct Attn32Args {
     float* out;
     float* lse;
     int B, G, HQ, HKV, W, D;
+    int vec;  // d_head % 4 == 0 and every tensor 16-byte aligned: whole-float4 loads and stores
 };
 
 constexpr int kMaxKeys32 = 4096 + 32;
-constexpr int kWaves32 = 4;
+constexpr int kQR32 = 16;   // query rows per workgroup, all of one (sequence, KV head) group
+constexpr int kKC32 = 64;   // keys per chunk staged in LDS
+constexpr float kSlack32 = 8.f * 0.6931471805599453f;  // natural-log units the reference may trail the max
 
-__global__ void __launch_bounds__(256) block_attn_f32_kernel(Attn32Args a) {
-    __shared__ float sc[kWaves32][kMaxKeys32];
-    __shared__ float qs[kWaves32][128];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int qi = blockIdx.x * kWaves32 + wave;  // (b, r, h) flattened
-    if (qi >= a.B * a.G * a.HQ) return;
-    const int h = qi % a.HQ, b = qi / (a.HQ * a.G);
-    const int kvh = h / (a.HQ / a.HKV);
+// Columns 4 c4 .. 4 c4 + 3 of a row of d floats, zero past d.
+__device__ __forceinline__ f32x4 load_cols(const float* row, int c4, int d, bool vec) {
+    const int c = 4 * c4;
+    if (c >= d) return f32x4{0.f, 0.f, 0.f, 0.f};
+    if (vec) return *reinterpret_cast<const f32x4*>(row + c);
+    f32x4 v = {row[c], 0.f, 0.f, 0.f};
+    if (c + 1 < d) v[1] = row[c + 1];
+    if (c + 2 < d) v[2] = row[c + 2];
+    if (c + 3 < d) v[3] = row[c + 3];
+    return v;
+}
+
+// fp32 attention of up to 16 query rows of one (sequence, KV head) group
+// against that group's keys: the min(len, W) ring rows, then the block's.
+// Key chunks of 64 rows are staged in LDS (the next chunk loaded into
+// registers while the current one is used); a staged row holds C4 float4
+// columns (C4 = the power of two >= d/4, zero past d) plus one, so that
+// consecutive rows start 4 banks apart.  Each of the 16 waves owns one query
+// row: lane k scores key k of the chunk against it (a sequential fma chain
+// over d), the row's maximum and sum are wave reductions, and the row keeps a
+// reference that trails its running maximum by at most 8 ln 2 (exp(s - ref)
+// stays below 256; output and sum carry the same factor, so their ratio is
+// unaffected), rescaled only when a chunk exceeds it.  For O = sum p v, lane
+// (q, c) accumulates column c over the chunk's keys q, q + 64/C4, ...; the key
+// subsets are summed across lanes at the end.  Four waves per SIMD keep the
+// LDS latency of the small per-row chains covered.
+constexpr int kRPW32 = 2;                        // query rows per wave
+constexpr int kThreads32 = 64 * kQR32 / kRPW32;  // 512
+template <int C4>
+__global__ void __launch_bounds__(kThreads32) block_attn_f32_kernel(Attn32Args a) {
+    constexpr int KQ = 64 / C4;                 // key subsets of the output lanes
+    constexpr int RPW = kRPW32;
+    constexpr int NW = 64 * C4 / kThreads32 >= 1 ? 64 * C4 / kThreads32 : 1;  // staged rows per thread and chunk
+    constexpr int LG = C4 == 1 ? 0 : C4 == 2 ? 1 : C4 == 4 ? 2 : C4 == 8 ? 3 : C4 == 16 ? 4 : 5;
+    static_assert((1 << LG) == C4 && C4 <= 32, "C4: a power of two up to 32");
+    __shared__ f32x4 qs[kQR32][C4 + 1];
+    __shared__ f32x4 ks[kKC32][C4 + 1];
+    __shared__ f32x4 vs[kKC32][C4 + 1];
+    __shared__ float ps[kQR32][kKC32 + 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = a.HQ / a.HKV, nrows = a.G * group;
+    const int nrb = (nrows + kQR32 - 1) / kQR32;
+    const int rb = blockIdx.x % nrb;
+    const int kvh = (blockIdx.x / nrb) % a.HKV, b = blockIdx.x / (nrb * a.HKV);
+    const int D = a.D;
+    const bool vec = a.vec != 0;
+
     const int64_t cl = a.ctx_len[b];
-    if (DFLASH_DEVICE_CHECKS && cl < 0 && lane == 0) DFL_VIOLATION(DFLASH_VIOLATION_CTX_LEN);
+    if (DFLASH_DEVICE_CHECKS && cl < 0 && tid == 0) DFL_VIOLATION(DFLASH_VIOLATION_CTX_LEN);
     const int n = (int)(cl < (int64_t)a.W ? (cl < 0 ? 0 : cl) : (int64_t)a.W);
     const int total = n + a.G;
-    const int D = a.D;
-    const float* qrow = a.q + (size_t)qi * D;
-    for (int d = lane; d < D; d += kWave) qs[wave][d] = qrow[d];
-    __builtin_amdgcn_wave_barrier();
-    float mx = -INFINITY;
-    for (int t = lane; t < total; t += kWave) {
-        const float* krow = t < n ? a.kr + ((size_t)((size_t)b * a.HKV + kvh) * a.W + t) * D
-                                  : a.kb + ((size_t)((size_t)b * a.G + (t - n)) * a.HKV + kvh) * D;
-        float s = 0.f;
-        for (int d = 0; d < D; ++d) s = fmaf(qs[wave][d], krow[d], s);
-        s *= a.scale;
-        sc[wave][t] = s;
-        mx = fmaxf(mx, s);
+    const int nch = (total + kKC32 - 1) / kKC32;
+
+    // query row jr of the group block -> its flattened (sequence, block row, head)
+    auto q_index = [&](int jr) {
+        return ((size_t)b * a.G + jr / group) * a.HQ + (size_t)kvh * group + jr % group;
+    };
+    for (int e = tid; e < kQR32 * C4; e += kThreads32) {
+        const int r = e >> LG, c4 = e & (C4 - 1);
+        const int jr = rb * kQR32 + r;
+        qs[r][c4] = jr < nrows ? load_cols(a.q + q_index(jr) * D, c4, D, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int t = lane; t < total; t += kWave) {
-        const float p = expf(sc[wave][t] - mx);
-        sc[wave][t] = p;
-        sum += p;
-    }
-    sum = wave_sum(sum);
-    wave_lds_sync();
-    const float inv = 1.f / sum;
-    for (int d = lane; d < D; d += kWave) {
-        float acc = 0.f;
-        for (int t = 0; t < total; ++t) {
-            const float* vrow = t < n ? a.vr + ((size_t)((size_t)b * a.HKV + kvh) * a.W + t) * D
-                                      : a.vb + ((size_t)((size_t)b * a.G + (t - n)) * a.HKV + kvh) * D;
-            acc = fmaf(sc[wave][t], vrow[d], acc);
+
+    // chunk loads: thread tid stages column tid % C4 of rows tid / C4 + (256 / C4) w
+    const int lc4 = tid & (C4 - 1), lrow = tid >> LG;
+    const float* kring = a.kr + ((size_t)b * a.HKV + kvh) * a.W * D;
+    const float* vring = a.vr + ((size_t)b * a.HKV + kvh) * a.W * D;
+    auto key_row = [&](const float* ring, const float* blk, int t) {
+        return t < n ? ring + (size_t)t * D : blk + (((size_t)b * a.G + (t - n)) * a.HKV + kvh) * D;
+    };
+    f32x4 kreg[NW], vreg[NW];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int key = lrow + (kThreads32 >> LG) * w, t = c * kKC32 + key;
+            const bool ok = key < kKC32 && t < total;
+            kreg[w] = ok ? load_cols(key_row(kring, a.kb, t), lc4, D, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vreg[w] = ok ? load_cols(key_row(vring, a.vb, t), lc4, D, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        a.out[(size_t)qi * D + d] = acc * inv;
+    };
+
+    float ref[RPW], l[RPW];
+    f32x4 acc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        ref[r] = -INFINITY;
+        l[r] = 0.f;
+        acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (a.lse && lane == 0) a.lse[qi] = mx + logf(sum);
+    const int pc4 = lane & (C4 - 1), kq = lane >> LG;
+    fetch(0);
+    for (int c = 0; c < nch; ++c) {
+        __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int key = lrow + (kThreads32 >> LG) * w;
+            if (key < kKC32) {
+                ks[key][lc4] = kreg[w];
+                vs[key][lc4] = vreg[w];
+            }
+        }
+        __syncthreads();
+        if (c + 1 < nch) fetch(c + 1);
+        // lane: key c * 64 + lane against rows RPW wave + r
+        float sc[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) sc[r] = 0.f;
+#pragma unroll 4
+        for (int c4 = 0; c4 < C4; ++c4) {
+            const f32x4 kv = ks[lane][c4];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const f32x4 qv = qs[RPW * wave + r][c4];
+                sc[r] = fmaf(qv[0], kv[0], sc[r]);
+                sc[r] = fmaf(qv[1], kv[1], sc[r]);
+                sc[r] = fmaf(qv[2], kv[2], sc[r]);
+                sc[r] = fmaf(qv[3], kv[3], sc[r]);
+            }
+        }
+        const bool valid = c * kKC32 + lane < total;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const float x = valid ? sc[r] * a.scale : -INFINITY;
+            const float cm = wave_max(x);
+            if (cm > ref[r] + kSlack32) {  // wave-uniform; always on the first chunk
+                const float f = expf(ref[r] - cm);
+                l[r] *= f;
+                acc[r] *= f;
+                ref[r] = cm;
+            }
+            const float pv = valid ? expf(x - ref[r]) : 0.f;
+            ps[RPW * wave + r][lane] = pv;
+            l[r] += pv;
+        }
+        wave_lds_sync();  // this wave's weights are in LDS
+#pragma unroll 4
+        for (int st = 0; st < C4; ++st) {
+            const int k = kq + KQ * st;
+            const f32x4 v = vs[k][pc4];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const float pv = ps[RPW * wave + r][k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(pv, v[e], acc[r][e]);
+            }
+        }
+    }
+    // sum the key subsets (lanes pc4 + C4 q) and the lanes' weight sums
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+        for (int o = C4; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][e] += __shfl_xor(acc[r][e], o);
+        l[r] = wave_sum(l[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int jr = rb * kQR32 + RPW * wave + r;
+        if (jr >= nrows) break;  // wave-uniform
+        const size_t qi = q_index(jr);
+        const int col = 4 * pc4;
+        if (kq == 0 && col < D) {
+            const f32x4 o = acc[r] * (1.f / l[r]);
+            float* orow = a.out + qi * D;
+            if (vec) {
+                *reinterpret_cast<f32x4*>(orow + col) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < D) orow[col + e] = o[e];
+            }
+        }
+        if (a.lse && lane == 0) a.lse[qi] = ref[r] + logf(l[r]);
+    }
 }
 
 // --------------------------------------------------------------- planning
@@ -629,13 +762,23 @@ extern "C" int dflash_block_attn(const void* q, const void* k_blk, const void* v
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dtype == DFLASH_DTYPE_FP32) {
+        auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        const int vec = d_head % 4 == 0 && al16(q) && al16(k_blk) && al16(v_blk) && al16(k_ring) &&
+                        al16(v_ring) && al16(out);
         Attn32Args a{static_cast<const float*>(q), static_cast<const float*>(k_blk),
                      static_cast<const float*>(v_blk), static_cast<const float*>(k_ring),
                      static_cast<const float*>(v_ring), ctx_len, scale,
-                     static_cast<float*>(out), lse, batch, gamma, n_q, n_kv, window, d_head};
-        const int nq = batch * gamma * n_q;
-        hipLaunchKernelGGL(block_attn_f32_kernel, dim3((nq + kWaves32 - 1) / kWaves32),
-                           dim3(64 * kWaves32), 0, st, a);
+                     static_cast<float*>(out), lse, batch, gamma, n_q, n_kv, window, d_head, vec};
+        // one workgroup per (sequence, KV head, block of 16 of its gamma * n_q / n_kv query rows)
+        const int64_t nrb = ((int64_t)gamma * (n_q / n_kv) + kQR32 - 1) / kQR32;
+        const dim3 grid((unsigned)((int64_t)batch * n_kv * nrb)), block(kThreads32);
+        const int c4 = (d_head + 3) / 4;
+        if (c4 <= 1) hipLaunchKernelGGL(block_attn_f32_kernel<1>, grid, block, 0, st, a);
+        else if (c4 <= 2) hipLaunchKernelGGL(block_attn_f32_kernel<2>, grid, block, 0, st, a);
+        else if (c4 <= 4) hipLaunchKernelGGL(block_attn_f32_kernel<4>, grid, block, 0, st, a);
+        else if (c4 <= 8) hipLaunchKernelGGL(block_attn_f32_kernel<8>, grid, block, 0, st, a);
+        else if (c4 <= 16) hipLaunchKernelGGL(block_attn_f32_kernel<16>, grid, block, 0, st, a);
+        else hipLaunchKernelGGL(block_attn_f32_kernel<32>, grid, block, 0, st, a);
         return launch_status();
     }
     AttnArgs a{};

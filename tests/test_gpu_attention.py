@@ -55,6 +55,60 @@ def test_tiny_fp32_stress_scores():
     _check(a, 1 / 8.0, fp32=True, what="tiny fp32 stress")
 
 
+@pytest.mark.parametrize("D", [1, 6, 30, 64, 100, 128])
+def test_fp32_head_sizes(D):
+    """fp32 path: head sizes that are not a multiple of 4 (element loads), the
+    smallest and the largest; no context, a partial chunk, a wrapped ring,
+    unused ring slots poisoned with NaN, scores with real spread."""
+    a = syn.attention_inputs(3, 8, 4, 2, D, 192, [0, 100, 500], seed=20 + D, dtype=torch.float32,
+                             q_mult=3 * np.sqrt(D), k_std=1.0, poison_invalid=True)
+    _check(a, 1 / np.sqrt(D), fp32=True, what=f"fp32 D={D}")
+
+
+def test_fp32_serving_heads_full_window():
+    """fp32 path at the drafter's head layout: 40 query rows per KV head (three
+    16-row blocks), 4,096 + 8 keys (65 chunks of 64), V shifted by 100."""
+    a = syn.attention_inputs(2, 8, 40, 8, 128, 4096, [4096, 9000], seed=21, dtype=torch.float32,
+                             q_mult=3 * np.sqrt(128), k_std=1.0, v_mean=100.0, poison_invalid=True)
+    _check(a, 1 / np.sqrt(128), fp32=True, what="fp32 40q/8kv full window")
+
+
+def test_fp32_unaligned_tensors():
+    """fp32 path with tensors 4 bytes past a 16-byte boundary (element loads
+    and stores although d is a multiple of 4)."""
+    a = syn.attention_inputs(2, 8, 4, 1, 64, 256, [256, 31], seed=22, dtype=torch.float32,
+                             q_mult=3 * 8.0, k_std=1.0)
+    for key in ("q", "k_blk", "v_blk", "k_ring", "v_ring"):
+        t = a[key]
+        flat = torch.empty(t.numel() + 1, dtype=t.dtype)
+        flat[1:] = t.reshape(-1)
+        a[key] = flat[1:].view(t.shape)
+        assert a[key].is_contiguous() and a[key].data_ptr() % 16 != 0
+    dev = cuda()
+    t = {k: v.to(dev) if k == "ctx_len" else v for k, v in a.items()}
+    for key in ("q", "k_blk", "v_blk", "k_ring", "v_ring"):
+        flat = torch.empty(a[key].numel() + 1, dtype=torch.float32, device=dev)
+        flat[1:] = a[key].reshape(-1).to(dev)
+        t[key] = flat[1:].view(a[key].shape)
+        assert t[key].data_ptr() % 16 != 0
+    print("[attn] fp32 unaligned", flush=True)
+    out, lse = dfl.dflash_block_attn(t["q"], t["k_blk"], t["v_blk"], t["k_ring"], t["v_ring"],
+                                     t["ctx_len"], 1 / 8.0, want_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = _ref(a, 1 / 8.0)
+    assert_close_scaled(to64(out), ref, F32_REL, F32_ABS, "fp32 unaligned")
+    assert np.abs(to64(lse) - rlse).max() <= 1e-5 * max(1.0, np.abs(rlse).max())
+
+
+@pytest.mark.parametrize("G", [1, 32])
+def test_fp32_block_sizes(G):
+    """fp32 path: a block of one query position, and of 32 (two 16-row blocks
+    per KV head with one query head per KV head)."""
+    a = syn.attention_inputs(2, G, 8, 8, 64, 128, [5, 200], seed=23, dtype=torch.float32,
+                             q_mult=3 * 8.0, k_std=1.0)
+    _check(a, 1 / 8.0, fp32=True, what=f"fp32 gamma={G}")
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_ragged_lengths_several_tiles(D):
     ctx = [0, 1, 63, 65, 300, 512, 2000]
