@@ -100,6 +100,14 @@ __device__ __forceinline__ void load_segment(f32x4 (&v)[kIters], __amdgpu_buffer
                                               rsrc, (int)(base + it * 1024u), 0, kLoadStream));
 }
 
+// The nucleus inside a run of entries that lies wholly at or below a cut's
+// index (keep z >= logit) or wholly above it (keep z > logit, which for the
+// finite or -inf logits of the domain is z >= the next float up; denormals
+// are not flushed): one comparison per entry.
+struct ThrCut {
+    float thr;
+    __device__ __forceinline__ float one(float z, int) const { return z >= thr ? z : -INFINITY; }
+};
 // Top-p nucleus of a row (dflash_nucleus_cut): entry (z, v) is kept iff
 // z > logit, or z == logit and v <= index; an entry outside it is taken as
 // -inf, exactly as in a row masked to its nucleus.  NoCut keeps every entry
@@ -113,6 +121,23 @@ struct RowCut {
     __device__ __forceinline__ void quad(f32x4& q, int v0) const {
 #pragma unroll
         for (int c = 0; c < 4; ++c) q[c] = one(q[c], v0 + c);
+    }
+    // Entries s0 .. s0 + len - 1 as one threshold, when they lie wholly on
+    // one side of the index.
+    __device__ __forceinline__ bool seg_uniform(int s0, int len, ThrCut& t) const {
+        if (s0 + len - 1 <= index) {
+            t.thr = logit;
+            return true;
+        }
+        if (s0 > index) {
+            // the next float above logit; above either zero, the smallest
+            // positive float (-inf: -FLT_MAX)
+            const uint32_t bits = __float_as_uint(logit);
+            t.thr = logit == 0.f ? __uint_as_float(1u)
+                                 : __uint_as_float((bits & 0x80000000u) ? bits - 1u : bits + 1u);
+            return true;
+        }
+        return false;
     }
     // The lane's entries v[it][c] = entry base + it*256 + c of segment `seg`
     // (wave-uniform).  Within a segment v <= index holds for every entry or
@@ -402,6 +427,13 @@ __device__ __forceinline__ int draw_softmax_row(const float* zr, int V, MArr sm,
     const float ms = sm[seg];
     const double f = (double)fast_exp2((ms - M) * c2);
     const double tgt = (target - before) / f;
+    if constexpr (std::is_same<CutT, RowCut>::value) {
+        ThrCut t;
+        if (cut.seg_uniform(seg * kSeg, kSeg, t)) {
+            const SoftmaxW<ThrCut> wfn{row_rsrc(zr, V), ms, c2, t};
+            return draw_in_segment(seg, V, tgt, wfn, lane);
+        }
+    }
     const SoftmaxW<CutT> wfn{row_rsrc(zr, V), ms, c2, cut};
     return draw_in_segment(seg, V, tgt, wfn, lane);
 }
@@ -887,6 +919,24 @@ struct ResidualW {
     }
 };
 
+// The same weights with other cut tests.
+template <class CutT, class CutU>
+__device__ __forceinline__ ResidualW<CutU> with_cuts(const ResidualW<CutT>& w, CutU cp, CutU cq) {
+    ResidualW<CutU> r;
+    r.zp = w.zp;
+    r.zq = w.zq;
+    r.has_q = w.has_q;
+    r.dq = w.dq;
+    r.Rp = w.Rp;
+    r.Rq = w.Rq;
+    r.Fp = w.Fp;
+    r.Fq = w.Fq;
+    r.c2 = w.c2;
+    r.cp = cp;
+    r.cq = cq;
+    return r;
+}
+
 // Verification tail: a group of a.nr workgroups per sequence (one when
 // greedy).  Every wave takes the accept decisions of the whole block, lane r
 // for block row r (the same arithmetic on the same values in every wave, so
@@ -1004,25 +1054,38 @@ __global__ void __launch_bounds__(64 * kTailWaves) verify_tail_kernel(TailArgs a
     w.cp = cut_from_lane(tc, j);
     w.cq = cut_from_lane(dc, j);
     const int base = seg * kSeg + 4 * lane;
-    // the segment's loads of both rows are issued before any is used (a quad
-    // past the row's end reads zeros and weighs nothing)
-    typename ResidualW<CutT>::Raw raw[kIters];
+    auto segment_sum = [&](const auto& wfn) {
+        // the segment's loads of both rows are issued before any is used (a
+        // quad past the row's end reads zeros and weighs nothing)
+        typename std::decay<decltype(wfn)>::type::Raw raw[kIters];
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) raw[it] = w.load(base + it * 256);
-    f32x4 t4[kIters];
+        for (int it = 0; it < kIters; ++it) raw[it] = wfn.load(base + it * 256);
+        f32x4 t4[kIters];
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-        const int e = base + it * 256;
-        const f32x4 x = w.w4(raw[it], e);
-        t4[it] = e < a.V ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < kIters; ++it) {
+            const int e = base + it * 256;
+            const f32x4 x = wfn.w4(raw[it], e);
+            t4[it] = e < a.V ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int h = 0; h < kIters / 2; ++h) {
+            const f32x4 x = t4[2 * h], y = t4[2 * h + 1];
+            s += (double)(((x[0] + x[1]) + (x[2] + x[3])) + ((y[0] + y[1]) + (y[2] + y[3])));
+        }
+        return wave_sum(s);
+    };
+    double s;
+    if constexpr (CUT) {
+        // outside the segment holding a cut's index, its test is one comparison
+        ThrCut tp, tq;
+        if (w.cp.seg_uniform(seg * kSeg, kSeg, tp) && w.cq.seg_uniform(seg * kSeg, kSeg, tq))
+            s = segment_sum(with_cuts(w, tp, tq));
+        else
+            s = segment_sum(w);
+    } else {
+        s = segment_sum(w);
     }
-    double s = 0.0;
-#pragma unroll
-    for (int h = 0; h < kIters / 2; ++h) {
-        const f32x4 x = t4[2 * h], y = t4[2 * h + 1];
-        s += (double)(((x[0] + x[1]) + (x[2] + x[3])) + ((y[0] + y[1]) + (y[2] + y[3])));
-    }
-    s = wave_sum(s);
     if (lane == 0) a.resid_s[(size_t)b * a.nseg + seg] = s;
 }
 
@@ -1084,7 +1147,16 @@ __global__ void __launch_bounds__(64) verify_draw_kernel(TailArgs a) {
         };
         const double target = u * tot;
         const int sj = find_segment(a.nseg, target, segw, lane, before);
-        tok = sj < 0 ? 0 : draw_in_segment(sj, a.V, target - before, w, lane);
+        if (sj < 0) {
+            tok = 0;
+        } else {
+            bool uniform = false;
+            ThrCut tp, tq;
+            if constexpr (CUT)
+                uniform = w.cp.seg_uniform(sj * kSeg, kSeg, tp) && w.cq.seg_uniform(sj * kSeg, kSeg, tq);
+            tok = uniform ? draw_in_segment(sj, a.V, target - before, with_cuts(w, tp, tq), lane)
+                          : draw_in_segment(sj, a.V, target - before, w, lane);
+        }
     } else {
         tok = draw_softmax_row(zpr, a.V, a.seg_m + rowj * a.nseg, a.seg_s + rowj * a.nseg, a.nseg, a.c2, sd.Mj,
                                sd.Sj, u, lane, tc);
