@@ -487,7 +487,8 @@ __device__ __forceinline__ void topk_compact(TopKRegs& s, float (*lv)[64], int (
     wave_lds_sync();
     s.lcount = newcount;
     s.cnt = 0;
-    s.tv = newcount == k ? fmaxf(lastv, floor) : floor;
+    // both the old filter and the new one bound the row's k-th largest entry from below
+    s.tv = fmaxf(s.tv, newcount == k ? fmaxf(lastv, floor) : floor);
 }
 
 // The k-th largest of a row's segment maxima (LDS), counting repeats; -inf
@@ -508,6 +509,21 @@ __device__ __forceinline__ float kth_segment_max(const float* sm, int nseg, int 
             counted += __popcll(ballot(s0 + lane < nseg && sm[s0 + lane] == m));
         if (counted >= k) return m;
         t = m;
+    }
+}
+
+// The k-th largest of the wave's 64 values counting repeats, or -inf when
+// fewer than k are above -inf: at most k rounds, each taking the largest
+// value left and counting its copies.
+__device__ __forceinline__ float wave_kth_largest(float x, int k) {
+    int counted = 0;
+    for (;;) {
+        const float m = wave_max(x);
+        if (m == -INFINITY) return -INFINITY;
+        const uint64_t at = ballot(x == m);
+        counted += __popcll(at);
+        if (counted >= k) return m;
+        x = x == m ? -INFINITY : x;
     }
 }
 
@@ -621,11 +637,26 @@ __global__ void __launch_bounds__(kRowThreads) topk_row_kernel(TopKArgs a) {
             uint64_t mask[kIters];
             int total = 0;
             cut.segment(v, seg, base);
+            float qm[kIters];
 #pragma unroll
             for (int it = 0; it < kIters; ++it) {
                 // quads past the row's end read as zeros: they take no part
                 if (base + it * 256 >= a.V) v[it] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                pass[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3])) >= tk.tv;
+                qm[it] = fmaxf(fmaxf(v[it][0], v[it][1]), fmaxf(v[it][2], v[it][3]));
+            }
+            if (tk.tv == -INFINITY && a.k <= 64) {
+                // no bound yet (fewer than k segments above -inf, e.g. a
+                // short row): k of the 64 lanes each hold an entry >= the
+                // k-th largest lane maximum, so it bounds the row's k-th
+                // largest entry from below and the filter may start there
+                float lm = qm[0];
+#pragma unroll
+                for (int it = 1; it < kIters; ++it) lm = fmaxf(lm, qm[it]);
+                tk.tv = wave_kth_largest(lm, a.k);
+            }
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) {
+                pass[it] = qm[it] >= tk.tv;
                 mask[it] = ballot(pass[it]);
                 total += __popcll(mask[it]);
             }
