@@ -108,6 +108,7 @@ struct SegStat {
 
 struct HeadArgs {
     const uint16_t* h;     // [rows, d] bf16
+    const uint16_t* hs;    // the same rows in K slabs: [pass][d / kHBK][256][kHBK], zero past rows
     const uint16_t* w;     // [V, d] bf16
     SegStat* stats;        // [rows][nseg]
     u32x4* cand;           // [rows][nseg][kQuads]: candidate quads (4 logits each), in mask order
@@ -250,20 +251,25 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
     // count as issued loads, which keeps every wave's wait counts the same);
     // what their LDS rows hold only reaches outputs that are never stored
     // (rows >= M) or entries the epilogue replaces by -inf (>= V).
+    // hidden rows from their K slabs: a stage's 256 rows are one contiguous
+    // 32 KB block (read in row pieces 2 d bytes apart, the rows' chunks at one
+    // K step all fall on the same few memory channels)
     uint32_t h_off[kLoadsPerWave];
 #pragma unroll
     for (int ins = 0; ins < kLoadsPerWave; ++ins) {
         const int r = (wave * kLoadsPerWave + ins) * kRowsPerIns + rl;
-        h_off[ins] = (uint32_t)r * (uint32_t)(a.d * 2) + (uint32_t)((pc ^ chunk_swz(r)) * 16);
+        h_off[ins] = (uint32_t)r * (uint32_t)kHRowB + (uint32_t)((pc ^ chunk_swz(r)) * 16);
     }
-    const i32x4 h_rsrc = byte_buffer(a.h + (size_t)a.row0 * a.d, (uint32_t)(a.M * a.d * 2));
+    const i32x4 h_rsrc = byte_buffer(a.hs + (size_t)a.row0 * a.d, (uint32_t)(kHeadRows * a.d * 2));
     // K step kk of a tile is read at byte offset kbyte(kk): each workgroup
     // starts its K sweep at its own step, so the CUs' concurrent loads are
     // spread over the memory channels instead of all touching one K column of
     // the hidden rows and of their weight rows (measured: 470 -> 446 us at
     // 256 x 5120 x 151,936)
     const int krot = gidx % nk;
-    auto kbyte = [&](int kk) { int x = kk + krot; x -= x >= nk ? nk : 0; return (uint32_t)(x * kHBK * 2); };
+    auto kstep = [&](int kk) { int x = kk + krot; x -= x >= nk ? nk : 0; return (uint32_t)x; };
+    auto kbyte = [&](int kk) { return kstep(kk) * (uint32_t)kHRowB; };                 // weight rows
+    auto kslab = [&](int kk) { return kstep(kk) * (uint32_t)(kHeadRows * kHRowB); };  // hidden slabs
     auto issue_w = [&](int j) {
         const int t = j / nk, kk = j - t * nk;
         const int v0 = (s0 + 2 * t) * kSegW;
@@ -282,7 +288,7 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
         const uint32_t lds = lds_addr(sh[j % kHSlots]) + (uint32_t)(wave * kLoadsPerWave * 1024);
 #pragma unroll
         for (int ins = 0; ins < kLoadsPerWave; ++ins)
-            dma16<false>(lds + ins * 1024, h_off[ins], h_rsrc, kbyte(kk));
+            dma16<false>(lds + ins * 1024, h_off[ins], h_rsrc, kslab(kk));
     };
 
     f32x4 acc[8][4];
@@ -507,6 +513,21 @@ __global__ void __launch_bounds__(64 * kHWaves) lm_head_kernel(HeadArgs a) {
                 for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+}
+
+// Hidden rows -> K slabs [pass][d / kHBK][256][kHBK] (rows past the last one
+// zero): 16 bytes per thread.
+__global__ void __launch_bounds__(256) head_slabs_kernel(const uint16_t* h, int rows, int d, uint16_t* hs) {
+    const int chunks = d / 8;  // 16-byte pieces of a row
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t npass_rows = (int64_t)((rows + kHeadRows - 1) / kHeadRows) * kHeadRows;
+    if (e >= npass_rows * chunks) return;
+    const int r = (int)(e / chunks), c8 = (int)(e % chunks);
+    const u32x4 v = r < rows ? *reinterpret_cast<const u32x4*>(h + (size_t)r * d + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    const int pass = r / kHeadRows, rr = r % kHeadRows;
+    const int kt = (c8 * 8) / kHBK, cc = (c8 * 8) % kHBK;
+    const size_t at = (((size_t)pass * (d / kHBK) + kt) * kHeadRows + rr) * kHBK + cc;
+    *reinterpret_cast<u32x4*>(hs + at) = v;
 }
 
 // ------------------------------------------------------------------ finalize
@@ -931,16 +952,18 @@ __global__ void __launch_bounds__(kFinThreads) lm_head_finalize_kernel(FinArgs a
 }
 
 struct HeadLayout {
-    size_t stats, cand, gsum, bytes;
+    size_t stats, cand, gsum, hs, bytes;
 };
 
-HeadLayout head_layout(int rows, int vocab) {
+HeadLayout head_layout(int rows, int vocab, int d) {
     const size_t nseg = ((size_t)vocab + kSegW - 1) / kSegW;
+    const size_t npass = ((size_t)rows + kHeadRows - 1) / kHeadRows;
     HeadLayout L{};
     Carve c;
     L.stats = c.take<SegStat>((size_t)rows * nseg);
     L.cand = c.take<u32x4>((size_t)rows * nseg * kQuads);
     L.gsum = c.take<u32x2>((size_t)rows * nseg * 4);
+    L.hs = c.take<uint16_t>(npass * kHeadRows * (size_t)d);
     L.bytes = c.total();
     return L;
 }
@@ -977,7 +1000,7 @@ bool head_shape_ok(int rows, int d_model, int vocab, int k) {
 extern "C" size_t dflash_lm_head_topk_workspace_size(int rows, int d_model, int vocab, int k) {
     if (rows < 1 || d_model < 1 || vocab < 1 || k < 1 || !head_shape_ok(rows, d_model, vocab, k))
         return 0;
-    return head_layout(rows, vocab).bytes;
+    return head_layout(rows, vocab, d_model).bytes;
 }
 
 extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_head, int rows,
@@ -995,7 +1018,7 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     if (!head_shape_ok(rows, d_model, vocab, k) || (reinterpret_cast<uintptr_t>(hidden) & 15) ||
         (reinterpret_cast<uintptr_t>(w_head) & 15))
         return DFLASH_ERR_UNSUPPORTED;
-    const HeadLayout L = head_layout(rows, vocab);
+    const HeadLayout L = head_layout(rows, vocab, d_model);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.bytes)
         return DFLASH_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
@@ -1004,6 +1027,14 @@ extern "C" int dflash_lm_head_topk(const uint16_t* hidden, const uint16_t* w_hea
     const int nseg = (vocab + kSegW - 1) / kSegW;
     HeadArgs ha{};
     ha.h = hidden;
+    ha.hs = reinterpret_cast<uint16_t*>(ws + L.hs);
+    {
+        const int64_t pieces = ((int64_t)(rows + kHeadRows - 1) / kHeadRows) * kHeadRows * (d_model / 8);
+        hipLaunchKernelGGL(head_slabs_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, hidden, rows,
+                           d_model, const_cast<uint16_t*>(ha.hs));
+        const int rc = launch_status();
+        if (rc) return rc;
+    }
     ha.w = w_head;
     ha.stats = reinterpret_cast<SegStat*>(ws + L.stats);
     ha.cand = reinterpret_cast<u32x4*>(ws + L.cand);
