@@ -474,7 +474,6 @@ struct Attn32Args {
     int vec;  // d_head % 4 == 0 and every tensor 16-byte aligned: whole-float4 loads and stores
 };
 
-constexpr int kMaxKeys32 = 4096 + 32;
 constexpr int kQR32 = 16;   // query rows per workgroup, all of one (sequence, KV head) group
 constexpr int kKC32 = 64;   // keys per chunk staged in LDS
 constexpr float kSlack32 = 8.f * 0.6931471805599453f;  // natural-log units the reference may trail the max
@@ -730,7 +729,7 @@ int attn_shape(int batch, int gamma, int n_q, int n_kv, int d_head, int window, 
         capped_product(kMaxQueryRows, {batch, gamma, n_q}) < 0)
         return DFLASH_ERR_UNSUPPORTED;
     if (dtype == DFLASH_DTYPE_BF16 && d_head != 64 && d_head != 128) return DFLASH_ERR_UNSUPPORTED;
-    if (dtype == DFLASH_DTYPE_FP32 && (d_head > 128 || window + gamma > kMaxKeys32))
+    if (dtype == DFLASH_DTYPE_FP32 && d_head > 128)
         return DFLASH_ERR_UNSUPPORTED;
     return DFLASH_OK;
 }

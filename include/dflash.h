@@ -110,10 +110,11 @@ int dflash_version(void);
  *   out     [batch, gamma, n_q, d_head]    dtype (bf16 rounded to nearest even)
  *   lse     [batch, gamma, n_q] float32, natural-log normaliser of the scaled
  *           scores; may be NULL.
- * Supported: d_head in {64, 128}; n_q % n_kv == 0; 1 <= gamma <= 32;
- *   window % 64 == 0, 64 <= window <= 2^28, batch*gamma*n_q <= 2^28; fp32
- *   additionally needs d_head <= 128.
- * Accuracy: fp32 softmax and accumulation; bf16 products.
+ * Supported: n_q % n_kv == 0; 1 <= gamma <= 32; window % 64 == 0,
+ *   64 <= window <= 2^28, batch*gamma*n_q <= 2^28; d_head in {64, 128}
+ *   (bf16) or 1 <= d_head <= 128 (fp32).
+ * Accuracy: fp32 softmax and accumulation; bf16 products (bf16) or fp32
+ *   fused multiply-adds (fp32).
  * ------------------------------------------------------------------------ */
 size_t dflash_block_attn_workspace_size(int batch, int gamma, int n_q, int n_kv,
                                         int d_head, int window, int dtype);

@@ -73,6 +73,14 @@ def test_fp32_serving_heads_full_window():
     _check(a, 1 / np.sqrt(128), fp32=True, what="fp32 40q/8kv full window")
 
 
+def test_fp32_long_window():
+    """fp32 path beyond 4,096 keys: an 8,192-slot window (129 key chunks), one
+    full and one partly filled ring."""
+    a = syn.attention_inputs(2, 8, 4, 1, 64, 8192, [9000, 5000], seed=24, dtype=torch.float32,
+                             q_mult=3 * 8.0, k_std=1.0, poison_invalid=True)
+    _check(a, 1 / 8.0, fp32=True, what="fp32 window 8192")
+
+
 def test_fp32_unaligned_tensors():
     """fp32 path with tensors 4 bytes past a 16-byte boundary (element loads
     and stores although d is a multiple of 4)."""
