@@ -192,7 +192,9 @@ __device__ __forceinline__ int quad_max(int v) {
 // compiler, which cannot see which ring slot a DMA targets, does not guard the
 // operand fetches from the other slots with waits for every load in flight;
 // the kernel waits for its own loads explicitly.  NT: non-temporal.  m0 (the
-// LDS destination) is declared clobbered, so the compiler keeps nothing there.
+// LDS destination) is declared clobbered, so the compiler keeps nothing there,
+// and the s_nop is the one wait state an LDS DMA needs after a scalar write of
+// m0 (the compiler puts the same s_nop between the two when it emits the DMA).
 // The backend warns that m0 is a reserved register whose value it will not
 // preserve around the statement; nothing needs it preserved (no other code
 // of this file reads or writes m0, which the codegen tests check), the
@@ -203,10 +205,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <bool NT>
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
     if (NT)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                      :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop

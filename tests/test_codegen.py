@@ -48,7 +48,8 @@ def test_lm_head_m0_is_written_only_for_its_lds_dma():
     """The LM head's LDS DMA is inline assembly that sets m0 (the LDS
     destination) itself.  Nothing else in that file may read or write m0, so
     no compiler-held value there can be overwritten: every m0 write is
-    immediately followed by the DMA that reads it."""
+    followed by one wait state (an LDS DMA must not read m0 in the instruction
+    right after a scalar write of it) and then by the DMA that reads it."""
     lines = [l.strip() for l in device_asm("lm_head.hip").splitlines()]
     ins = [l for l in lines if l and not l.startswith((";", ".", "_")) and not l.endswith(":")]
     writes = 0
@@ -58,7 +59,8 @@ def test_lm_head_m0_is_written_only_for_its_lds_dma():
         op = l.split()[0]
         if op == "s_mov_b32" and l.split()[1].rstrip(",") == "m0":
             writes += 1
-            assert i + 1 < len(ins) and re.match(r"buffer_load_dwordx4 .* lds", ins[i + 1]), ins[i + 1]
+            assert i + 2 < len(ins) and ins[i + 1] == "s_nop 0", ins[i + 1]
+            assert re.match(r"buffer_load_dwordx4 .* lds", ins[i + 2]), ins[i + 2]
         else:
             raise AssertionError(f"unexpected m0 use: {l}")
     assert writes > 0
