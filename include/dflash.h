@@ -35,7 +35,9 @@
  *   are passed as uint16_t bit patterns.  All tensors are dense, row-major, in
  *   the index order written next to them.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *   enqueues work on it and returns; nothing is synchronised.
+ *   enqueues work on it and returns; nothing is synchronised.  The calls make
+ *   no allocation, memset or host synchronisation, so a caller may record them
+ *   into a HIP graph (stream capture) and replay it.
  * - The caller owns every buffer.  The library never allocates or frees
  *   memory and keeps no state between calls; scratch space comes only from
  *   the caller's `workspace` (device memory of at least the size the matching
