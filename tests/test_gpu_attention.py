@@ -117,6 +117,26 @@ def test_fp32_block_sizes(G):
     _check(a, 1 / 8.0, fp32=True, what=f"fp32 gamma={G}")
 
 
+@pytest.mark.parametrize("HQ,HKV,G", [(8, 8, 8), (16, 8, 16), (32, 8, 8), (64, 8, 16), (16, 1, 8),
+                                      (32, 2, 16)])
+def test_bf16_gqa_group_sizes(HQ, HKV, G):
+    """Query heads per KV head of 1, 2, 4, 8 and 16 (the workload has 5): from one
+    16-row query tile per (sequence, KV head) up to 256 query rows, which the
+    launch splits into several groups of query tiles."""
+    ctx = [0, 100, 700]
+    a = syn.attention_inputs(len(ctx), G, HQ, HKV, 128, 512, ctx, seed=30 + HQ + HKV + G,
+                             q_mult=3 * np.sqrt(128), k_std=1.0, poison_invalid=True)
+    _check(a, 1 / np.sqrt(128), what=f"bf16 {HQ}q/{HKV}kv gamma={G}")
+
+
+@pytest.mark.parametrize("HQ,HKV", [(8, 8), (32, 4)])
+def test_bf16_gqa_group_sizes_d64(HQ, HKV):
+    ctx = [64, 300]
+    a = syn.attention_inputs(len(ctx), 16, HQ, HKV, 64, 256, ctx, seed=40 + HQ,
+                             q_mult=3 * np.sqrt(64), k_std=1.0)
+    _check(a, 1 / np.sqrt(64), what=f"bf16 d=64 {HQ}q/{HKV}kv gamma=16")
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_ragged_lengths_several_tiles(D):
     ctx = [0, 1, 63, 65, 300, 512, 2000]
