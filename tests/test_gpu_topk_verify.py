@@ -193,6 +193,38 @@ def test_verify_tiny_greedy_and_sampled():
         _verify_case(zt, zd, _drafts_from(zd, 1.0, s), 1.0, s, step=step, what=f"tiny T=1 {step}")
 
 
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_block_of_one_position(T):
+    """gamma = 1: the block is the anchor alone.  Top-k and the draft draw run on
+    one row per sequence; verification has no draft to test, so nothing is
+    accepted and the one committed token is the bonus token, the target row's
+    argmax (greedy) or a draw from it (sampled)."""
+    B, G, V = 6, 1, 5000
+    zt, zd = syn.logits_pair(B, G, V, 2.0, 1.0, seed=31)
+    seeds = syn.philox_seeds(B, 3) if T > 0 else None
+    tk = _topk_case(zd, 4, T, seeds, step=4, what=f"gamma=1 T={T}")
+    print(f"[verify] gamma=1 T={T}", flush=True)
+    dev = cuda()
+    res = dfl.spec_verify(zt.to(dev), zd.to(dev) if T > 0 else None, tk["draft"], T,
+                          seeds=None if seeds is None else seeds.to(dev), step=4,
+                          draft_lse=tk["lse"] if T > 0 else None)
+    torch.cuda.synchronize()
+    ref = oracle.spec_verify(to64(zt), to64(zd) if T > 0 else None, np.zeros((B, 0)), f32(T),
+                             seeds=None if seeds is None else to64(seeds).astype(np.uint64), step=4)
+    np.testing.assert_array_equal(to64(res["accept_len"]), np.zeros(B))
+    np.testing.assert_array_equal(ref["accept_len"], np.zeros(B))
+    out = to64(res["out_tokens"])[:, 0]
+    if T == 0:
+        np.testing.assert_array_equal(out, ref["out_tokens"][:, 0])
+        np.testing.assert_array_equal(out, np.argmax(to64(zt)[:, 0], axis=1))
+        return
+    sd = to64(seeds).astype(np.uint64)
+    for b in range(B):
+        if out[b] != ref["out_tokens"][b, 0]:
+            u = oracle.uniform(int(sd[b]), 4, b, 0, 2)
+            assert draw_boundary_ok(to64(zt)[b, 0], f32(T), u, int(out[b]), int(ref["out_tokens"][b, 0])), b
+
+
 def test_verify_greedy_planted_prefixes():
     """Drafts equal to the target argmax for a planted number of leading rows."""
     B, G, V = 9, 8, 4096
