@@ -72,6 +72,18 @@ def test_fuse_partial_second_row_tile():
     _case(rows, 5, 128, 256, 2, 2, 64, W, B, seqs, pos, seed=5)
 
 
+@pytest.mark.parametrize("rows,n_taps,d_tgt,d_model,NL,NKV,DH,W,B", [
+    (1, 5, 64, 128, 1, 2, 32, 64, 1),       # one row, the smallest d_model, d_head 32
+    (17, 3, 192, 384, 1, 2, 96, 128, 4),    # three taps, d_model 384 (a ragged 160-column tile), d_head 96
+    (9, 1, 256, 8192, 1, 1, 64, 64, 3),     # one tap, the largest d_model
+])
+def test_fuse_shape_edges(rows, n_taps, d_tgt, d_model, NL, NKV, DH, W, B):
+    # distinct (sequence, slot) targets, positions past the window on some rows
+    seqs = np.arange(rows) % B
+    pos = (np.arange(rows) // B) * 7 + 3 * W // 2
+    _case(rows, n_taps, d_tgt, d_model, NL, NKV, DH, W, B, seqs, pos, seed=6 + rows)
+
+
 def test_fuse_wraps_ring():
     """Positions 36..99 of one sequence in a 64-slot ring: every slot is written
     once and the row at position p lands in slot p mod 64."""
