@@ -190,6 +190,26 @@ def test_uneven_runs_over_two_passes():
              check_rows=[0, 1, 255, 256, 299], what="uneven runs, 300 rows")
 
 
+@pytest.mark.parametrize("V,T", [(4, 0.0), (4, 0.9), (5, 0.9)])
+def test_vocabulary_as_small_as_k(V, T):
+    """The smallest vocabularies the call allows: V = k (every entry is a
+    candidate) and V = k + 1, in one partial segment."""
+    h, w = syn.lm_head_inputs(6, 64, V, seed=11)
+    run_case(h, w, 3, 4, T, seeds=syn.philox_seeds(2, 4) if T > 0 else None, what=f"V={V}")
+
+
+def test_largest_vocabulary():
+    """V = 1,048,576 entries (8,192 segments per row), the largest the call allows."""
+    h, w = syn.lm_head_inputs(8, 64, 1 << 20, seed=12)
+    run_case(h, w, 8, 16, 0.7, seeds=syn.philox_seeds(1, 5), check_rows=[0, 3, 7], what="V=2^20")
+
+
+def test_largest_model_width():
+    """d_model = 65,536, the largest the call allows: 1,024 K stages per tile."""
+    h, w = syn.lm_head_inputs(5, 65536, 600, seed=13)
+    run_case(h, w, 5, 8, 0.9, seeds=syn.philox_seeds(1, 6), what="d=65536")
+
+
 def test_few_rows():
     h, w = syn.lm_head_inputs(8, 512, 4096, seed=5)
     run_case(h, w, 8, 8, 0.7, seeds=syn.philox_seeds(1, 0), what="8 rows")
