@@ -41,9 +41,11 @@ def test_conv_serving_shape():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("B,G,D,ng", [(3, 1, 256, 1), (5, 16, 512, 64), (1, 8, 128, 16), (7, 3, 5120, 1)])
+@pytest.mark.parametrize("B,G,D,ng", [(3, 1, 256, 1), (5, 16, 512, 64), (1, 8, 128, 16), (7, 3, 5120, 1),
+                                      (2, 32, 8, 1), (2, 8, 16384, 2048)])
 def test_conv_edges(B, G, D, ng):
-    """A block of one (the anchor alone), groups of 8 channels, one group."""
+    """A block of one (the anchor alone), groups of 8 channels, one group, the
+    narrowest width (8 channels) over a block of 32, and 2,048 groups of 8."""
     _check(B, G, D, ng, seed=32 + G)
 
 

@@ -71,6 +71,13 @@ def test_select_path_chunked_tables_and_edges(k, G, r):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("B,G,k,V,r", [(2, 40, 8, 3000, 4096), (2, 4096, 4, 1000, 8)])
+def test_select_path_largest_rank_and_block(B, G, k, V, r):
+    """The call's limits: embedding rank r = 4,096, and a walk of 4,096 positions."""
+    _check_select(_inputs(B, G, k, V, r, seed=31 + r), f"r={r} G={G}")
+
+
+@pytest.mark.gpu
 def test_select_path_planted_chain():
     G, V, r, k = 8, 64, 16, 5
     rng = np.random.default_rng(5)
