@@ -209,6 +209,12 @@ def test_cut_paths_the_sample_does_not_predict():
     check_cut(syn.normal((3, 5001), 12, "topp_odd", std=2.0), 0.7, 0.95, what="V % 4 != 0")
 
 
+def test_cut_largest_vocabulary():
+    """Rows of 2^24 - 1 entries, the longest the calls allow (each mass bin's
+    64-bit fixed-point sum is still exact there): cut, mask and oracle agree."""
+    check_cut(syn.normal((2, (1 << 24) - 1), 13, "topp_huge", std=2.0), 0.7, 0.99, what="V=2^24-1")
+
+
 def test_cut_full_vocabulary_rows():
     zt, zd = syn.logits_pair(32, 8, 151936, 2.0, 1.0, seed=3)
     rows = zt.reshape(-1, 151936)
